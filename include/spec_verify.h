@@ -1,0 +1,179 @@
+/* spec_verify.h -- C ABI of the MI355X (gfx950) verify-and-resample library
+ * for speculative sampling.
+ *
+ * What one call computes (for each of B sequences, independently):
+ *   - the target model's K_b+1 logit rows and the draft model's K_b logit
+ *     rows are turned into "adjusted distributions" q_t (target) and p_t
+ *     (draft): temperature, then one filter (plain, top-k, nucleus or
+ *     greedy), applied before the rejection step and to both models
+ *     (paperlayer.ai summary of arXiv 2302.01318, section "Modified
+ *     Rejection Sampling"; FDE Interviews breakdown, section 01);
+ *   - draft token d_t is kept with probability min(1, q_t(d_t)/p_t(d_t)),
+ *     left to right; q is the target and p the draft (FDE Interviews
+ *     breakdown, section 01 and its figure "The idea, visually");
+ *   - at the first rejection n a replacement is drawn from the normalised
+ *     positive part of q_n - p_n and the rest of the draft is discarded;
+ *     if all K_b drafts survive, one more token is drawn from the target's
+ *     last logit row (same sources; roadtointelligence.com "Speculative
+ *     Decoding", section "Draft, then verify", with its letters swapped);
+ *   - each sequence therefore emits between 1 and K_b+1 tokens.
+ *
+ * Random numbers come from Philox4x32-10 (Salmon et al., SC'11) keyed by
+ * `seed`, with counter (g lo, t, purpose, g hi), g = row_offset + b, and
+ * purposes ACCEPT = 0, RESAMPLE = 1, BONUS = 2.  The uniform is
+ * (word0 >> 8) * 2^-24.  Results are a pure function of the inputs, the seed
+ * and g, so a batch may be split across calls or devices with row_offset.
+ *
+ * Threading and streams: a handle serves one stream at a time; use one
+ * handle per concurrently used stream.  spec_verify_run is asynchronous on
+ * the given stream, allocates nothing and never synchronises.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sv_handle_s* sv_handle_t;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Filter applied to both models' rows (after temperature, before the
+ * rejection step).
+ *   SV_PLAIN : softmax(x / tau) over every token whose logit is not -inf.
+ *   SV_TOPK  : keep every token whose raw logit is >= the k-th largest raw
+ *              logit of the row (ties at the boundary are all kept), then
+ *              softmax(x / tau) over the kept set.
+ *   SV_TOPP  : nucleus.  Tokens are grouped by equal logit and visited in
+ *              descending order of probability under softmax(x / tau); a
+ *              group is kept iff the mass of the groups before it is
+ *              < top_p (the first group is always kept; top_p = 1 keeps
+ *              every token of non-zero probability); renormalised.
+ *   SV_GREEDY: one-hot at the lowest index among the maximal raw logits;
+ *              the temperature is ignored. */
+typedef enum { SV_PLAIN = 0, SV_TOPK = 1, SV_TOPP = 2, SV_GREEDY = 3 } sv_mode;
+
+/* Return codes (synchronous argument errors launch nothing). */
+enum {
+  SV_OK = 0,
+  SV_EINVAL = -1,    /* bad pointer, size or default parameter            */
+  SV_ECAPACITY = -2, /* B > max_batch or K_max > max_k                    */
+  SV_EDTYPE = -3,    /* unknown dtype                                      */
+  SV_EHIP = -4,      /* a HIP runtime call failed; see last_error          */
+  SV_ENOMEM = -5     /* workspace allocation failed at create              */
+};
+
+/* row_status bits, written per sequence by the device.  Bits 0, 1, 2 and 6
+ * are errors: the sequence then has accepted = -1 and every out_token -1.
+ * The others are informational. */
+enum {
+  SV_ST_TOKEN = 1u << 0,         /* a draft token d_t (t < K_b) is outside [0, V)   */
+  SV_ST_NONFINITE = 1u << 1,     /* a used logit is NaN or +inf                    */
+  SV_ST_EMPTY = 1u << 2,         /* every logit of a used row is -inf               */
+  SV_ST_ZERO_RESIDUAL = 1u << 3, /* (q-p)+ had no mass (rounding): drew from q_n    */
+  SV_ST_PZERO = 1u << 4,         /* a tested draft token had p_t(d_t) = 0           */
+  SV_ST_MARGIN = 1u << 5,        /* a device-side decision was within 1e-6 of its
+                                    boundary (an accept ratio, a CDF boundary or a
+                                    nucleus cumulative mass)                        */
+  SV_ST_PARAM = 1u << 6,         /* invalid per-row parameter (K_b, mode, tau, k,
+                                    top_p)                                          */
+  SV_ST_FULLSELECT = 1u << 7,    /* a top-k/top-p threshold needed the full-row
+                                    selection (slow path)                           */
+  SV_ST_REREAD = 1u << 8         /* the final draw re-read full logit rows           */
+};
+
+/* Create-time capacity.  vocab is fixed for the handle; 1 <= vocab <= 2^22,
+ * max_batch >= 1, 0 <= max_k <= 64.  device is the HIP device ordinal. */
+typedef struct {
+  int32_t max_batch;
+  int32_t max_k;
+  int32_t vocab;
+  int32_t dtype; /* sv_dtype */
+  int32_t device;
+} sv_config;
+
+/* Per-call arguments.  Every pointer is a device pointer on the handle's
+ * device; the caller owns all of them and keeps them alive until the work
+ * on the stream has finished.  All arrays are dense and row-major.
+ *
+ *   target_logits [B][K_max+1][V]  dtype of the handle.  Target position t
+ *                                  scores draft slot t; position K_b is the
+ *                                  bonus position.  Rows t > K_b are never
+ *                                  read (padding may hold anything).
+ *   draft_logits  [B][K_max][V]    rows t >= K_b are never read.  May be NULL
+ *                                  when K_max = 0.
+ *   draft_tokens  [B][K_max] int32 may be NULL when K_max = 0.
+ *   k_per_row     [B] int32 in [0, K_max], or NULL (every row uses K_max).
+ *   mode          [B] uint8 sv_mode, or NULL (default_mode).
+ *   temperature   [B] float > 0, or NULL (default_temperature).
+ *   top_k         [B] int32 in [1, V], or NULL (default_top_k).
+ *   top_p         [B] float in (0, 1], or NULL (default_top_p).
+ *   seed, row_offset: see the RNG note above.
+ * Outputs:
+ *   accepted      [B] int32: n in [0, K_b], or -1 for an error row.
+ *   out_tokens    [B][K_max+1] int32: d_0..d_{n-1}, then the resampled or
+ *                                  bonus token, then -1.
+ *   row_status    [B] uint32 SV_ST_* bits, or NULL.
+ *   diag          [B][K_max][2] float: (q_t(d_t), p_t(d_t)) for t < K_b,
+ *                                  NaN elsewhere and on error rows; or NULL.
+ * B = 0 is a no-op. */
+typedef struct {
+  int32_t B;
+  int32_t K_max;
+  const void* target_logits;
+  const void* draft_logits;
+  const int32_t* draft_tokens;
+  const int32_t* k_per_row;
+  const uint8_t* mode;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t default_mode;
+  float default_temperature;
+  int32_t default_top_k;
+  float default_top_p;
+  uint64_t seed;
+  uint64_t row_offset;
+  int32_t* accepted;
+  int32_t* out_tokens;
+  uint32_t* row_status;
+  float* diag;
+} sv_args;
+
+/* Creates a handle for cfg->device and allocates its device workspace
+ * (hipMalloc).  On success *out receives the handle and SV_OK is returned;
+ * on failure *out is NULL and a negative code is returned. */
+int spec_verify_create(sv_handle_t* out, const sv_config* cfg);
+
+/* Enqueues the whole step on `stream` (a hipStream_t; NULL is the null
+ * stream).  Validates the arguments on the host first (see
+ * spec_verify_validate) and returns a negative code without launching
+ * anything if they are invalid.  Data errors found on the device are
+ * reported per sequence through row_status.  No allocation, no host
+ * synchronisation. */
+int spec_verify_run(sv_handle_t h, const sv_args* args, void* stream);
+
+/* Waits for the last run enqueued through h, then frees its workspace and
+ * the handle.  NULL is accepted. */
+int spec_verify_destroy(sv_handle_t h);
+
+/* Host-only check of a (config, args) pair: pointer presence, sizes
+ * against the capacity, default parameters that some row may use.  Makes no
+ * HIP call and dereferences no device pointer. */
+int spec_verify_validate(const sv_config* cfg, const sv_args* args);
+
+/* Bytes of device workspace spec_verify_create allocates for cfg, or 0 if
+ * cfg is invalid.  Host-only. */
+uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
+
+/* Text of the last error reported on the calling thread ("" if none). */
+const char* spec_verify_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */
