@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the verify-and-resample step on one MI355X.
+
+One step = one spec_verify_run call over a batch of B=64 sequences, K=4
+draft tokens, V=128256 bf16 logits, nucleus top-p 0.8 at temperature 0.8 on
+both models (target N(0, 4^2) plus +8 on 20 tokens per position, draft =
+target + N(0, 0.7^2)): the whole hot path (filter thresholds, softmax
+statistics, accept walk, resample / bonus draw) in the library's kernel.
+
+Inputs are synthetic and resident in HBM before timing; R input sets rotate
+so the 256 MB Infinity Cache cannot serve repeated reads.  Draft tokens are
+drawn by the library itself (the step with K = 0 on the draft rows).
+
+Prints one JSON line: value = rows/s; roofline = algorithmic logit bytes per
+launch / average kernel time (HIP events on the launch stream) against the
+8 TB/s HBM peak; cpu_baseline = the fp64 oracle on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verify rows/s and logits GB/s (% of HBM peak), B=64 K=4 V=128256 bf16"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("sv_kernels.hip", "sv_host.hip", "sv_internal.h"):
+        with open(os.path.join(ROOT, "speculative_sampling_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"verify_kernel_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets (>= 4 defeats the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+              "(rows are independent; a multi-GPU run would shard B with row_offset).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from speculative_sampling_amd import binding, workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    name = workloads.HEADLINE
+    sets = []
+    for r in range(args.sets):
+        w = workloads.config(name, device=dev, gen_seed=1000 + r, seed=r)
+        sets.append(w)
+    v = binding.Verifier(64, 4, 128256, torch.bfloat16, 0)
+    sampler = binding.Verifier(64 * 4, 0, 128256, torch.bfloat16, 0)
+    for w in sets:
+        toks, st = sampler.sample(w.draft, seed=w.draft_seed, default_mode=w.default_mode,
+                                  default_temperature=w.default_temperature,
+                                  default_top_p=w.default_top_p)
+        w.draft_tokens = toks.to(torch.int32).contiguous()
+    torch.cuda.synchronize()
+    sampler.close()
+    w0 = sets[0]
+    B, K, V = w0.B, w0.K_max, w0.V
+    alg_bytes = w0.algorithmic_bytes()
+    outs = [v.outputs(B, K) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+    argss = [binding.make_args(w.target, w.draft, w.draft_tokens, accepted=o[0], out_tokens=o[1],
+                               row_status=o[2], diag=o[3], default_mode=w.default_mode,
+                               default_temperature=w.default_temperature,
+                               default_top_p=w.default_top_p, seed=w.seed)
+             for w, o in zip(sets, outs)]
+
+    def step(i):
+        binding.spec_verify_run(v.handle, argss[i % len(argss)], stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: events around every launch (one kernel per call here)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_kernel_ms = sum(per) / len(per)
+    ms_per_step = total_ms / args.steps
+    rows_per_s = B / (ms_per_step * 1e-3)
+    gbs_step = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (avg_kernel_ms * 1e-3) / 1e9
+
+    # acceptance actually achieved by the synthetic draft (context)
+    acc = torch.cat([o[0] for o in outs]).float()
+    alpha_tokens = float(acc.mean().item())
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(sets[0], args.cpu_seconds)
+
+    traffic = stored_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "K": K, "V": V, "dtype": "bf16", "mode": "top-p",
+                   "top_p": w0.default_top_p, "temperature": w0.default_temperature,
+                   "input_sets": len(sets), "parallelism": "single-gpu"},
+        "logits_GBps": gbs_step,
+        "pct_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS,
+        "kernel_ms": {"avg": avg_kernel_ms, "p10": per[len(per) // 10], "p50": per[len(per) // 2],
+                      "p90": per[(9 * len(per)) // 10]},
+        "mean_accepted": alpha_tokens,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    v.close()
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it stands, on whole sequences of the same workload until
+    the time budget is spent; reported in rows/s (sequences per second)."""
+    import oracle
+    from speculative_sampling_amd import workloads
+
+    tgt = workloads.host_array(w.target)
+    drf = workloads.host_array(w.draft)
+    toks = w.draft_tokens.cpu().numpy()
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.B and time.perf_counter() - t0 < budget_s:
+        oracle.verify(tgt[done:done + 1], drf[done:done + 1], toks[done:done + 1],
+                      default_mode=w.default_mode, default_temperature=w.default_temperature,
+                      default_top_p=w.default_top_p, seed=w.seed, row_offset=done)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of input set 0 ({el:.1f} s, single-threaded fp64)"}
+
+
+if __name__ == "__main__":
+    main()

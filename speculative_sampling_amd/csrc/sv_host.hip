@@ -1,0 +1,258 @@
+// Host side of libspec_verify: the C ABI declared in include/spec_verify.h.
+//
+// create  allocates the device workspace once (chunk records, candidate
+//         lists, row records and the self-resetting arrival counters);
+// run     validates on the host, then enqueues one fused kernel per batch of
+//         at most kMaxBlocksPerLaunch work-groups on the caller's stream;
+// destroy waits for the last run and frees.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "spec_verify.h"
+#include "sv_internal.h"
+
+struct sv_handle_s {
+  sv_config cfg;
+  int S, L, cap, R_max;
+  void* ws;
+  size_t ws_bytes;
+  sv::ChunkRec* chunks;
+  float2* cands;
+  sv::RowRec* rows;
+  uint32_t* rowctr;
+  uint32_t* seqctr;
+  hipEvent_t last;
+  bool has_run;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+// Work-groups per launch: keeps the grid's work-item count below 2^32.
+constexpr size_t kMaxBlocksPerLaunch = (size_t)1 << 23;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+struct Geometry {
+  int S, L, cap, R_max;
+  size_t off_chunks, off_cands, off_rows, off_rowctr, off_seqctr, total;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_config(const sv_config* cfg) {
+  if (!cfg) return fail(SV_EINVAL, "config is NULL");
+  if (cfg->dtype != SV_F32 && cfg->dtype != SV_BF16) return fail(SV_EDTYPE, "unknown dtype");
+  if (cfg->vocab < 1 || cfg->vocab > sv::kMaxVocab) return fail(SV_EINVAL, "vocab must be in [1, 2^22]");
+  if (cfg->max_batch < 1) return fail(SV_EINVAL, "max_batch must be >= 1");
+  if (cfg->max_k < 0 || cfg->max_k > sv::kMaxK) return fail(SV_EINVAL, "max_k must be in [0, 64]");
+  if (cfg->device < 0) return fail(SV_EINVAL, "device must be >= 0");
+  return SV_OK;
+}
+
+Geometry geometry(const sv_config* cfg) {
+  Geometry g;
+  const int V = cfg->vocab;
+  const int ve = cfg->dtype == SV_BF16 ? 8 : 4;
+  const int chunk_cap = sv::chunk_capacity(cfg->dtype);
+  g.S = (V + chunk_cap - 1) / chunk_cap;
+  const int per = (V + g.S - 1) / g.S;
+  g.L = (per + ve - 1) / ve * ve;
+  g.cap = std::min(sv::kCandCap, g.L);
+  g.R_max = 2 * cfg->max_k + 1;
+  const size_t rows = (size_t)cfg->max_batch * g.R_max;
+  size_t off = 0;
+  g.off_chunks = off;
+  off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
+  g.off_cands = off;
+  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(float2), 256);
+  g.off_rows = off;
+  off = align_up(off + rows * sizeof(sv::RowRec), 256);
+  g.off_rowctr = off;
+  off = align_up(off + rows * sizeof(uint32_t), 256);
+  g.off_seqctr = off;
+  off = align_up(off + (size_t)cfg->max_batch * sizeof(uint32_t), 256);
+  g.total = off;
+  return g;
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t spec_verify_workspace_bytes(const sv_config* cfg) {
+  if (check_config(cfg) != SV_OK) return 0;
+  return geometry(cfg).total;
+}
+
+int spec_verify_validate(const sv_config* cfg, const sv_args* a) {
+  int rc = check_config(cfg);
+  if (rc != SV_OK) return rc;
+  if (!a) return fail(SV_EINVAL, "args is NULL");
+  if (a->B < 0) return fail(SV_EINVAL, "B must be >= 0");
+  if (a->K_max < 0) return fail(SV_EINVAL, "K_max must be >= 0");
+  if (a->B > cfg->max_batch) return fail(SV_ECAPACITY, "B exceeds max_batch");
+  if (a->K_max > cfg->max_k) return fail(SV_ECAPACITY, "K_max exceeds max_k");
+  if (a->B == 0) return SV_OK;
+  if (!a->target_logits) return fail(SV_EINVAL, "target_logits is NULL");
+  if (a->K_max > 0 && (!a->draft_logits || !a->draft_tokens))
+    return fail(SV_EINVAL, "draft_logits and draft_tokens are required when K_max > 0");
+  if (!a->accepted || !a->out_tokens) return fail(SV_EINVAL, "accepted and out_tokens are required");
+  // Defaults are checked only where some row can use them.
+  if (!a->mode && (a->default_mode < SV_PLAIN || a->default_mode > SV_GREEDY))
+    return fail(SV_EINVAL, "default_mode is not an sv_mode");
+  const bool any_mode = a->mode != nullptr;
+  const int dm = a->default_mode;
+  if (!a->temperature && (any_mode || dm != SV_GREEDY) && !finite_pos(a->default_temperature))
+    return fail(SV_EINVAL, "default_temperature must be finite and > 0");
+  if (!a->top_k && (any_mode || dm == SV_TOPK) &&
+      (a->default_top_k < 1 || a->default_top_k > cfg->vocab))
+    return fail(SV_EINVAL, "default_top_k must be in [1, V]");
+  if (!a->top_p && (any_mode || dm == SV_TOPP) &&
+      !(a->default_top_p > 0.0f && a->default_top_p <= 1.0f))
+    return fail(SV_EINVAL, "default_top_p must be in (0, 1]");
+  return SV_OK;
+}
+
+int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
+  if (!out) return fail(SV_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc != SV_OK) return rc;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
+  if (hipSetDevice(cfg->device) != hipSuccess) return fail(SV_EHIP, "hipSetDevice failed");
+  Geometry g = geometry(cfg);
+  sv_handle_s* h = new (std::nothrow) sv_handle_s();
+  if (!h) {
+    (void)hipSetDevice(prev);
+    return fail(SV_ENOMEM, "host allocation failed");
+  }
+  h->cfg = *cfg;
+  h->S = g.S;
+  h->L = g.L;
+  h->cap = g.cap;
+  h->R_max = g.R_max;
+  h->ws_bytes = g.total;
+  hipError_t e = hipMalloc(&h->ws, g.total);
+  if (e != hipSuccess) {
+    delete h;
+    (void)hipSetDevice(prev);
+    return fail(SV_ENOMEM, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
+  }
+  char* base = static_cast<char*>(h->ws);
+  h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
+  h->cands = reinterpret_cast<float2*>(base + g.off_cands);
+  h->rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
+  h->rowctr = reinterpret_cast<uint32_t*>(base + g.off_rowctr);
+  h->seqctr = reinterpret_cast<uint32_t*>(base + g.off_seqctr);
+  // The arrival counters start at zero; every run leaves them at zero.
+  e = hipMemset(base + g.off_rowctr, 0, g.total - g.off_rowctr);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    (void)hipSetDevice(prev);
+    return fail(SV_EHIP, std::string("workspace initialisation failed: ") + hipGetErrorString(e));
+  }
+  h->has_run = false;
+  (void)hipSetDevice(prev);
+  *out = h;
+  return SV_OK;
+}
+
+int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
+  if (!h) return fail(SV_EINVAL, "handle is NULL");
+  int rc = spec_verify_validate(&h->cfg, a);
+  if (rc != SV_OK) return rc;
+  if (a->B == 0) return SV_OK;
+  const sv_config& cfg = h->cfg;
+  const int es = cfg.dtype == SV_BF16 ? 2 : 4;
+  // 16-byte vector loads need every row start on a 16-byte boundary.
+  const bool vec = ((size_t)cfg.vocab * es) % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
+                   (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);
+  sv::KParams p;
+  p.B = a->B;
+  p.K_max = a->K_max;
+  p.V = cfg.vocab;
+  p.R = 2 * a->K_max + 1;
+  p.S = h->S;
+  p.L = h->L;
+  p.cap = h->cap;
+  p.b_base = 0;
+  p.target = a->target_logits;
+  p.draft = a->draft_logits;
+  p.tokens = a->draft_tokens;
+  p.kpr = a->k_per_row;
+  p.mode = a->mode;
+  p.temp = a->temperature;
+  p.topk = a->top_k;
+  p.topp = a->top_p;
+  p.dmode = a->default_mode;
+  p.dtemp = a->default_temperature;
+  p.dtopk = a->default_top_k;
+  p.dtopp = a->default_top_p;
+  p.seed = a->seed;
+  p.row_offset = a->row_offset;
+  p.accepted = a->accepted;
+  p.out_tokens = a->out_tokens;
+  p.status = a->row_status;
+  p.diag = a->diag;
+  p.chunks = h->chunks;
+  p.cands = h->cands;
+  p.rows = h->rows;
+  p.rowctr = h->rowctr;
+  p.seqctr = h->seqctr;
+
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
+  if (prev != cfg.device && hipSetDevice(cfg.device) != hipSuccess)
+    return fail(SV_EHIP, "hipSetDevice failed");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t per_seq = (size_t)p.R * p.S;
+  const int seq_per_launch = (int)std::max<size_t>(1, kMaxBlocksPerLaunch / per_seq);
+  hipError_t e = hipSuccess;
+  for (int b0 = 0; b0 < a->B && e == hipSuccess; b0 += seq_per_launch) {
+    p.b_base = b0;
+    const int nseq = std::min(seq_per_launch, a->B - b0);
+    e = sv::launch_verify(p, cfg.dtype, vec, nseq, s);
+  }
+  if (e == hipSuccess) e = hipEventRecord(h->last, s);
+  if (e == hipSuccess) h->has_run = true;
+  if (prev != cfg.device) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}
+
+int spec_verify_destroy(sv_handle_t h) {
+  if (!h) return SV_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->cfg.device);
+  hipError_t e = hipSuccess;
+  if (h->has_run) e = hipEventSynchronize(h->last);
+  (void)hipEventDestroy(h->last);
+  (void)hipFree(h->ws);
+  (void)hipSetDevice(prev);
+  delete h;
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("waiting for the last run failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal layout shared by the host code and the gfx950 kernels of
+// libspec_verify.  Not part of the public ABI (include/spec_verify.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+// Work-group shape of every kernel: 4 wave64s.
+constexpr int kThreads = 256;
+// Each thread keeps kLoads 16-byte vectors of its chunk in registers
+// (64 VGPRs): 128 bf16 or 64 fp32 logits.
+constexpr int kLoads = 16;
+// Candidate list capacity per chunk (tokens near the chunk max kept for the
+// top-k / nucleus threshold search).
+constexpr int kCandCap = 512;
+// Largest kept set the final draw handles from the candidate lists without
+// re-reading the logit rows.
+constexpr int kListMax = 512;
+// Largest number of chunks per row (V <= 2^22 with 16384 fp32 per chunk).
+constexpr int kMaxChunks = 256;
+constexpr int kMaxK = 64;
+constexpr int kMaxVocab = 1 << 22;
+
+inline int chunk_capacity(int dtype) { return kThreads * kLoads * (dtype == SV_BF16 ? 8 : 4); }
+
+// Per-(row, chunk) partial results written by the streaming pass.
+struct ChunkRec {
+  float m;         // chunk maximum of the raw logits (-inf if none is finite)
+  float cut;       // every token of the chunk with logit >= cut (and > -inf) is
+                   // in the chunk's candidate list; +inf when the list is
+                   // incomplete
+  double z;        // sum over the chunk of 2^((x - m) * c2)   (plain, nucleus)
+  int32_t cnt;     // candidates stored
+  int32_t arg;     // lowest index whose logit equals m      (greedy)
+  uint32_t flags;  // kCfNonFinite
+  int32_t pad;
+};
+constexpr uint32_t kCfNonFinite = 1u;
+
+// Per logit row (one model at one position of one sequence) after merging.
+struct RowRec {
+  float M;          // row maximum (raw logit)
+  float T;          // kept set is {x >= T}; -inf for plain
+  double c2;        // log2(e) / temperature
+  double Zs;        // kept mass: sum_{x >= T} 2^((x - M) * c2)
+  double pid;       // probability of this row's draft token (NaN if none)
+  int32_t g;        // greedy argmax
+  int32_t n_keep;   // |{x >= T}|, -1 if not counted
+  uint32_t flags;   // SV_ST_* error/info bits of the row, plus kRf* below
+  int32_t pad;
+};
+constexpr uint32_t kRfListOk = 1u << 16;  // kept set is in the candidate lists
+
+struct KParams {
+  int32_t B, K_max, V, R, S, L, cap;
+  int32_t b_base;  // first sequence of this launch
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* kpr;
+  const uint8_t* mode;
+  const float* temp;
+  const int32_t* topk;
+  const float* topp;
+  int32_t dmode;
+  float dtemp;
+  int32_t dtopk;
+  float dtopp;
+  uint64_t seed;
+  uint64_t row_offset;
+  int32_t* accepted;
+  int32_t* out_tokens;
+  uint32_t* status;
+  float* diag;
+  ChunkRec* chunks;
+  float2* cands;
+  RowRec* rows;
+  uint32_t* rowctr;
+  uint32_t* seqctr;
+};
+
+// Enqueues the fused verify kernel for sequences [p.b_base, p.b_base + nseq).
+hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,143 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/spec_verify.h declares, and its host-side validation
+rejects bad arguments before anything is launched.  Also checks that the
+oracle and the library share no code."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_sampling_amd import binding
+from speculative_sampling_amd.binding import (SV_BF16, SV_ECAPACITY, SV_EDTYPE, SV_EINVAL, SV_F32,
+                                              SV_GREEDY, SV_OK, SV_PLAIN, SV_TOPK, SV_TOPP, SvArgs)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                               reason="libspec_verify.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_binding_lists_every_header_function():
+    assert sorted(binding.EXPORTS) == header_functions()
+
+
+@needs_lib
+def test_library_exports_every_header_function():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def _args(**kw):
+    # fake, never dereferenced device addresses: validation is host-only
+    a = SvArgs()
+    a.B, a.K_max = kw.get("B", 4), kw.get("K_max", 2)
+    a.target_logits = kw.get("target", 0x10000)
+    a.draft_logits = kw.get("draft", 0x20000)
+    a.draft_tokens = kw.get("tokens", 0x30000)
+    a.accepted = kw.get("accepted", 0x40000)
+    a.out_tokens = kw.get("out_tokens", 0x50000)
+    a.mode = kw.get("mode", None)
+    a.temperature = kw.get("temperature", None)
+    a.top_k = kw.get("top_k_arr", None)
+    a.top_p = kw.get("top_p_arr", None)
+    a.default_mode = kw.get("default_mode", SV_PLAIN)
+    a.default_temperature = kw.get("tau", 1.0)
+    a.default_top_k = kw.get("top_k", 1)
+    a.default_top_p = kw.get("top_p", 1.0)
+    return a
+
+
+def validate(args, max_batch=8, max_k=4, vocab=100, dtype=SV_BF16):
+    return binding.spec_verify_validate(max_batch, max_k, vocab, dtype, args)
+
+
+@needs_lib
+def test_validate_accepts_good_arguments():
+    assert validate(_args()) == SV_OK
+    assert validate(_args(B=0, target=None, accepted=None)) == SV_OK
+    assert validate(_args(K_max=0, draft=None, tokens=None)) == SV_OK
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    ({"target": None}, SV_EINVAL),
+    ({"draft": None}, SV_EINVAL),
+    ({"tokens": None}, SV_EINVAL),
+    ({"accepted": None}, SV_EINVAL),
+    ({"out_tokens": None}, SV_EINVAL),
+    ({"B": 9}, SV_ECAPACITY),
+    ({"K_max": 5}, SV_ECAPACITY),
+    ({"B": -1}, SV_EINVAL),
+    ({"default_mode": 7}, SV_EINVAL),
+    ({"tau": 0.0}, SV_EINVAL),
+    ({"tau": float("nan")}, SV_EINVAL),
+    ({"default_mode": SV_TOPK, "top_k": 0}, SV_EINVAL),
+    ({"default_mode": SV_TOPK, "top_k": 101}, SV_EINVAL),
+    ({"default_mode": SV_TOPP, "top_p": 0.0}, SV_EINVAL),
+    ({"default_mode": SV_TOPP, "top_p": 1.5}, SV_EINVAL),
+    ({"mode": 0x60000, "top_p": 0.0}, SV_EINVAL),  # some row may use the default
+])
+def test_validate_rejects(kw, code):
+    assert validate(_args(**kw)) == code
+    assert binding.spec_verify_last_error() != ""
+
+
+@needs_lib
+def test_validate_ignores_defaults_no_row_uses():
+    # greedy ignores the temperature; plain ignores top-k / top-p defaults
+    assert validate(_args(default_mode=SV_GREEDY, tau=0.0)) == SV_OK
+    assert validate(_args(default_mode=SV_PLAIN, top_k=0, top_p=0.0)) == SV_OK
+    # per-row arrays replace the defaults
+    assert validate(_args(temperature=0x70000, tau=-1.0)) == SV_OK
+
+
+@needs_lib
+def test_validate_config():
+    assert validate(_args(), dtype=7) == SV_EDTYPE
+    assert validate(_args(), vocab=0) == SV_EINVAL
+    assert validate(_args(), vocab=(1 << 22) + 1) == SV_EINVAL
+    assert validate(_args(), max_k=65) == SV_EINVAL
+
+
+@needs_lib
+def test_workspace_bytes():
+    small = binding.spec_verify_workspace_bytes(64, 4, 128256, SV_BF16)
+    big = binding.spec_verify_workspace_bytes(128, 4, 128256, SV_BF16)
+    assert 0 < small < big < 1 << 32
+    assert binding.spec_verify_workspace_bytes(64, 4, 0, SV_BF16) == 0
+    assert binding.spec_verify_workspace_bytes(8, 8, 32000, SV_F32) > 0
+
+
+def test_oracle_and_library_share_no_code():
+    lib_dir = os.path.join(ROOT, "speculative_sampling_amd")
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "oracle")):
+        for f in files:
+            if f.endswith((".cpp", ".h", ".py")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "speculative_sampling_amd" not in text and "sv_internal" not in text, f
+                assert "spec_verify.h" not in text, f
+    for dirpath, _, files in os.walk(lib_dir):
+        for f in files:
+            if f.endswith((".hip", ".h", ".py", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "oracle.h" not in text, f
+                assert "from oracle" not in text, f
+
+
+def test_product_path_fails_loudly_without_library(tmp_path):
+    missing = str(tmp_path / "libspec_verify.so")
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            binding.load_library(missing)
+    finally:
+        binding._lib = saved
