@@ -1,9 +1,10 @@
 // Host side of libspec_verify: the C ABI declared in include/spec_verify.h.
 //
 // create  allocates the device workspace once (chunk records, candidate
-//         lists, row records and the self-resetting arrival counters);
-// run     validates on the host, then enqueues one fused kernel per batch of
-//         at most kMaxBlocksPerLaunch work-groups on the caller's stream;
+//         lists, row records, kept lists);
+// run     validates on the host, then enqueues the kernels of the step for
+//         batches of at most kMaxBlocksPerLaunch work-groups on the caller's
+//         stream;
 // destroy waits for the last run and frees.
 
 #include <hip/hip_runtime.h>
@@ -26,8 +27,7 @@ struct sv_handle_s {
   sv::ChunkRec* chunks;
   float2* cands;
   sv::RowRec* rows;
-  uint32_t* rowctr;
-  uint32_t* seqctr;
+  sv::KeptEntry* kept;
   hipEvent_t last;
   bool has_run;
 };
@@ -45,7 +45,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, cap, R_max;
-  size_t off_chunks, off_cands, off_rows, off_rowctr, off_seqctr, total;
+  size_t off_chunks, off_cands, off_rows, off_kept, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -78,10 +78,8 @@ Geometry geometry(const sv_config* cfg) {
   off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(float2), 256);
   g.off_rows = off;
   off = align_up(off + rows * sizeof(sv::RowRec), 256);
-  g.off_rowctr = off;
-  off = align_up(off + rows * sizeof(uint32_t), 256);
-  g.off_seqctr = off;
-  off = align_up(off + (size_t)cfg->max_batch * sizeof(uint32_t), 256);
+  g.off_kept = off;
+  off = align_up(off + rows * sv::kListMax * sizeof(sv::KeptEntry), 256);
   g.total = off;
   return g;
 }
@@ -158,11 +156,8 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
   h->cands = reinterpret_cast<float2*>(base + g.off_cands);
   h->rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
-  h->rowctr = reinterpret_cast<uint32_t*>(base + g.off_rowctr);
-  h->seqctr = reinterpret_cast<uint32_t*>(base + g.off_seqctr);
-  // The arrival counters start at zero; every run leaves them at zero.
-  e = hipMemset(base + g.off_rowctr, 0, g.total - g.off_rowctr);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
+  h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
+  e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
@@ -217,8 +212,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.chunks = h->chunks;
   p.cands = h->cands;
   p.rows = h->rows;
-  p.rowctr = h->rowctr;
-  p.seqctr = h->seqctr;
+  p.kept = h->kept;
 
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");

@@ -11,13 +11,15 @@ namespace sv {
 
 // Work-group shape of every kernel: 4 wave64s.
 constexpr int kThreads = 256;
-// Each thread keeps kLoads 16-byte vectors of its chunk in registers
-// (64 VGPRs): 128 bf16 or 64 fp32 logits.
+// Each thread of the streaming kernel keeps kLoads 16-byte vectors of its
+// chunk in registers (64 VGPRs): 128 bf16 or 64 fp32 logits.
 constexpr int kLoads = 16;
 // Candidate list capacity per chunk (tokens near the chunk max kept for the
 // top-k / nucleus threshold search).
-constexpr int kCandCap = 512;
-// Largest kept set the final draw handles from the candidate lists without
+constexpr int kCandCap = 1024;
+// Candidates of one row the merge kernel caches in LDS.
+constexpr int kMergeCache = 2048;
+// Largest kept set the final draw takes from the merged kept list without
 // re-reading the logit rows.
 constexpr int kListMax = 512;
 // Largest number of chunks per row (V <= 2^22 with 16384 fp32 per chunk).
@@ -27,7 +29,7 @@ constexpr int kMaxVocab = 1 << 22;
 
 inline int chunk_capacity(int dtype) { return kThreads * kLoads * (dtype == SV_BF16 ? 8 : 4); }
 
-// Per-(row, chunk) partial results written by the streaming pass.
+// Per-(row, chunk) partial results written by the streaming kernel.
 struct ChunkRec {
   float m;         // chunk maximum of the raw logits (-inf if none is finite)
   float cut;       // every token of the chunk with logit >= cut (and > -inf) is
@@ -53,7 +55,16 @@ struct RowRec {
   uint32_t flags;   // SV_ST_* error/info bits of the row, plus kRf* below
   int32_t pad;
 };
-constexpr uint32_t kRfListOk = 1u << 16;  // kept set is in the candidate lists
+// The row's kept set is stored, in vocabulary order with its probabilities,
+// in the row's KeptEntry list.
+constexpr uint32_t kRfListOk = 1u << 16;
+
+// One token of a target row's kept set: vocabulary index and probability.
+struct KeptEntry {
+  int32_t idx;
+  int32_t pad;
+  double q;
+};
 
 struct KParams {
   int32_t B, K_max, V, R, S, L, cap;
@@ -79,11 +90,12 @@ struct KParams {
   ChunkRec* chunks;
   float2* cands;
   RowRec* rows;
-  uint32_t* rowctr;
-  uint32_t* seqctr;
+  KeptEntry* kept;  // [rows][kListMax]
 };
 
-// Enqueues the fused verify kernel for sequences [p.b_base, p.b_base + nseq).
+// Enqueues the three kernels of one call for sequences
+// [p.b_base, p.b_base + nseq): the streaming chunk pass (one instance per
+// sampling mode present), the row merge and the per-sequence finalize.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream);
 
 }  // namespace sv

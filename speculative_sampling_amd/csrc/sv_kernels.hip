@@ -1,23 +1,24 @@
 // gfx950 kernels of the verify-and-resample step of speculative sampling.
 //
-// One fused launch per call.  The grid is (sequence, logit row, chunk):
-// every used logit row (target positions 0..K_b, draft positions 0..K_b-1)
-// is split into S chunks of at most 32768 bf16 / 16384 fp32 logits, and each
-// work-group streams one chunk from HBM into registers exactly once.  The
-// work is chained without host round trips or extra launches:
+// A call runs three kernels on the caller's stream; the kernel boundaries
+// order them, so no work-group ever waits for another:
 //
-//   chunk pass  (every WG)       max, sum of 2^((x - m) c2), nucleus / top-k
-//                                candidates, greedy argmax -> ChunkRec
-//   row merge   (last chunk WG   log-sum-exp merge, threshold selection,
-//                of a row)       kept mass, probability of the draft token
-//                                -> RowRec
-//   finalize    (last row WG of  accept walk, first rejection, resample from
-//                a sequence)     normalize((q - p)+) or bonus draw, outputs
-//
-// "Last" is decided with a device-scope counter per row and per sequence
-// (release fence, atomic increment, acquire fence); no work-group ever waits
-// for another, so there is no co-residency assumption.  The counters reset
-// themselves, so a call needs no memset.
+//   chunk_kernel    grid (sequence, logit row, chunk).  Every used logit row
+//                   (target positions 0..K_b, draft positions 0..K_b-1) is
+//                   split into S chunks of at most 32768 bf16 / 16384 fp32
+//                   logits; each work-group streams its chunk from HBM into
+//                   registers exactly once and reduces it: maximum, sum of
+//                   2^((x - m) c2), the candidate list of the nucleus / top-k
+//                   threshold search, the greedy argmax.  One instance per
+//                   sampling mode keeps the registers of each mode's loop
+//                   minimal.
+//   merge_kernel    grid (sequence, logit row).  Log-sum-exp merge of the
+//                   chunks, radix selection of the threshold over the
+//                   candidates (cached in LDS), kept mass, the probability of
+//                   the row's draft token, and for target rows the kept set
+//                   in vocabulary order with its probabilities.
+//   final_kernel    grid (sequence).  Accept walk, first rejection, resample
+//                   from normalize((q - p)+) or the bonus draw, outputs.
 //
 // The step follows the pages' rule (FDE Interviews breakdown of Chen et al.,
 // section 01 and its figure; paperlayer.ai summary of arXiv 2302.01318,
@@ -38,14 +39,16 @@ namespace sv {
 namespace {
 
 constexpr float kInf = __builtin_inff();
+constexpr float kMaxFinite = 3.402823466e38f;
 constexpr double kLog2e = 1.4426950408889634074;
 // Fixed-point scale of masses (units of the row's largest term): integer
 // accumulation makes histogram sums independent of atomic order.
 constexpr double kFix = 1099511627776.0;  // 2^40
 constexpr double kWindow = 1e-6;
-// Nucleus candidates: tokens whose term is within 2^-12 of the chunk's
-// largest term.
-constexpr float kCandLog2 = 12.0f;
+// Nucleus candidates: tokens whose term is within 2^-10 of the chunk's
+// largest term (on the pages' workloads a window of 2^-8 to 2^-9.4 already
+// covers the nucleus; a list that overflows is retried with 2^-8, 2^-6).
+constexpr float kCandLog2 = 10.0f;
 
 constexpr uint32_t kPurposeAccept = 0, kPurposeResample = 1, kPurposeBonus = 2;
 constexpr uint32_t kErrBits = SV_ST_TOKEN | SV_ST_NONFINITE | SV_ST_EMPTY | SV_ST_PARAM;
@@ -104,6 +107,32 @@ __device__ __forceinline__ float load_logit(const void* row, int e) {
     return static_cast<const float*>(row)[e];
 }
 
+// The vector of VE logits starting at e0 (< c1), with -inf past c1.
+template <int DT, bool VEC>
+__device__ __forceinline__ uint4 load_vec(const char* row, int e0, int c1) {
+  constexpr int VE = Fmt<DT>::VE, ES = Fmt<DT>::ES;
+  if constexpr (VEC) {
+    return *reinterpret_cast<const uint4*>(row + (size_t)e0 * ES);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (DT == SV_BF16) {
+        const int e = e0 + 2 * j;
+        const uint16_t* r16 = reinterpret_cast<const uint16_t*>(row);
+        const uint32_t lo = e < c1 ? (uint32_t)r16[e] : 0xff80u;
+        const uint32_t hi = e + 1 < c1 ? (uint32_t)r16[e + 1] : 0xff80u;
+        w[j] = lo | (hi << 16);
+      } else {
+        const int e = e0 + j;
+        w[j] = e < c1 ? reinterpret_cast<const uint32_t*>(row)[e] : 0xff800000u;
+      }
+    }
+    (void)VE;
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Order-preserving key of a float (-0 is folded onto +0 so equal values
 // share a key).
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -146,6 +175,7 @@ struct Red {
   float f[4];
   double d[4];
   int i[4];
+  unsigned long long u[4];
 };
 
 __device__ __forceinline__ float block_max(float v, Red& r) {
@@ -188,6 +218,15 @@ __device__ __forceinline__ int block_max_i(int v, Red& r) {
   __syncthreads();
   return max(max(r.i[0], r.i[1]), max(r.i[2], r.i[3]));
 }
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, Red& r) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.u[w] = v;
+  __syncthreads();
+  return (r.u[0] + r.u[1]) + (r.u[2] + r.u[3]);
+}
 
 // Exclusive prefix sum over the work-group in thread order (fp64).
 __device__ __forceinline__ double block_exclusive_scan(double v, double* total, Red& r) {
@@ -215,10 +254,14 @@ struct SeqParams {
   bool valid;
 };
 
+__device__ __forceinline__ int raw_mode(const KParams& P, int b) {
+  return P.mode ? (int)P.mode[b] : P.dmode;
+}
+
 __device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
   SeqParams s;
   s.Kb = P.kpr ? P.kpr[b] : P.K_max;
-  s.mode = P.mode ? (int)P.mode[b] : P.dmode;
+  s.mode = raw_mode(P, b);
   s.tau = P.temp ? P.temp[b] : P.dtemp;
   s.topk = P.topk ? P.topk[b] : P.dtopk;
   s.topp = P.topp ? P.topp[b] : P.dtopp;
@@ -235,38 +278,28 @@ __device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
   return s;
 }
 
-// --------------------------------------------------------- shared mem ----
+template <int DT>
+__device__ __forceinline__ const void* row_ptr(const KParams& P, int b, bool tgt, int t) {
+  constexpr int ES = Fmt<DT>::ES;
+  const size_t r = tgt ? ((size_t)b * (P.K_max + 1) + t) : ((size_t)b * P.K_max + t);
+  return static_cast<const char*>(tgt ? P.target : P.draft) + r * (size_t)P.V * ES;
+}
+
+// Row r of a sequence: target positions 0..K_max, then draft positions.
+__device__ __forceinline__ bool decode_row(const KParams& P, const SeqParams& sp, int r, bool* tgt, int* t) {
+  *tgt = r <= P.K_max;
+  *t = *tgt ? r : r - P.K_max - 1;
+  return *tgt ? (*t <= sp.Kb) : (*t < sp.Kb);
+}
+
+// ======================================================= chunk kernel ====
+
 struct SmemChunk {
   float2 cand[kCandCap];
   int cnt;
-};
-struct SmemMerge {
-  ChunkRec crec[kMaxChunks];
-  uint32_t hc[256];
-  unsigned long long hm[256];
-  uint32_t sel_digit;
-  uint32_t sel_hit;
-};
-struct SmemFinal {
-  float x[kListMax];
-  int idx[kListMax];
-  float sx[kListMax];
-  int sidx[kListMax];
-  double w[kListMax];
-  double c[kListMax];
-  int n;
-};
-struct Smem {
-  union {
-    SmemChunk ch;
-    SmemMerge mg;
-    SmemFinal fin;
-  };
   Red red;
-  int flag;
 };
 
-// ------------------------------------------------------- chunk pass -----
 // Loads this thread's part of chunk [c0, c1) into registers: vector i holds
 // logits c0 + (i * 256 + tid) * VE + [0, VE).  Every load is issued
 // unconditionally from a clamped in-bounds address and the out-of-range
@@ -320,21 +353,53 @@ __device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoads], const char* row
 }
 
 // Hides the packed logits from the optimiser between passes so that each pass
-// unpacks them again instead of keeping 128 unpacked values live (which would
-// double the register footprint and spill).
+// unpacks them again instead of keeping 128 unpacked values live.
 __device__ __forceinline__ void fence_regs(uint4 (&buf)[kLoads]) {
 #pragma unroll
   for (int i = 0; i < kLoads; ++i)
     asm volatile("" : "+v"(buf[i].x), "+v"(buf[i].y), "+v"(buf[i].z), "+v"(buf[i].w));
 }
 
+// Appends (logit, index) of the elements >= c of one vector to the list.
+template <int DT>
+__device__ __forceinline__ void append_vec(const uint4& v, float c, int e0, int cap, SmemChunk& sm) {
+  constexpr int VE = Fmt<DT>::VE;
+#pragma unroll
+  for (int k = 0; k < VE; ++k) {
+    const float x = elem<DT>(v, k);
+    if (x >= c) {
+      const int pos = atomicAdd(&sm.cnt, 1);
+      if (pos < cap) sm.cand[pos] = make_float2(x, __int_as_float(e0 + k));
+    }
+  }
+}
+
+// Collects, from the vectors flagged in `mask` (re-read from memory, where
+// the chunk was just streamed from), every element >= cut.
+template <int DT, bool VEC>
+__device__ __forceinline__ int collect_masked(uint32_t mask, const char* row, float cut, int c0, int c1,
+                                              int cap, SmemChunk& sm) {
+  constexpr int VE = Fmt<DT>::VE;
+  const float c = fmaxf(cut, -kMaxFinite);
+  __syncthreads();
+  if (threadIdx.x == 0) sm.cnt = 0;
+  __syncthreads();
+  while (mask) {
+    const int i = __ffs(mask) - 1;
+    mask &= mask - 1;
+    const int e0 = c0 + (i * kThreads + (int)threadIdx.x) * VE;
+    append_vec<DT>(load_vec<DT, VEC>(row, e0, c1), c, e0, cap, sm);
+  }
+  __syncthreads();
+  return sm.cnt;
+}
+
+// Register-resident count of elements >= cut (wave ballots, no VGPRs).
 template <int DT>
 __device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut, Red& red) {
   constexpr int VE = Fmt<DT>::VE;
-  // -inf logits are never candidates
-  const float c = fmaxf(cut, -3.402823466e38f);
+  const float c = fmaxf(cut, -kMaxFinite);  // -inf logits are never candidates
   fence_regs(buf);
-  // wave-uniform count: compare into a lane mask, popcount on the scalar unit
   int n = 0;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i)
@@ -346,46 +411,29 @@ __device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut, Red& re
   return (red.i[0] + red.i[1]) + (red.i[2] + red.i[3]);
 }
 
-// Appends (logit, index) of this vector's elements >= c to the chunk list.
+// Per-thread bitmask of the vectors holding an element >= cut.
 template <int DT>
-__device__ __forceinline__ void append_vec(const uint4& v, float c, int e0, int cap, Smem& sm) {
+__device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut) {
   constexpr int VE = Fmt<DT>::VE;
-#pragma unroll
-  for (int k = 0; k < VE; ++k) {
-    const float x = elem<DT>(v, k);
-    if (x >= c) {
-      const int pos = atomicAdd(&sm.ch.cnt, 1);
-      if (pos < cap) sm.ch.cand[pos] = make_float2(x, __int_as_float(e0 + k));
-    }
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ void collect_ge(uint4 (&buf)[kLoads], float cut, int c0, int cap,
-                                           Smem& sm) {
-  constexpr int VE = Fmt<DT>::VE;
-  const float c = fmaxf(cut, -3.402823466e38f);
-  const int tid = threadIdx.x;
+  const float c = fmaxf(cut, -kMaxFinite);
   fence_regs(buf);
-  __syncthreads();
-  if (tid == 0) sm.ch.cnt = 0;
-  __syncthreads();
+  uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     bool any = false;
 #pragma unroll
     for (int k = 0; k < VE; ++k) any |= elem<DT>(buf[i], k) >= c;
-    if (any) append_vec<DT>(buf[i], c, c0 + (i * kThreads + tid) * VE, cap, sm);
+    mask |= any ? (1u << i) : 0u;
   }
-  __syncthreads();
+  return mask;
 }
 
-// Picks a cut such that the candidate count lies in [need, cap]; grows the
-// window from `d` (raw logit units below the chunk max) until `need` tokens
-// are in, then shrinks it while the list would overflow.  Returns +inf when
-// no such cut exists (the list would be incomplete).
+// Top-k window: a cut whose candidate count lies in [need, cap].  Grows the
+// window below the chunk max from d (logit units) until `need` tokens are in,
+// then bisects while the list would overflow.  +inf when none exists.
 template <int DT>
-__device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, float d, int need, int cap, Red& red) {
+__device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, float d, int need, int cap,
+                                            Red& red) {
   float lo = 0.0f;  // window known to hold < need tokens (or 0)
   float cut = mx - d;
   int n = count_ge<DT>(buf, cut, red);
@@ -393,7 +441,7 @@ __device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, floa
     lo = d;
     d *= 4.0f;
     cut = mx - d;
-    if (!(cut > -3.402823466e38f)) {  // window covers every finite logit
+    if (!(cut > -kMaxFinite)) {  // the window covers every finite logit
       cut = -kInf;
       n = count_ge<DT>(buf, cut, red);
       break;
@@ -407,76 +455,26 @@ __device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, floa
     if (!(mid > lo && mid < hi)) break;
     const float cm = mx - mid;
     const int nm = count_ge<DT>(buf, cm, red);
-    if (nm < need) {
-      lo = mid;
-    } else if (nm > cap) {
-      hi = mid;
-    } else {
-      return cm;
-    }
+    if (nm < need) lo = mid;
+    else if (nm > cap) hi = mid;
+    else return cm;
   }
   return kInf;
 }
 
-// Counting and collecting straight from the chunk in memory (cache-resident
-// after the streaming load); used only when a nucleus window overflows the
-// candidate list.
-template <int DT>
-__device__ __forceinline__ int count_ge_mem(const void* row, int c0, int c1, float cut, Red& red) {
-  const float c = fmaxf(cut, -3.402823466e38f);
-  int n = 0;
-  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) n += load_logit<DT>(row, e) >= c ? 1 : 0;
-  return block_sum_i(n, red);
-}
-
-template <int DT>
-__device__ __forceinline__ void collect_ge_mem(const void* row, int c0, int c1, float cut, int cap, Smem& sm) {
-  const float c = fmaxf(cut, -3.402823466e38f);
-  __syncthreads();
-  if (threadIdx.x == 0) sm.ch.cnt = 0;
-  __syncthreads();
-  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) {
-    const float x = load_logit<DT>(row, e);
-    if (x >= c) {
-      const int pos = atomicAdd(&sm.ch.cnt, 1);
-      if (pos < cap) sm.ch.cand[pos] = make_float2(x, __int_as_float(e));
-    }
-  }
-  __syncthreads();
-}
-
-// Largest window (below mx, in logit units) whose candidate count fits the
-// list: bisects between 0 (the maximum alone) and `d` (known to overflow).
-template <int DT>
-__device__ __forceinline__ float shrink_cut_mem(const void* row, int c0, int c1, float mx, float d, int cap, Red& red) {
-  float lo = 0.0f, hi = d, best = kInf;
-  if (count_ge_mem<DT>(row, c0, c1, mx, red) <= cap) best = mx;
-  for (int it = 0; it < 24 && best != kInf; ++it) {
-    const float mid = 0.5f * (lo + hi);
-    if (!(mid > lo && mid < hi)) break;
-    if (count_ge_mem<DT>(row, c0, c1, mx - mid, red) <= cap) {
-      lo = mid;
-      best = mx - mid;
-    } else {
-      hi = mid;
-    }
-  }
-  return best;
-}
-
-// One exp per logit: sum of 2^((x - mx) c2) over the thread's logits, and
-// (CAND) the candidates of the nucleus window x >= cut.  FMA selects the
-// 1-op exponent x*c2 - o (o = mx*c2 rounded), valid when |o| < 2^10.
-template <int DT, bool FMA, bool CAND>
-__device__ __forceinline__ float exp_pass(uint4 (&buf)[kLoads], float mx, float c2, float o, float cut,
-                                          int c0, int cap, Smem& sm) {
+// One exp per logit: returns this thread's sum of 2^((x - mx) c2) and sets in
+// *hits the vectors whose terms sum to >= 0.999 * 2^-10 (every element
+// >= cut lies in such a vector, up to rounding of the terms).  FMA selects
+// the 1-op exponent x*c2 - o (o = mx*c2 rounded), exact up to a common
+// offset |delta| <= 2^-14 when |o| < 2^10.
+template <int DT, bool FMA>
+__device__ __forceinline__ float exp_pass(uint4 (&buf)[kLoads], float mx, float c2, float o,
+                                          uint32_t* hits) {
   constexpr int VE = Fmt<DT>::VE;
-  const int tid = threadIdx.x;
-  // An element with x >= cut has a term >= 2^-12 (up to rounding), so a
-  // vector whose terms sum below 0.999 * 2^-12 holds no candidate.
-  const float hit_sum = 0.999f * 0.000244140625f;
+  const float hit_sum = 0.999f * 0.0009765625f;
   fence_regs(buf);
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     float e[VE];
@@ -491,23 +489,25 @@ __device__ __forceinline__ float exp_pass(uint4 (&buf)[kLoads], float mx, float 
       s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     else
       s = (e[0] + e[1]) + (e[2] + e[3]);
-    if (CAND && s >= hit_sum) append_vec<DT>(buf[i], cut, c0 + (i * kThreads + tid) * VE, cap, sm);
+    mask |= s >= hit_sum ? (1u << i) : 0u;
     if ((i & 3) == 0) acc0 += s;
     else if ((i & 3) == 1) acc1 += s;
     else if ((i & 3) == 2) acc2 += s;
     else acc3 += s;
   }
+  *hits = mask;
   return (acc0 + acc1) + (acc2 + acc3);
 }
 
-// Streaming pass over one chunk held in registers; writes its ChunkRec and
-// candidate list.  The kernel instance for MODE handles rows whose
-// effective mode is MODE, or plain (top-p >= 1, top-k >= V).
-template <int DT, int MODE>
+// Streaming pass over one chunk; writes its ChunkRec and candidate list.
+// The instance for MODE handles sequences whose effective mode is MODE, or
+// plain (top-p >= 1, top-k >= V).
+template <int DT, bool VEC, int MODE>
 __device__ __forceinline__ void chunk_pass(const KParams& P, const SeqParams& sp, uint4 (&buf)[kLoads],
-                                           size_t slot, int c0, int c1, const void* row, Smem& sm) {
+                                           size_t slot, int c0, int c1, const char* row, SmemChunk& sm) {
   constexpr int VE = Fmt<DT>::VE;
   const int tid = threadIdx.x;
+  const int cap = P.cap;
   ChunkRec rec;
   rec.cut = kInf;
   rec.z = 0.0;
@@ -549,98 +549,119 @@ __device__ __forceinline__ void chunk_pass(const KParams& P, const SeqParams& sp
         has_cands = true;
         const int need = sp.topk;
         float cut = kInf;
-        if (need <= P.cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, P.cap, sm.red);
+        if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, cap, sm.red);
         if (cut != kInf) {
-          collect_ge<DT>(buf, cut, c0, P.cap, sm);
-          rec.cnt = min(sm.ch.cnt, P.cap);
-          rec.cut = sm.ch.cnt <= P.cap ? cut : kInf;
+          const int n = collect_masked<DT, VEC>(vectors_ge<DT>(buf, cut), row, cut, c0, c1, cap, sm);
+          rec.cnt = min(n, cap);
+          rec.cut = n <= cap ? cut : kInf;
         }
       }
     }
   }
   if constexpr (MODE != SV_GREEDY) {
-   if (!handled) {
-    // plain and nucleus: one exp per logit
-    fence_regs(buf);
-    float mx = -kInf;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-      for (int k = 0; k < VE; ++k) mx = fmaxf(mx, elem<DT>(buf[i], k));
-    mx = block_max(mx, sm.red);
-    rec.m = mx;
-    const bool cand = MODE == SV_TOPP && sp.mode == SV_TOPP;
-    has_cands = cand;
-    if (mx == kInf) {
-      rec.flags |= kCfNonFinite;
-    } else if (mx == -kInf) {
-      // nothing finite in this chunk: only NaN can still make the row invalid
+    if (!handled) {
+      // plain and nucleus: one exp per logit
       fence_regs(buf);
-      int bad = 0;
+      float mx = -kInf;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i)
 #pragma unroll
-        for (int k = 0; k < VE; ++k) bad |= !(elem<DT>(buf[i], k) < kInf);
-      if (block_max_i(bad, sm.red)) rec.flags |= kCfNonFinite;
-      rec.cut = -kInf;  // the (empty) candidate list is complete
-    } else {
-      const float c2 = (float)sp.c2;
-      const float o = mx * c2;
-      // the fma form is exact up to a common offset |delta| <= 2^-14 when |o| < 2^10
-      const bool fma_ok = fabsf(o) < 1024.0f;
-      const float cut = mx - kCandLog2 / c2;
-      const int cap = P.cap;
-      if (cand) {
-        __syncthreads();
-        if (tid == 0) sm.ch.cnt = 0;
-        __syncthreads();
-      }
-      float zt;
-      if (cand) {
-        if constexpr (MODE == SV_TOPP) {
-          zt = fma_ok ? exp_pass<DT, true, true>(buf, mx, c2, o, cut, c0, cap, sm)
-                      : exp_pass<DT, false, true>(buf, mx, c2, o, cut, c0, cap, sm);
-        }
+        for (int k = 0; k < VE; ++k) mx = fmaxf(mx, elem<DT>(buf[i], k));
+      mx = block_max(mx, sm.red);
+      rec.m = mx;
+      const bool cand = MODE == SV_TOPP && sp.mode == SV_TOPP;
+      has_cands = cand;
+      if (mx == kInf) {
+        rec.flags |= kCfNonFinite;
+      } else if (mx == -kInf) {
+        // nothing finite in this chunk: only NaN can still make the row invalid
+        fence_regs(buf);
+        int bad = 0;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+          for (int k = 0; k < VE; ++k) bad |= !(elem<DT>(buf[i], k) < kInf);
+        if (block_max_i(bad, sm.red)) rec.flags |= kCfNonFinite;
+        rec.cut = -kInf;  // the (empty) candidate list is complete
       } else {
-        zt = fma_ok ? exp_pass<DT, true, false>(buf, mx, c2, o, cut, c0, cap, sm)
-                    : exp_pass<DT, false, false>(buf, mx, c2, o, cut, c0, cap, sm);
-      }
-      const double z = block_sum((double)zt, sm.red);
-      // terms were 2^(x*c2 - o); refer them to 2^((x - m) c2) exactly
-      const double delta = fma_ok ? (double)mx * (double)c2 - (double)o : 0.0;
-      rec.z = z * exp2(-delta);
-      if (cand) {
-        __syncthreads();
-        int n = sm.ch.cnt;
-        float used = cut;
-        if (n > cap) {
-          // too many near the top: narrow the window until the list fits
-          used = shrink_cut_mem<DT>(row, c0, c1, mx, kCandLog2 / c2, cap, sm.red);
-          if (used != kInf) {
-            collect_ge_mem<DT>(row, c0, c1, used, cap, sm);
-            n = sm.ch.cnt;
+        const float c2 = (float)sp.c2;
+        const float o = mx * c2;
+        const bool fma_ok = fabsf(o) < 1024.0f;
+        uint32_t hits = 0;
+        const float zt = fma_ok ? exp_pass<DT, true>(buf, mx, c2, o, &hits)
+                                : exp_pass<DT, false>(buf, mx, c2, o, &hits);
+        const double z = block_sum((double)zt, sm.red);
+        // terms were 2^(x*c2 - o); refer them to 2^((x - m) c2) exactly
+        const double delta = fma_ok ? (double)mx * (double)c2 - (double)o : 0.0;
+        rec.z = z * exp2(-delta);
+        if (cand) {
+          float used = mx - kCandLog2 / c2;
+          int n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
+          // too many near the top: narrow the window (the candidates of a
+          // narrower window lie in the same vectors)
+          if (n > cap) {
+            used = mx - 8.0f / c2;
+            n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
           }
+          if (n > cap) {
+            used = mx - 6.0f / c2;
+            n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
+          }
+          rec.cnt = min(n, cap);
+          rec.cut = n <= cap ? used : kInf;
         }
-        rec.cnt = min(n, cap);
-        rec.cut = (n <= cap) ? used : kInf;
       }
     }
-   }
   }
 
   // publish the chunk's candidates and record
   if (has_cands) {
-    float2* dst = P.cands + slot * (size_t)P.cap;
-    for (int j = tid; j < rec.cnt; j += kThreads) dst[j] = sm.ch.cand[j];
+    float2* dst = P.cands + slot * (size_t)cap;
+    for (int j = tid; j < rec.cnt; j += kThreads) dst[j] = sm.cand[j];
   }
   if (tid == 0) P.chunks[slot] = rec;
 }
 
-// -------------------------------------------------------- selection -----
-// MSB-first radix selection over order-preserving keys.  Finds the largest
-// logit value T whose inclusive descending cumulative count (top-k) or mass
-// (nucleus, fixed point) reaches `target`.  Histograms hold counts and
-// fixed-point masses, so the result does not depend on atomic order.
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
+  __shared__ SmemChunk sm;
+  const int S = P.S, R = P.R;
+  const uint32_t blk = blockIdx.x;
+  const int b = P.b_base + (int)(blk / (uint32_t)(R * S));
+  const int rem = (int)(blk % (uint32_t)(R * S));
+  const int r = rem / S, c = rem % S;
+  // each sequence is streamed by the instance of its sampling mode
+  if (raw_mode(P, b) != MODE) return;
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid) return;
+  bool tgt;
+  int t;
+  if (!decode_row(P, sp, r, &tgt, &t)) return;  // padding row: never read
+  const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
+  const size_t slot = ((size_t)b * R + r) * S + c;
+  const int c0 = c * P.L;
+  const int c1 = min(P.V, c0 + P.L);
+  uint4 buf[kLoads];
+  load_chunk<DT, VEC>(buf, row, c0, c1);
+  chunk_pass<DT, VEC, MODE>(P, sp, buf, slot, c0, c1, row, sm);
+}
+
+// ======================================================= merge kernel ====
+
+struct SmemMerge {
+  ChunkRec crec[kMaxChunks];
+  float cx[kMergeCache];
+  int cidx[kMergeCache];
+  unsigned long long cm[kMergeCache];
+  uint32_t hc[256];
+  unsigned long long hm[256];
+  alignas(16) int kidx[kListMax + 4];
+  unsigned long long km[kListMax];
+  int n, nk;
+  uint32_t sel_digit, sel_hit;
+  Red red;
+};
+
 struct SelOut {
   float T;
   bool reached;
@@ -648,65 +669,32 @@ struct SelOut {
   unsigned long long m_keep, m_above;
 };
 
-// Source of elements: either the candidate lists of a row's chunks or the
-// full row in global memory.
-template <int DT>
-struct Source {
-  const float2* cands;
-  int cap;
-  int V;
-  const ChunkRec* crec;  // in LDS
-  size_t slot0;
-  int S;
-  bool full;
-  const void* row;
-  float M;
-  double c2;
-  bool exact_exp;
-
-  template <class F>
-  __device__ __forceinline__ void for_each(F&& f) const {
-    if (full) {
-      for (int e = threadIdx.x; e < V; e += kThreads) f(load_logit<DT>(row, e));
-    } else {
-      for (int s = 0; s < S; ++s) {
-        const float2* c = cands + (slot0 + s) * (size_t)cap;
-        const int n = crec[s].cnt;
-        for (int j = threadIdx.x; j < n; j += kThreads) f(c[j].x);
-      }
-    }
-  }
-  __device__ __forceinline__ unsigned long long mass(float x) const {
-    double e;
-    if (exact_exp)
-      e = exp2(((double)x - (double)M) * c2);
-    else
-      e = (double)__builtin_amdgcn_exp2f((x - M) * (float)c2);
-    return (unsigned long long)(e * kFix + 0.5);
-  }
-};
-
-template <int DT>
-__device__ __forceinline__ SelOut radix_select(const Source<DT>& src, bool by_mass, unsigned long long target, Smem& sm) {
+// MSB-first radix selection over order-preserving keys.  Finds the largest
+// logit value T whose inclusive descending cumulative count (top-k) or mass
+// (nucleus, fixed point) reaches `target`.  Histograms hold counts and
+// fixed-point masses, so the result does not depend on atomic order.
+// `each(f)` calls f(x, mass) for this thread's share of the elements.
+template <int DT, class Each>
+__device__ __forceinline__ SelOut radix_select(Each&& each, bool by_mass, unsigned long long target,
+                                               SmemMerge& sm) {
   const int tid = threadIdx.x;
   const int levels = DT == SV_BF16 ? 2 : 4;
   uint32_t pkey = 0, pmask = 0;
   unsigned long long above_c = 0, above_m = 0;
   bool reached = true;
-  uint32_t last_c = 0;
-  unsigned long long last_m = 0;
+  unsigned long long last_c = 0, last_m = 0;
   for (int lv = 0; lv < levels; ++lv) {
     const int shift = 24 - 8 * lv;
     __syncthreads();
-    sm.mg.hc[tid] = 0;
-    sm.mg.hm[tid] = 0;
+    sm.hc[tid] = 0;
+    sm.hm[tid] = 0;
     __syncthreads();
-    src.for_each([&](float x) {
+    each([&](float x, unsigned long long m) {
       const uint32_t key = fkey(x);
       if ((key & pmask) == pkey) {
         const uint32_t dg = (key >> shift) & 255u;
-        atomicAdd(&sm.mg.hc[dg], 1u);
-        atomicAdd(&sm.mg.hm[dg], src.mass(x));
+        atomicAdd(&sm.hc[dg], 1u);
+        atomicAdd(&sm.hm[dg], m);
       }
     });
     __syncthreads();
@@ -716,13 +704,12 @@ __device__ __forceinline__ SelOut radix_select(const Source<DT>& src, bool by_ma
       unsigned long long c[4], m[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = sm.mg.hc[4 * lane + j];
-        m[j] = sm.mg.hm[4 * lane + j];
+        c[j] = sm.hc[4 * lane + j];
+        m[j] = sm.hm[4 * lane + j];
       }
-      unsigned long long lc = c[0] + c[1] + c[2] + c[3];
-      unsigned long long lm = m[0] + m[1] + m[2] + m[3];
-      // inclusive suffix over lanes >= lane
-      unsigned long long sc = lc, sms = lm;
+      const unsigned long long lc = c[0] + c[1] + c[2] + c[3];
+      const unsigned long long lm = m[0] + m[1] + m[2] + m[3];
+      unsigned long long sc = lc, sms = lm;  // inclusive suffix over lanes >= lane
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const unsigned long long yc = __shfl_down(sc, o);
@@ -732,21 +719,14 @@ __device__ __forceinline__ SelOut radix_select(const Source<DT>& src, bool by_ma
           sms += ym;
         }
       }
-      // suffix sums per digit
-      unsigned long long suf_c[4], suf_m[4];
       unsigned long long rc = sc - lc, rm = sms - lm;  // digits of higher lanes
+      int best = -1;
 #pragma unroll
       for (int j = 3; j >= 0; --j) {
         rc += c[j];
         rm += m[j];
-        suf_c[j] = rc;
-        suf_m[j] = rm;
-      }
-      int best = -1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = by_mass ? (above_m + suf_m[j] >= target) : (above_c + suf_c[j] >= target);
-        if (ok) best = 4 * lane + j;
+        const bool ok = by_mass ? (above_m + rm >= target) : (above_c + rc >= target);
+        if (ok && best < 0) best = 4 * lane + j;
       }
       const int hit = wave_max_i(best);
       int lowest = 256;
@@ -755,40 +735,20 @@ __device__ __forceinline__ SelOut radix_select(const Source<DT>& src, bool by_ma
         if (c[j] > 0) lowest = 4 * lane + j;
       const int low = wave_min_i(lowest);
       if (lane == 0) {
-        sm.mg.sel_hit = hit >= 0 ? 1u : 0u;
-        sm.mg.sel_digit = hit >= 0 ? (uint32_t)hit : (low < 256 ? (uint32_t)low : 0u);
+        sm.sel_hit = hit >= 0 ? 1u : 0u;
+        sm.sel_digit = hit >= 0 ? (uint32_t)hit : (low < 256 ? (uint32_t)low : 0u);
       }
     }
     __syncthreads();
-    const uint32_t dg = sm.mg.sel_digit;
-    if (!sm.mg.sel_hit) reached = false;
-    // add everything strictly above the chosen digit
-    unsigned long long add_c = 0, add_m = 0;
-    if (tid < 64) {
-      for (int j = 0; j < 4; ++j) {
-        const int d = 4 * tid + j;
-        if (d > (int)dg) {
-          add_c += sm.mg.hc[d];
-          add_m += sm.mg.hm[d];
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        add_c += __shfl_xor(add_c, o);
-        add_m += __shfl_xor(add_m, o);
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      sm.red.d[0] = __longlong_as_double((long long)add_c);
-      sm.red.d[1] = __longlong_as_double((long long)add_m);
-      sm.red.d[2] = __longlong_as_double((long long)sm.mg.hc[dg]);
-      sm.red.d[3] = __longlong_as_double((long long)sm.mg.hm[dg]);
-    }
-    __syncthreads();
-    above_c += (unsigned long long)__double_as_longlong(sm.red.d[0]);
-    above_m += (unsigned long long)__double_as_longlong(sm.red.d[1]);
-    last_c = (uint32_t)__double_as_longlong(sm.red.d[2]);
-    last_m = (unsigned long long)__double_as_longlong(sm.red.d[3]);
+    const uint32_t dg = sm.sel_digit;
+    if (!sm.sel_hit) reached = false;
+    // everything strictly above the chosen digit joins the "above" totals
+    const unsigned long long add_c = block_sum_u64((int)tid > (int)dg ? sm.hc[tid] : 0ull, sm.red);
+    const unsigned long long add_m = block_sum_u64((int)tid > (int)dg ? sm.hm[tid] : 0ull, sm.red);
+    above_c += add_c;
+    above_m += add_m;
+    last_c = sm.hc[dg];
+    last_m = sm.hm[dg];
     pkey |= dg << shift;
     pmask |= 255u << shift;
   }
@@ -796,31 +756,46 @@ __device__ __forceinline__ SelOut radix_select(const Source<DT>& src, bool by_ma
   SelOut r;
   r.T = key_value(pkey);
   r.reached = reached;
-  r.n_keep = (uint32_t)above_c + last_c;
+  r.n_keep = (uint32_t)(above_c + last_c);
   r.m_keep = above_m + last_m;
   r.m_above = above_m;
   return r;
 }
 
-// --------------------------------------------------------- row merge ----
-template <int DT>
-__device__ __forceinline__ void row_merge(const KParams& P, const SeqParams& sp, int b, size_t rowid, const void* row,
-                          int tok, Smem& sm) {
+__device__ __forceinline__ unsigned long long fixed_mass(double e) {
+  return (unsigned long long)(e * kFix + 0.5);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
+  __shared__ SmemMerge sm;
   const int tid = threadIdx.x;
-  const int S = P.S;
-  const size_t slot0 = rowid * (size_t)S;
-  for (int s = tid; s < S; s += kThreads) sm.mg.crec[s] = P.chunks[slot0 + s];
-  __syncthreads();
+  const int S = P.S, R = P.R;
+  const uint32_t blk = blockIdx.x;
+  const int b = P.b_base + (int)(blk / (uint32_t)R);
+  const int r = (int)(blk % (uint32_t)R);
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid) return;
+  bool tgt;
+  int t;
+  if (!decode_row(P, sp, r, &tgt, &t)) return;
+  const void* row = row_ptr<DT>(P, b, tgt, t);
+  const size_t rowid = (size_t)b * R + r;
+  const size_t slot0 = rowid * S;
   const int mode = sp.mode;
+  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
+
+  for (int s = tid; s < S; s += kThreads) sm.crec[s] = P.chunks[slot0 + s];
+  __syncthreads();
 
   float m_s = -kInf;
   int f_s = 0;
   for (int s = tid; s < S; s += kThreads) {
-    m_s = fmaxf(m_s, sm.mg.crec[s].m);
-    f_s |= (int)sm.mg.crec[s].flags;
+    m_s = fmaxf(m_s, sm.crec[s].m);
+    f_s |= (int)sm.crec[s].flags;
   }
   const float M = block_max(m_s, sm.red);
-  const int cflags = block_max_i(f_s, sm.red);  // only bit 0 is used
+  const int cflags = block_max_i(f_s, sm.red);
 
   RowRec rr;
   rr.M = M;
@@ -839,58 +814,95 @@ __device__ __forceinline__ void row_merge(const KParams& P, const SeqParams& sp,
   if (!(rr.flags & kErrBits) && (mode == SV_PLAIN || mode == SV_TOPP)) {
     double term = 0.0;
     for (int s = tid; s < S; s += kThreads) {
-      const ChunkRec& c = sm.mg.crec[s];
+      const ChunkRec& c = sm.crec[s];
       if (c.m > -kInf) term += c.z * exp2(((double)c.m - (double)M) * sp.c2);
     }
     Z = block_sum(term, sm.red);
     if (!(Z > 0.0) || !(Z < 1e300)) rr.flags |= SV_ST_NONFINITE;
   }
 
+  bool list_kept = false;
   if (!(rr.flags & kErrBits)) {
     if (mode == SV_PLAIN) {
       rr.Zs = Z;
     } else if (mode == SV_GREEDY) {
       int best = 0x7fffffff;
       for (int s = tid; s < S; s += kThreads)
-        if (sm.mg.crec[s].m == M) best = min(best, sm.mg.crec[s].arg);
+        if (sm.crec[s].m == M) best = min(best, sm.crec[s].arg);
       rr.g = block_min_i(best, sm.red);
       rr.T = M;
       rr.n_keep = 1;
     } else {
+      // candidates >= C, where C = max over chunks of the chunk cuts: every
+      // logit >= C of the row is among them
       float cmax = -kInf;
-      for (int s = tid; s < S; s += kThreads) cmax = fmaxf(cmax, sm.mg.crec[s].cut);
+      for (int s = tid; s < S; s += kThreads) cmax = fmaxf(cmax, sm.crec[s].cut);
       const float C = block_max(cmax, sm.red);
       const bool by_mass = mode == SV_TOPP;
       unsigned long long target;
       if (by_mass) {
-        const double t = (double)sp.topp * Z * kFix;
-        target = t < 1.0 ? 1ull : (unsigned long long)t;
+        const double tt = (double)sp.topp * Z * kFix;
+        target = tt < 1.0 ? 1ull : (unsigned long long)tt;
       } else {
         target = (unsigned long long)sp.topk;
       }
-      Source<DT> src{P.cands, P.cap, P.V, sm.mg.crec, slot0, S, false, row, M, sp.c2, true};
-      SelOut so;
       bool fast = C < kInf;
       if (fast) {
-        so = radix_select<DT>(src, by_mass, target, sm);
+        __syncthreads();
+        if (tid == 0) sm.n = 0;
+        __syncthreads();
+        for (int s = 0; s < S; ++s) {
+          const float2* cl = P.cands + (slot0 + s) * (size_t)P.cap;
+          const int cn = sm.crec[s].cnt;
+          for (int j = tid; j < cn; j += kThreads) {
+            const float2 v = cl[j];
+            if (v.x >= C) {
+              const int pos = atomicAdd(&sm.n, 1);
+              if (pos < kMergeCache) {
+                sm.cx[pos] = v.x;
+                sm.cidx[pos] = __float_as_int(v.y);
+                sm.cm[pos] = fixed_mass(exp2(((double)v.x - (double)M) * sp.c2));
+              }
+            }
+          }
+        }
+        __syncthreads();
+        fast = sm.n <= kMergeCache;
+      }
+      SelOut so;
+      if (fast) {
+        const int n = sm.n;
+        so = radix_select<DT>(
+            [&](auto&& f) {
+              for (int j = tid; j < n; j += kThreads) f(sm.cx[j], sm.cm[j]);
+            },
+            by_mass, target, sm);
         fast = so.reached && so.T >= C;
       }
       if (!fast) {
-        src.full = true;
-        src.exact_exp = false;
-        so = radix_select<DT>(src, by_mass, target, sm);
+        // full-row selection: re-read the row (rare: an incomplete or
+        // insufficient candidate window)
+        const float c2f = (float)sp.c2;
+        so = radix_select<DT>(
+            [&](auto&& f) {
+              for (int e = tid; e < P.V; e += kThreads) {
+                const float x = load_logit<DT>(row, e);
+                f(x, fixed_mass((double)__builtin_amdgcn_exp2f((x - M) * c2f)));
+              }
+            },
+            by_mass, target, sm);
         rr.flags |= SV_ST_FULLSELECT;
       }
       rr.T = so.T;
       rr.n_keep = (int)so.n_keep;
       rr.Zs = (double)so.m_keep / kFix;
-      if (fast && so.n_keep <= (uint32_t)kListMax) rr.flags |= kRfListOk;
       if (by_mass) {
         const double lo = (double)so.m_above / kFix / Z, hi = (double)so.m_keep / kFix / Z;
         if (fabs(lo - (double)sp.topp) < kWindow || fabs(hi - (double)sp.topp) < kWindow)
           rr.flags |= SV_ST_MARGIN;
       }
       if (!(rr.Zs > 0.0)) rr.flags |= SV_ST_EMPTY;
+      list_kept = fast && tgt && so.n_keep <= (uint32_t)kListMax;
     }
   }
 
@@ -906,108 +918,139 @@ __device__ __forceinline__ void row_merge(const KParams& P, const SeqParams& sp,
       }
     }
   }
+
+  if (list_kept && !(rr.flags & kErrBits)) {
+    // the target row's kept set, in vocabulary order, with probabilities:
+    // compact it, then rank each entry by its vocabulary index
+    rr.flags |= kRfListOk;
+    const int n = sm.n;
+    __syncthreads();
+    if (tid == 0) sm.nk = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += kThreads) {
+      if (sm.cx[j] >= rr.T) {
+        const int pos = atomicAdd(&sm.nk, 1);
+        sm.kidx[pos] = sm.cidx[j];
+        sm.km[pos] = sm.cm[j];
+      }
+    }
+    __syncthreads();
+    const int nk = sm.nk;  // == n_keep <= kListMax
+    for (int j = nk; j < ((nk + 3) & ~3); ++j)
+      if (tid == 0) sm.kidx[j] = 0x7fffffff;  // pad to whole int4s
+    __syncthreads();
+    KeptEntry* out = P.kept + rowid * kListMax;
+    const int4* k4 = reinterpret_cast<const int4*>(sm.kidx);
+    for (int j = tid; j < nk; j += kThreads) {
+      const int my = sm.kidx[j];
+      int rank = 0;
+      for (int i = 0; i < (nk + 3) / 4; ++i) {
+        const int4 v = k4[i];
+        rank += (v.x < my) + (v.y < my) + (v.z < my) + (v.w < my);
+      }
+      KeptEntry ke;
+      ke.idx = my;
+      ke.pad = 0;
+      ke.q = (double)sm.km[j] / kFix / rr.Zs;
+      out[rank] = ke;
+    }
+  }
   if (tid == 0) P.rows[rowid] = rr;
 }
 
-// -------------------------------------------------------- final draw ----
+// ======================================================= final kernel ====
+
+struct SmemFinal {
+  int idx[kListMax];
+  double w[kListMax];
+  double c[kListMax];
+  Red red;
+  uint32_t misc[4];
+};
+
 struct Draw {
   int y;
   double S;
   uint32_t flags;
 };
 
-// Inverse CDF over the target's kept set (taken from its candidate lists),
-// in vocabulary order.  w = (q - p)+ when `resample`, else w = q.
+// Inverse CDF over the target's kept set (vocabulary order): w = (q - p)+
+// when resampling, else w = q.
 template <int DT>
-__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec rq, const bool resample, const RowRec rp,
-                               size_t rowq,
-                               const void* drow, double u, Smem& sm) {
+__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample,
+                                               const RowRec& rp, size_t rowq, const void* drow, double u,
+                                               SmemFinal& sm) {
   const int tid = threadIdx.x;
-  const int S = P.S;
-  __syncthreads();
-  if (tid == 0) sm.fin.n = 0;
-  __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    const ChunkRec cr = P.chunks[rowq * S + s];
-    const float2* c = P.cands + (rowq * S + s) * (size_t)P.cap;
-    for (int j = tid; j < cr.cnt; j += kThreads) {
-      const float2 v = c[j];
-      if (v.x >= rq.T) {
-        const int pos = atomicAdd(&sm.fin.n, 1);
-        if (pos < kListMax) {
-          sm.fin.x[pos] = v.x;
-          sm.fin.idx[pos] = __float_as_int(v.y);
-        }
-      }
+  const int N = rq.n_keep;  // <= kListMax
+  const KeptEntry* kl = P.kept + rowq * kListMax;
+  double qv[2];
+  int iv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * tid + j;
+    qv[j] = 0.0;
+    iv[j] = 0;
+    if (i < N) {
+      const KeptEntry ke = kl[i];
+      qv[j] = ke.q;
+      iv[j] = ke.idx;
     }
   }
-  __syncthreads();
-  const int N = min(sm.fin.n, kListMax);
-  // order by vocabulary index (indices are distinct)
-  for (int i = tid; i < N; i += kThreads) {
-    const int my = sm.fin.idx[i];
-    int r = 0;
-    for (int j = 0; j < N; ++j) r += sm.fin.idx[j] < my ? 1 : 0;
-    sm.fin.sx[r] = sm.fin.x[i];
-    sm.fin.sidx[r] = my;
-  }
-  __syncthreads();
   Draw d;
   d.flags = 0;
+  double w[2];
+  bool use_p = resample;
+  double total = 0.0, ex = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
-    const bool resid = resample && pass == 0;
-    for (int i = tid; i < N; i += kThreads) {
-      const double q = exp2(((double)sm.fin.sx[i] - (double)rq.M) * rq.c2) / rq.Zs;
-      double w = q;
-      if (resid) {
-        const float xp = load_logit<DT>(drow, sm.fin.sidx[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      w[j] = qv[j];
+      if (use_p && 2 * tid + j < N) {
+        const float xp = load_logit<DT>(drow, iv[j]);
         const double p = xp >= rp.T ? exp2(((double)xp - (double)rp.M) * rp.c2) / rp.Zs : 0.0;
-        w = q > p ? q - p : 0.0;
+        w[j] = qv[j] > p ? qv[j] - p : 0.0;
       }
-      sm.fin.w[i] = w;
     }
-    __syncthreads();
-    // prefix in vocabulary order: thread t owns elements 2t, 2t+1
-    const int i0 = 2 * tid, i1 = 2 * tid + 1;
-    const double w0 = i0 < N ? sm.fin.w[i0] : 0.0, w1 = i1 < N ? sm.fin.w[i1] : 0.0;
-    double total;
-    const double ex = block_exclusive_scan(w0 + w1, &total, sm.red);
-    if (i0 < N) sm.fin.c[i0] = ex + w0;
-    if (i1 < N) sm.fin.c[i1] = (ex + w0) + w1;
-    __syncthreads();
-    d.S = total;
-    if (total > 0.0 || pass == 1) break;
+    ex = block_exclusive_scan(w[0] + w[1], &total, sm.red);
+    if (total > 0.0 || !use_p) break;
     d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
-    __syncthreads();
+    use_p = false;
   }
-  const double target = u * d.S;
-  int first = 0x7fffffff, lastnz = -1;
-  for (int i = tid; i < N; i += kThreads) {
-    if (sm.fin.c[i] > target && sm.fin.w[i] > 0.0) first = min(first, i);
-    if (sm.fin.w[i] > 0.0) lastnz = max(lastnz, i);
+  d.S = total;
+  const double target = u * total;
+  // first element whose running sum exceeds the target; last non-zero one
+  int first = 0x7fffffff, lastnz = -1, firstnz = 0x7fffffff;
+  double c = ex;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * tid + j;
+    const double cn = c + w[j];
+    if (i < N) {
+      sm.w[i] = w[j];
+      sm.c[i] = cn;
+      sm.idx[i] = iv[j];
+      if (w[j] > 0.0) {
+        if (cn > target) first = min(first, i);
+        lastnz = max(lastnz, i);
+        firstnz = min(firstnz, i);
+      }
+    }
+    c = cn;
   }
   first = block_min_i(first, sm.red);
   lastnz = block_max_i(lastnz, sm.red);
+  firstnz = block_min_i(firstnz, sm.red);
   int iy = first <= lastnz ? first : lastnz;
   if (iy < 0) iy = 0;
-  d.y = N > 0 ? sm.fin.sidx[iy] : 0;
-  if (tid == 0 && N > 0) {
+  d.y = N > 0 ? sm.idx[iy] : 0;
+  if (N > 0 && lastnz >= 0) {
     // margins of interior CDF boundaries
-    const double hi = sm.fin.c[iy] / d.S, lo = (sm.fin.c[iy] - sm.fin.w[iy]) / d.S;
-    bool nz_before = false, nz_after = false;
-    for (int i = 0; i < iy; ++i) nz_before |= sm.fin.w[i] > 0.0;
-    for (int i = iy + 1; i < N; ++i) nz_after |= sm.fin.w[i] > 0.0;
-    if ((nz_before && u - lo < kWindow) || (nz_after && hi - u < kWindow)) sm.flag = 1;
-    else sm.flag = 0;
+    const double hi = sm.c[iy] / d.S, lo = (sm.c[iy] - sm.w[iy]) / d.S;
+    if ((firstnz < iy && u - lo < kWindow) || (lastnz > iy && hi - u < kWindow)) d.flags |= SV_ST_MARGIN;
   }
-  __syncthreads();
-  if (sm.flag) d.flags |= SV_ST_MARGIN;
-  __syncthreads();
   return d;
 }
 
-// Inverse CDF over full logit rows re-read from memory, in tiles of
-// 256 x 8 tokens (thread t owns tokens 8t..8t+7 of a tile).
 template <int DT>
 __device__ __forceinline__ double weight(const RowRec& rq, bool use_p, const RowRec& rp, float xq, float xp) {
   double q = 0.0;
@@ -1018,15 +1061,19 @@ __device__ __forceinline__ double weight(const RowRec& rq, bool use_p, const Row
   return q > p ? q - p : 0.0;
 }
 
+// Inverse CDF over full logit rows re-read from memory, in tiles of
+// 256 x 8 tokens (thread t owns tokens 8t..8t+7 of a tile).
 template <int DT>
-__device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec rq, const bool resample, const RowRec rp,
-                               const void* qrow,
-                               const void* prow, double u, Smem& sm) {
+__device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample,
+                                               const RowRec& rp, const void* qrow, const void* prow,
+                                               double u, SmemFinal& sm) {
   const int tid = threadIdx.x;
   const int V = P.V;
   constexpr int TILE = kThreads * 8;
   Draw d;
   d.flags = SV_ST_REREAD;
+  d.y = 0;
+  d.S = 0.0;
   bool use_p = resample;
   for (int pass = 0; pass < 2; ++pass) {
     // total mass and the first / last token of non-zero weight
@@ -1062,6 +1109,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec rq
     for (int base = 0; base < V && y < 0; base += TILE) {
       double wk[8];
       double s = 0.0;
+#pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int e = base + 8 * tid + k;
         wk[k] = e < V ? weight<DT>(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f) : 0.0;
@@ -1074,6 +1122,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec rq
         int cand = 0x7fffffff;
         double c = run + ex;
         double cl = 0.0, ch = 0.0;
+#pragma unroll
         for (int k = 0; k < 8; ++k) {
           const double cn = c + wk[k];
           if (cn > target && wk[k] > 0.0 && cand == 0x7fffffff) {
@@ -1100,7 +1149,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec rq
     }
     if (y < 0) {  // rounding left no token above the target
       y = nz_hi < 0 ? 0 : nz_hi;
-      lo = S - 0.0;
+      lo = S;
       hi = S;
     }
     d.y = y;
@@ -1111,14 +1160,6 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec rq
   return d;
 }
 
-template <int DT>
-__device__ __forceinline__ const void* row_ptr(const KParams& P, int b, bool tgt, int t) {
-  constexpr int ES = Fmt<DT>::ES;
-  const size_t r = tgt ? ((size_t)b * (P.K_max + 1) + t) : ((size_t)b * P.K_max + t);
-  return static_cast<const char*>(tgt ? P.target : P.draft) + r * (size_t)P.V * ES;
-}
-
-template <int DT>
 __device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st) {
   const int tid = threadIdx.x;
   for (int i = tid; i <= P.K_max; i += kThreads) P.out_tokens[(size_t)b * (P.K_max + 1) + i] = -1;
@@ -1131,28 +1172,33 @@ __device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st
 }
 
 template <int DT>
-__device__ __forceinline__ void finalize(const KParams& P, const SeqParams& sp, int b, Smem& sm) {
+__global__ __launch_bounds__(kThreads) void final_kernel(const KParams P) {
+  __shared__ SmemFinal sm;
   const int tid = threadIdx.x;
+  const int b = P.b_base + (int)blockIdx.x;
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid) {
+    write_error(P, b, SV_ST_PARAM);
+    return;
+  }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
   const uint64_t g = P.row_offset + (uint64_t)b;
   const size_t rbase = (size_t)b * R;
-  // OR of the row records' flags
-  uint32_t st;
-  {
-    uint32_t v = 0;
-    for (int t = tid; t <= Kb; t += kThreads) v |= P.rows[rbase + t].flags;
-    for (int t = tid; t < Kb; t += kThreads) v |= P.rows[rbase + KM + 1 + t].flags;
+
+  // OR of the used rows' flags
+  uint32_t v = 0;
+  for (int t = tid; t <= Kb; t += kThreads) v |= P.rows[rbase + t].flags;
+  for (int t = tid; t < Kb; t += kThreads) v |= P.rows[rbase + KM + 1 + t].flags;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o);
-    __syncthreads();
-    if ((tid & 63) == 0) sm.red.i[tid >> 6] = (int)v;
-    __syncthreads();
-    st = (uint32_t)(sm.red.i[0] | sm.red.i[1] | sm.red.i[2] | sm.red.i[3]);
-    __syncthreads();
-  }
+  for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o);
+  __syncthreads();
+  if ((tid & 63) == 0) sm.red.i[tid >> 6] = (int)v;
+  __syncthreads();
+  uint32_t st = (uint32_t)(sm.red.i[0] | sm.red.i[1] | sm.red.i[2] | sm.red.i[3]);
+  __syncthreads();
   st &= ~kRfListOk;
   if (st & kErrBits) {
-    write_error<DT>(P, b, st & kErrBits);
+    write_error(P, b, st & kErrBits);
     return;
   }
   // accept walk (one thread; K_b <= 64)
@@ -1180,12 +1226,12 @@ __device__ __forceinline__ void finalize(const KParams& P, const SeqParams& sp, 
         P.diag[((size_t)b * KM + t) * 2 + 0] = __builtin_nanf("");
         P.diag[((size_t)b * KM + t) * 2 + 1] = __builtin_nanf("");
       }
-    sm.red.i[0] = n;
-    sm.red.i[1] = (int)s2;
+    sm.misc[0] = (uint32_t)n;
+    sm.misc[1] = s2;
   }
   __syncthreads();
-  const int n = sm.red.i[0];
-  st |= (uint32_t)sm.red.i[1];
+  const int n = (int)sm.misc[0];
+  st |= sm.misc[1];
   __syncthreads();
 
   const bool resample = n < Kb;
@@ -1199,18 +1245,18 @@ __device__ __forceinline__ void finalize(const KParams& P, const SeqParams& sp, 
     d.S = 1.0;
     d.flags = (resample && rp.g == rq.g) ? SV_ST_ZERO_RESIDUAL : 0u;
   } else if (rq.flags & kRfListOk) {
-    d = draw_from_list<DT>(P, rq, resample, rp, rbase + n,
-                           resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, sm);
+    d = draw_from_list<DT>(P, rq, resample, rp, rbase + n, resample ? row_ptr<DT>(P, b, false, n) : nullptr,
+                           u, sm);
   } else {
     d = draw_from_rows<DT>(P, rq, resample, rp, row_ptr<DT>(P, b, true, n),
                            resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, sm);
   }
   st |= d.flags;
   for (int i = tid; i <= KM; i += kThreads) {
-    int v = -1;
-    if (i < n) v = P.tokens[(size_t)b * KM + i];
-    else if (i == n) v = d.y;
-    P.out_tokens[(size_t)b * (KM + 1) + i] = v;
+    int val = -1;
+    if (i < n) val = P.tokens[(size_t)b * KM + i];
+    else if (i == n) val = d.y;
+    P.out_tokens[(size_t)b * (KM + 1) + i] = val;
   }
   if (tid == 0) {
     P.accepted[b] = n;
@@ -1218,103 +1264,39 @@ __device__ __forceinline__ void finalize(const KParams& P, const SeqParams& sp, 
   }
 }
 
-// ------------------------------------------------------------ kernel ----
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void verify_kernel(const KParams P) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int S = P.S, R = P.R;
-  const size_t blk = blockIdx.x;
-  const int b = P.b_base + (int)(blk / ((size_t)R * S));
-  const int rem = (int)(blk % ((size_t)R * S));
-  const int r = rem / S, c = rem % S;
-
-  // Each sequence is handled by the instance of its sampling mode (an invalid
-  // mode value by the plain instance, which reports the error).
-  const int raw_mode = P.mode ? (int)P.mode[b] : P.dmode;
-  if ((raw_mode >= SV_PLAIN && raw_mode <= SV_GREEDY ? raw_mode : SV_PLAIN) != MODE) return;
-  const SeqParams sp = load_params(P, b);
-  if (!sp.valid) {
-    if (r == 0 && c == 0) write_error<DT>(P, b, SV_ST_PARAM);
-    return;
+template <int DT, bool VEC>
+void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  switch (mode) {
+    case SV_PLAIN: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, p); break;
+    case SV_TOPK: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, p); break;
+    case SV_TOPP: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, p); break;
   }
-  const bool tgt = r <= P.K_max;
-  const int t = tgt ? r : r - P.K_max - 1;
-  if (tgt ? (t > sp.Kb) : (t >= sp.Kb)) return;  // padding row: never read
+}
 
-  const void* row = row_ptr<DT>(P, b, tgt, t);
-  const size_t rowid = (size_t)b * R + r;
-  const size_t slot = rowid * S + c;
-  const int c0 = c * P.L;
-  const int c1 = min(P.V, c0 + P.L);
-
-  {
-    uint4 buf[kLoads];
-    load_chunk<DT, VEC>(buf, static_cast<const char*>(row), c0, c1);
-    chunk_pass<DT, MODE>(P, sp, buf, slot, c0, c1, row, sm);
+template <int DT, bool VEC>
+void launch_all(const KParams& p, int nseq, hipStream_t stream) {
+  const dim3 block(kThreads);
+  // one streaming instance per sampling mode that can occur
+  for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode) {
+    if (!p.mode && mode != p.dmode) continue;
+    launch_chunk<DT, VEC>(p, mode, dim3((unsigned)((size_t)nseq * p.R * p.S)), stream);
   }
-
-  // last chunk of the row merges it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&P.rowctr[rowid], 1u);
-    sm.flag = old == (uint32_t)(S - 1);
-    if (sm.flag) {
-      atomicExch(&P.rowctr[rowid], 0u);
-      __threadfence();
-    }
-  }
-  __syncthreads();
-  if (!sm.flag) return;
-
-  const int tok = (t < sp.Kb) ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
-  row_merge<DT>(P, sp, b, rowid, row, tok, sm);
-
-  // last row of the sequence finalizes it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&P.seqctr[b], 1u);
-    sm.flag = old == (uint32_t)(2 * sp.Kb);
-    if (sm.flag) {
-      atomicExch(&P.seqctr[b], 0u);
-      __threadfence();
-    }
-  }
-  __syncthreads();
-  if (!sm.flag) return;
-  finalize<DT>(P, sp, b, sm);
+  hipLaunchKernelGGL((merge_kernel<DT, VEC>), dim3((unsigned)((size_t)nseq * p.R)), block, 0, stream, p);
+  hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)nseq), block, 0, stream, p);
 }
 
 }  // namespace
 
-template <int DT, bool VEC>
-static void launch_mode(const KParams& p, int mode, dim3 grid, hipStream_t stream) {
-  const dim3 block(kThreads);
-  switch (mode) {
-    case SV_PLAIN: hipLaunchKernelGGL((verify_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, p); break;
-    case SV_TOPK: hipLaunchKernelGGL((verify_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, p); break;
-    case SV_TOPP: hipLaunchKernelGGL((verify_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((verify_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, p); break;
-  }
-}
-
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream) {
-  const size_t blocks = (size_t)nseq * p.R * p.S;
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks);
-  // One instance per sampling mode present: with a per-row mode array every
-  // instance runs (each skips the sequences of other modes).
-  for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode) {
-    if (!p.mode && mode != p.dmode) continue;
-    if (dtype == SV_BF16) {
-      if (vec) launch_mode<SV_BF16, true>(p, mode, grid, stream);
-      else launch_mode<SV_BF16, false>(p, mode, grid, stream);
-    } else {
-      if (vec) launch_mode<SV_F32, true>(p, mode, grid, stream);
-      else launch_mode<SV_F32, false>(p, mode, grid, stream);
-    }
+  if (nseq <= 0) return hipSuccess;
+  if (dtype == SV_BF16) {
+    if (vec) launch_all<SV_BF16, true>(p, nseq, stream);
+    else launch_all<SV_BF16, false>(p, nseq, stream);
+  } else {
+    if (vec) launch_all<SV_F32, true>(p, nseq, stream);
+    else launch_all<SV_F32, false>(p, nseq, stream);
   }
   return hipGetLastError();
 }
