@@ -25,7 +25,8 @@ struct sv_handle_s {
   void* ws;
   size_t ws_bytes;
   sv::ChunkRec* chunks;
-  float2* cands;
+  uint4* cvec;
+  int32_t* cidx;
   sv::RowRec* rows;
   sv::KeptEntry* kept;
   hipEvent_t last;
@@ -45,7 +46,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, cap, R_max;
-  size_t off_chunks, off_cands, off_rows, off_kept, total;
+  size_t off_chunks, off_cvec, off_cidx, off_rows, off_kept, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -65,17 +66,20 @@ Geometry geometry(const sv_config* cfg) {
   const int V = cfg->vocab;
   const int ve = cfg->dtype == SV_BF16 ? 8 : 4;
   const int chunk_cap = sv::chunk_capacity(cfg->dtype);
+  // whole chunks of chunk_cap logits, the row's remainder in the last one
   g.S = (V + chunk_cap - 1) / chunk_cap;
-  const int per = (V + g.S - 1) / g.S;
-  g.L = (per + ve - 1) / ve * ve;
-  g.cap = std::min(sv::kCandCap, g.L);
+  g.L = chunk_cap;
+  (void)ve;
+  g.cap = std::max(32, std::min(sv::kCandVecs, 4096 / g.S));
   g.R_max = 2 * cfg->max_k + 1;
   const size_t rows = (size_t)cfg->max_batch * g.R_max;
   size_t off = 0;
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
-  g.off_cands = off;
-  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(float2), 256);
+  g.off_cvec = off;
+  off = align_up(off + rows * g.S * (size_t)g.cap * 16, 256);
+  g.off_cidx = off;
+  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int32_t), 256);
   g.off_rows = off;
   off = align_up(off + rows * sizeof(sv::RowRec), 256);
   g.off_kept = off;
@@ -154,7 +158,8 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   }
   char* base = static_cast<char*>(h->ws);
   h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
-  h->cands = reinterpret_cast<float2*>(base + g.off_cands);
+  h->cvec = reinterpret_cast<uint4*>(base + g.off_cvec);
+  h->cidx = reinterpret_cast<int32_t*>(base + g.off_cidx);
   h->rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
   h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
@@ -191,6 +196,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.L = h->L;
   p.cap = h->cap;
   p.b_base = 0;
+  p.b_end = 0;
   p.target = a->target_logits;
   p.draft = a->draft_logits;
   p.tokens = a->draft_tokens;
@@ -210,7 +216,8 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.status = a->row_status;
   p.diag = a->diag;
   p.chunks = h->chunks;
-  p.cands = h->cands;
+  p.cvec = h->cvec;
+  p.cidx = h->cidx;
   p.rows = h->rows;
   p.kept = h->kept;
 
@@ -225,6 +232,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   for (int b0 = 0; b0 < a->B && e == hipSuccess; b0 += seq_per_launch) {
     p.b_base = b0;
     const int nseq = std::min(seq_per_launch, a->B - b0);
+    p.b_end = b0 + nseq;
     e = sv::launch_verify(p, cfg.dtype, vec, nseq, s);
   }
   if (e == hipSuccess) e = hipEventRecord(h->last, s);

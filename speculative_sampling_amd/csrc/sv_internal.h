@@ -11,32 +11,34 @@ namespace sv {
 
 // Work-group shape of every kernel: 4 wave64s.
 constexpr int kThreads = 256;
-// Each thread of the streaming kernel keeps kLoads 16-byte vectors of its
-// chunk in registers (64 VGPRs): 128 bf16 or 64 fp32 logits.
+// The streaming kernel gives each wave (64 lanes) one chunk of a row; each
+// lane keeps kLoads 16-byte vectors of it in registers (64 VGPRs): 128 bf16
+// or 64 fp32 logits, so a chunk holds at most 8192 bf16 / 4096 fp32 logits.
 constexpr int kLoads = 16;
-// Candidate list capacity per chunk (tokens near the chunk max kept for the
-// top-k / nucleus threshold search).
-constexpr int kCandCap = 1024;
+// Candidate list capacity per chunk, in 16-byte logit vectors: the vectors
+// that may hold a token near the maximum, kept for the top-k / nucleus
+// threshold search (fewer per chunk when a row has many chunks).
+constexpr int kCandVecs = 256;
 // Candidates of one row the merge kernel caches in LDS.
 constexpr int kMergeCache = 2048;
 // Largest kept set the final draw takes from the merged kept list without
 // re-reading the logit rows.
 constexpr int kListMax = 512;
-// Largest number of chunks per row (V <= 2^22 with 16384 fp32 per chunk).
-constexpr int kMaxChunks = 256;
+// Largest number of chunks per row (V <= 2^22 with 4096 fp32 per chunk).
+constexpr int kMaxChunks = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxVocab = 1 << 22;
 
-inline int chunk_capacity(int dtype) { return kThreads * kLoads * (dtype == SV_BF16 ? 8 : 4); }
+inline int chunk_capacity(int dtype) { return 64 * kLoads * (dtype == SV_BF16 ? 8 : 4); }
 
 // Per-(row, chunk) partial results written by the streaming kernel.
 struct ChunkRec {
   float m;         // chunk maximum of the raw logits (-inf if none is finite)
-  float cut;       // every token of the chunk with logit >= cut (and > -inf) is
-                   // in the chunk's candidate list; +inf when the list is
-                   // incomplete
+  float cut;       // every token of the chunk with logit >= cut (and > -inf) lies
+                   // in a vector of the chunk's candidate list; +inf when the
+                   // list is incomplete
   double z;        // sum over the chunk of 2^((x - m) * c2)   (plain, nucleus)
-  int32_t cnt;     // candidates stored
+  int32_t cnt;     // candidate vectors stored
   int32_t arg;     // lowest index whose logit equals m      (greedy)
   uint32_t flags;  // kCfNonFinite
   int32_t pad;
@@ -67,8 +69,9 @@ struct KeptEntry {
 };
 
 struct KParams {
-  int32_t B, K_max, V, R, S, L, cap;
-  int32_t b_base;  // first sequence of this launch
+  int32_t B, K_max, V, R, S, L;
+  int32_t cap;  // candidate vectors per chunk
+  int32_t b_base, b_end;  // sequences [b_base, b_end) of this launch
   const void* target;
   const void* draft;
   const int32_t* tokens;
@@ -88,12 +91,13 @@ struct KParams {
   uint32_t* status;
   float* diag;
   ChunkRec* chunks;
-  float2* cands;
+  uint4* cvec;     // [row][chunk][cap] candidate vectors (raw logits)
+  int32_t* cidx;   // [row][chunk][cap] index of each vector's first logit
   RowRec* rows;
   KeptEntry* kept;  // [rows][kListMax]
 };
 
-// Enqueues the three kernels of one call for sequences
+// Enqueues the kernels of one call for sequences
 // [p.b_base, p.b_base + nseq): the streaming chunk pass (one instance per
 // sampling mode present), the row merge and the per-sequence finalize.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream);

@@ -39,6 +39,7 @@ namespace sv {
 namespace {
 
 constexpr float kInf = __builtin_inff();
+constexpr int kWave = 64;
 constexpr float kMaxFinite = 3.402823466e38f;
 constexpr double kLog2e = 1.4426950408889634074;
 // Fixed-point scale of masses (units of the row's largest term): integer
@@ -172,7 +173,7 @@ __device__ __forceinline__ int wave_max_i(int v) {
 }
 
 struct Red {
-  float f[4];
+  float f[8];
   double d[4];
   int i[4];
   unsigned long long u[4];
@@ -293,44 +294,46 @@ __device__ __forceinline__ bool decode_row(const KParams& P, const SeqParams& sp
 }
 
 // ======================================================= chunk kernel ====
+//
+// Each wave owns one chunk of a logit row (64 lanes x kLoads vectors) and
+// reduces it on its own, with wave ballots and shuffles only: no barrier and
+// no LDS, so the waves of a work-group never wait for one another.
 
-struct SmemChunk {
-  float2 cand[kCandCap];
-  int cnt;
-  Red red;
-};
-
-// Loads this thread's part of chunk [c0, c1) into registers: vector i holds
-// logits c0 + (i * 256 + tid) * VE + [0, VE).  Every load is issued
+// Loads this lane's part of chunk [c0, c1) into registers: vector i holds
+// logits c0 + (i * 64 + lane) * VE + [0, VE).  Every load is issued
 // unconditionally from a clamped in-bounds address and the out-of-range
 // vectors are replaced by -inf afterwards, so all kLoads requests are in
 // flight together.
 template <int DT, bool VEC>
-__device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoads], const char* row, int c0, int c1) {
+__device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoads], const char* row, int c0, int c1, int lane) {
   constexpr int VE = Fmt<DT>::VE, ES = Fmt<DT>::ES;
-  const int tid = threadIdx.x;
   const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
   if constexpr (VEC) {
     // c0 and c1 are multiples of VE and c1 - c0 >= VE
-    const int last = c1 - VE;
+    const uint4* base = reinterpret_cast<const uint4*>(row + (size_t)c0 * ES);
+    if (c1 - c0 == kWave * kLoads * VE) {
+      // a whole chunk: one base address and constant offsets
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int e0 = c0 + (i * kThreads + tid) * VE;
-      buf[i] = *reinterpret_cast<const uint4*>(row + (size_t)min(e0, last) * ES);
-    }
+      for (int i = 0; i < kLoads; ++i) buf[i] = base[i * kWave + lane];
+    } else {
+      // the row's last chunk: clamped addresses, -inf past c1
+      const int nvec = (c1 - c0) / VE;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const bool ok = c0 + (i * kThreads + tid) * VE < c1;
-      buf[i].x = ok ? buf[i].x : ninf;
-      buf[i].y = ok ? buf[i].y : ninf;
-      buf[i].z = ok ? buf[i].z : ninf;
-      buf[i].w = ok ? buf[i].w : ninf;
+      for (int i = 0; i < kLoads; ++i) buf[i] = base[min(i * kWave + lane, nvec - 1)];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const bool ok = i * kWave + lane < nvec;
+        buf[i].x = ok ? buf[i].x : ninf;
+        buf[i].y = ok ? buf[i].y : ninf;
+        buf[i].z = ok ? buf[i].z : ninf;
+        buf[i].w = ok ? buf[i].w : ninf;
+      }
     }
   } else {
     const int last = c1 - 1;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int e0 = c0 + (i * kThreads + tid) * VE;
+      const int e0 = c0 + (i * kWave + lane) * VE;
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -360,43 +363,9 @@ __device__ __forceinline__ void fence_regs(uint4 (&buf)[kLoads]) {
     asm volatile("" : "+v"(buf[i].x), "+v"(buf[i].y), "+v"(buf[i].z), "+v"(buf[i].w));
 }
 
-// Appends (logit, index) of the elements >= c of one vector to the list.
+// Number of the chunk's elements >= cut (wave ballots).
 template <int DT>
-__device__ __forceinline__ void append_vec(const uint4& v, float c, int e0, int cap, SmemChunk& sm) {
-  constexpr int VE = Fmt<DT>::VE;
-#pragma unroll
-  for (int k = 0; k < VE; ++k) {
-    const float x = elem<DT>(v, k);
-    if (x >= c) {
-      const int pos = atomicAdd(&sm.cnt, 1);
-      if (pos < cap) sm.cand[pos] = make_float2(x, __int_as_float(e0 + k));
-    }
-  }
-}
-
-// Collects, from the vectors flagged in `mask` (re-read from memory, where
-// the chunk was just streamed from), every element >= cut.
-template <int DT, bool VEC>
-__device__ __forceinline__ int collect_masked(uint32_t mask, const char* row, float cut, int c0, int c1,
-                                              int cap, SmemChunk& sm) {
-  constexpr int VE = Fmt<DT>::VE;
-  const float c = fmaxf(cut, -kMaxFinite);
-  __syncthreads();
-  if (threadIdx.x == 0) sm.cnt = 0;
-  __syncthreads();
-  while (mask) {
-    const int i = __ffs(mask) - 1;
-    mask &= mask - 1;
-    const int e0 = c0 + (i * kThreads + (int)threadIdx.x) * VE;
-    append_vec<DT>(load_vec<DT, VEC>(row, e0, c1), c, e0, cap, sm);
-  }
-  __syncthreads();
-  return sm.cnt;
-}
-
-// Register-resident count of elements >= cut (wave ballots, no VGPRs).
-template <int DT>
-__device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut, Red& red) {
+__device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut) {
   constexpr int VE = Fmt<DT>::VE;
   const float c = fmaxf(cut, -kMaxFinite);  // -inf logits are never candidates
   fence_regs(buf);
@@ -405,13 +374,10 @@ __device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut, Red& re
   for (int i = 0; i < kLoads; ++i)
 #pragma unroll
     for (int k = 0; k < VE; ++k) n += __popcll(__ballot(elem<DT>(buf[i], k) >= c));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red.i[threadIdx.x >> 6] = n;
-  __syncthreads();
-  return (red.i[0] + red.i[1]) + (red.i[2] + red.i[3]);
+  return n;
 }
 
-// Per-thread bitmask of the vectors holding an element >= cut.
+// Per-lane bitmask of the vectors holding an element >= cut.
 template <int DT>
 __device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut) {
   constexpr int VE = Fmt<DT>::VE;
@@ -428,25 +394,42 @@ __device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut) 
   return mask;
 }
 
+// Exact maximum of the chunk, and whether it holds a NaN or +inf.
+template <int DT>
+__device__ __forceinline__ float chunk_max(const uint4 (&buf)[kLoads], bool* bad) {
+  constexpr int VE = Fmt<DT>::VE;
+  float mx = -kInf;
+  int nf = 0;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+    for (int k = 0; k < VE; ++k) {
+      const float x = elem<DT>(buf[i], k);
+      mx = fmaxf(mx, x);
+      nf |= !(x < kInf);
+    }
+  *bad = __ballot(nf) != 0;
+  return wave_max(mx);
+}
+
 // Top-k window: a cut whose candidate count lies in [need, cap].  Grows the
 // window below the chunk max from d (logit units) until `need` tokens are in,
 // then bisects while the list would overflow.  +inf when none exists.
 template <int DT>
-__device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, float d, int need, int cap,
-                                            Red& red) {
+__device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, float d, int need, int cap) {
   float lo = 0.0f;  // window known to hold < need tokens (or 0)
   float cut = mx - d;
-  int n = count_ge<DT>(buf, cut, red);
+  int n = count_ge<DT>(buf, cut);
   for (int it = 0; n < need && it < 64; ++it) {
     lo = d;
     d *= 4.0f;
     cut = mx - d;
     if (!(cut > -kMaxFinite)) {  // the window covers every finite logit
       cut = -kInf;
-      n = count_ge<DT>(buf, cut, red);
+      n = count_ge<DT>(buf, cut);
       break;
     }
-    n = count_ge<DT>(buf, cut, red);
+    n = count_ge<DT>(buf, cut);
   }
   if (n <= cap) return cut;
   float hi = d;
@@ -454,7 +437,7 @@ __device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, floa
     const float mid = 0.5f * (lo + hi);
     if (!(mid > lo && mid < hi)) break;
     const float cm = mx - mid;
-    const int nm = count_ge<DT>(buf, cm, red);
+    const int nm = count_ge<DT>(buf, cm);
     if (nm < need) lo = mid;
     else if (nm > cap) hi = mid;
     else return cm;
@@ -462,194 +445,248 @@ __device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, floa
   return kInf;
 }
 
-// One exp per logit: returns this thread's sum of 2^((x - mx) c2) and sets in
-// *hits the vectors whose terms sum to >= 0.999 * 2^-10 (every element
-// >= cut lies in such a vector, up to rounding of the terms).  FMA selects
-// the 1-op exponent x*c2 - o (o = mx*c2 rounded), exact up to a common
-// offset |delta| <= 2^-14 when |o| < 2^10.
-template <int DT, bool FMA>
-__device__ __forceinline__ float exp_pass(uint4 (&buf)[kLoads], float mx, float c2, float o,
-                                          uint32_t* hits) {
+// One exp per logit: returns the lane's sum of the terms 2^(x c2 - o) and
+// the largest term of each of its vectors (emax[i]).  With o = r c2 rounded
+// to fp32 each term is 2^((x - r) c2 + delta), delta = r c2 - o being common
+// to all of them; the exponent x c2 - o is rounded once (fma).  The logits
+// are only used through the terms, so each vector is unpacked right where
+// it is consumed.
+template <int DT>
+__device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, float o, float (&emax)[kLoads]) {
   constexpr int VE = Fmt<DT>::VE;
-  const float hit_sum = 0.999f * 0.0009765625f;
-  fence_regs(buf);
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  uint32_t mask = 0;
+  float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     float e[VE];
 #pragma unroll
-    for (int k = 0; k < VE; ++k) {
-      const float x = elem<DT>(buf[i], k);
-      const float a = FMA ? fmaf(x, c2, -o) : (x - mx) * c2;
-      e[k] = __builtin_amdgcn_exp2f(a);
+    for (int k = 0; k < VE; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(elem<DT>(buf[i], k), c2, -o));
+    float si, mi;
+    if constexpr (VE == 8) {
+      si = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      mi = fmaxf(fmaxf(fmaxf(e[0], e[1]), e[2]), fmaxf(fmaxf(e[3], e[4]), e[5]));
+      mi = fmaxf(fmaxf(mi, e[6]), e[7]);
+    } else {
+      si = (e[0] + e[1]) + (e[2] + e[3]);
+      mi = fmaxf(fmaxf(fmaxf(e[0], e[1]), e[2]), e[3]);
     }
-    float s;
-    if constexpr (VE == 8)
-      s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    else
-      s = (e[0] + e[1]) + (e[2] + e[3]);
-    mask |= s >= hit_sum ? (1u << i) : 0u;
-    if ((i & 3) == 0) acc0 += s;
-    else if ((i & 3) == 1) acc1 += s;
-    else if ((i & 3) == 2) acc2 += s;
-    else acc3 += s;
+    emax[i] = mi;
+    acc += si;
   }
-  *hits = mask;
-  return (acc0 + acc1) + (acc2 + acc3);
+  return acc;
 }
 
-// Streaming pass over one chunk; writes its ChunkRec and candidate list.
-// The instance for MODE handles sequences whose effective mode is MODE, or
-// plain (top-p >= 1, top-k >= V).
-template <int DT, bool VEC, int MODE>
-__device__ __forceinline__ void chunk_pass(const KParams& P, const SeqParams& sp, uint4 (&buf)[kLoads],
-                                           size_t slot, int c0, int c1, const char* row, SmemChunk& sm) {
+// Lists the vectors flagged in `mask` (whole, from the registers) with the
+// index of their first logit, in (vector, lane) order; returns how many
+// there are (entries beyond cap are dropped).
+__device__ __forceinline__ int list_vectors(uint4* dv, int32_t* di, uint32_t mask, const uint4 (&buf)[kLoads],
+                                            int c0, int ve, int cap, int lane) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const bool h = (mask >> i) & 1u;
+    const uint64_t bal = __ballot(h);
+    if (h) {
+      const int pos = n + __popcll(bal & below);
+      if (pos < cap) {
+        dv[pos] = buf[i];
+        di[pos] = c0 + (i * kWave + lane) * ve;
+      }
+    }
+    n += __popcll(bal);
+  }
+  return n;
+}
+
+// Softmax statistics of a plain / nucleus chunk from one exp per logit.
+struct PlainStats {
+  float o;        // exponent offset: terms are 2^(x c2 - o)
+  double zw;      // sum of the chunk's terms
+  double ma;      // the chunk maximum, from its largest term
+  int st;         // 0 = statistics valid, 1 = no finite logit, 2 = NaN or +inf
+  float emax[kLoads];  // largest term of each of the lane's vectors
+};
+
+// The exponent reference r is the largest logit of the lanes' first
+// vectors.  A chunk whose terms overflow (a logit far above r) or hold a NaN
+// is re-read once and redone from its exact maximum.
+template <int DT, bool VEC>
+__device__ __forceinline__ void plain_stats(uint4 (&buf)[kLoads], float c2, const char* row, int c0, int c1,
+                                            int lane, PlainStats& ps) {
   constexpr int VE = Fmt<DT>::VE;
-  const int tid = threadIdx.x;
-  const int cap = P.cap;
+  float r = -kInf;
+#pragma unroll
+  for (int k = 0; k < VE; ++k) r = fmaxf(r, elem<DT>(buf[0], k));
+  r = wave_max(r);
+  float o = r * c2;
+  float zt = 0.0f;
+  const bool ok = r > -kInf && r < kInf;  // false on NaN
+  if (ok) zt = exp_pass<DT>(buf, c2, o, ps.emax);
+  ps.st = 0;
+  if (!ok || __ballot(!(zt < kInf))) {
+    // rare: re-read the chunk
+    load_chunk<DT, VEC>(buf, row, c0, c1, lane);
+    bool bad;
+    const float mx = chunk_max<DT>(buf, &bad);
+    ps.st = bad ? 2 : (mx == -kInf ? 1 : 0);
+    o = mx * c2;
+    zt = 0.0f;
+    if (ps.st == 0) zt = exp_pass<DT>(buf, c2, o, ps.emax);  // every term <= 2^delta now
+    else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) ps.emax[i] = 0.0f;
+    }
+  }
+  float em = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) em = fmaxf(em, ps.emax[i]);
+  em = wave_max(em);
+  ps.o = o;
+  ps.zw = wave_sum((double)zt);
+  // the largest term 2^a belongs to the chunk maximum x = (a + o) / c2
+  ps.ma = ps.st == 0 ? ((double)log2f(em) + (double)o) / (double)c2 : -1e300;
+}
+
+// Finishes a plain / nucleus chunk.  A nucleus chunk lists every logit
+// x >= g - 10/c2, where g >= the chunk maximum is the largest maximum among
+// the chunks of the same row in this work-group (lists that overflow are
+// retried with 8 and 6); its vectors are flagged from their largest terms
+// with a 2^-8 margin in the exponent, a superset of those holding one.
+template <int DT>
+__device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats& ps, float c2, bool cand,
+                                             double g, const uint4 (&buf)[kLoads], size_t slot, int c0, int lane,
+                                             ChunkRec& rec) {
+  if (ps.st == 2) {
+    rec.flags |= kCfNonFinite;
+    return;
+  }
+  if (ps.st == 1) {
+    rec.m = -kInf;
+    rec.cut = -kInf;  // nothing finite: the (empty) candidate list is complete
+    return;
+  }
+  const float m = (float)ps.ma;
+  rec.m = m;
+  // refer the sum to m: 2^(x c2 - o) = 2^((x - m) c2) 2^(m c2 - o)
+  rec.z = ps.zw * exp2((double)ps.o - (double)m * (double)c2);
+  if (cand) {
+    uint4* dv = P.cvec + slot * (size_t)P.cap;
+    int32_t* di = P.cidx + slot * (size_t)P.cap;
+    int n = 0;
+    float cut = kInf;
+    for (int attempt = 0; attempt < 3; ++attempt) {
+      cut = (float)(g - (attempt == 0 ? kCandLog2 : attempt == 1 ? 8.0f : 6.0f) / (double)c2);
+      // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
+      const float thr = exp2f((float)((double)cut * (double)c2 - (double)ps.o) - 0.00390625f);
+      uint32_t mask = 0;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) mask |= ps.emax[i] >= thr ? (1u << i) : 0u;
+      n = list_vectors(dv, di, mask, buf, c0, Fmt<DT>::VE, P.cap, lane);
+      if (n <= P.cap) break;
+    }
+    rec.cnt = n <= P.cap ? n : 0;
+    rec.cut = n <= P.cap ? cut : kInf;  // +inf: incomplete, the merge falls back to the full row
+  }
+}
+
+// Streaming pass: one wave per chunk.  The instance for MODE handles the
+// sequences whose sampling mode is MODE; those whose effective mode is plain
+// (top-p >= 1, top-k >= V) take the plain path.
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
+  constexpr int VE = Fmt<DT>::VE;
+  constexpr int kWaves = kThreads / kWave;
+  __shared__ float s_max[kWaves];
+  __shared__ int s_key[kWaves];
+  const int lane = (int)__lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int S = P.S, R = P.R;
+  const uint32_t gw = blockIdx.x * (uint32_t)kWaves + (uint32_t)wv;
+  const int b = P.b_base + (int)(gw / (uint32_t)(R * S));
+  const int rem = (int)(gw % (uint32_t)(R * S));
+  const int r = rem / S, c = rem % S;
+  // no early return: the nucleus instance meets at one barrier
+  bool active = b < P.b_end && raw_mode(P, b) == MODE;
+  SeqParams sp{};
+  if (active) {
+    sp = load_params(P, b);
+    active = sp.valid;
+  }
+  bool tgt = false;
+  int t = 0;
+  if (active) active = decode_row(P, sp, r, &tgt, &t);  // padding rows are never read
+  const char* row = active ? static_cast<const char*>(row_ptr<DT>(P, b, tgt, t)) : nullptr;
+  const size_t slot = ((size_t)b * R + r) * S + c;
+  const int c0 = c * P.L;
+  const int c1 = min(P.V, c0 + P.L);
+  const float c2 = (float)sp.c2;
   ChunkRec rec;
+  rec.m = -kInf;
   rec.cut = kInf;
   rec.z = 0.0;
   rec.cnt = 0;
   rec.arg = -1;
   rec.flags = 0;
   rec.pad = 0;
-  bool has_cands = false;
-  bool handled = false;
+  uint4 buf[kLoads];
+  if (active) load_chunk<DT, VEC>(buf, row, c0, c1, lane);
 
-  if constexpr (MODE == SV_TOPK || MODE == SV_GREEDY) {
-    if (sp.mode == MODE) {
-      handled = true;
-      // maximum and the NaN / +inf check
-      fence_regs(buf);
-      float mx = -kInf;
-      int bad = 0;
+  const bool special = active && (MODE == SV_TOPK || MODE == SV_GREEDY) && sp.mode == MODE;
+  if (special) {
+    bool bad;
+    const float mx = chunk_max<DT>(buf, &bad);
+    rec.m = mx;
+    if (bad) {
+      rec.flags |= kCfNonFinite;
+    } else if (MODE == SV_GREEDY) {
+      int best = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i)
 #pragma unroll
-        for (int k = 0; k < VE; ++k) {
-          const float x = elem<DT>(buf[i], k);
-          mx = fmaxf(mx, x);
-          bad |= !(x < kInf);
-        }
-      if (block_max_i(bad, sm.red)) rec.flags |= kCfNonFinite;
-      mx = block_max(mx, sm.red);
-      rec.m = mx;
-      if constexpr (MODE == SV_GREEDY) {
-        fence_regs(buf);
-        int best = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-          for (int k = 0; k < VE; ++k)
-            if (elem<DT>(buf[i], k) == mx) best = min(best, c0 + (i * kThreads + tid) * VE + k);
-        rec.arg = block_min_i(best, sm.red);
-      } else {
-        has_cands = true;
-        const int need = sp.topk;
-        float cut = kInf;
-        if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, cap, sm.red);
-        if (cut != kInf) {
-          const int n = collect_masked<DT, VEC>(vectors_ge<DT>(buf, cut), row, cut, c0, c1, cap, sm);
-          rec.cnt = min(n, cap);
-          rec.cut = n <= cap ? cut : kInf;
-        }
+        for (int k = 0; k < VE; ++k)
+          if (elem<DT>(buf[i], k) == mx) best = min(best, c0 + (i * kWave + lane) * VE + k);
+      rec.arg = wave_min_i(best);
+    } else {
+      const int need = sp.topk, cap = P.cap;
+      float cut = kInf;
+      if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, cap);
+      if (cut != kInf) {
+        const int n = list_vectors(P.cvec + slot * (size_t)cap, P.cidx + slot * (size_t)cap,
+                                   vectors_ge<DT>(buf, cut), buf, c0, VE, cap, lane);
+        rec.cnt = min(n, cap);
+        rec.cut = n <= cap ? cut : kInf;
       }
     }
   }
   if constexpr (MODE != SV_GREEDY) {
-    if (!handled) {
-      // plain and nucleus: one exp per logit
-      fence_regs(buf);
-      float mx = -kInf;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-        for (int k = 0; k < VE; ++k) mx = fmaxf(mx, elem<DT>(buf[i], k));
-      mx = block_max(mx, sm.red);
-      rec.m = mx;
-      const bool cand = MODE == SV_TOPP && sp.mode == SV_TOPP;
-      has_cands = cand;
-      if (mx == kInf) {
-        rec.flags |= kCfNonFinite;
-      } else if (mx == -kInf) {
-        // nothing finite in this chunk: only NaN can still make the row invalid
-        fence_regs(buf);
-        int bad = 0;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-          for (int k = 0; k < VE; ++k) bad |= !(elem<DT>(buf[i], k) < kInf);
-        if (block_max_i(bad, sm.red)) rec.flags |= kCfNonFinite;
-        rec.cut = -kInf;  // the (empty) candidate list is complete
-      } else {
-        const float c2 = (float)sp.c2;
-        const float o = mx * c2;
-        const bool fma_ok = fabsf(o) < 1024.0f;
-        uint32_t hits = 0;
-        const float zt = fma_ok ? exp_pass<DT, true>(buf, mx, c2, o, &hits)
-                                : exp_pass<DT, false>(buf, mx, c2, o, &hits);
-        const double z = block_sum((double)zt, sm.red);
-        // terms were 2^(x*c2 - o); refer them to 2^((x - m) c2) exactly
-        const double delta = fma_ok ? (double)mx * (double)c2 - (double)o : 0.0;
-        rec.z = z * exp2(-delta);
-        if (cand) {
-          float used = mx - kCandLog2 / c2;
-          int n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
-          // too many near the top: narrow the window (the candidates of a
-          // narrower window lie in the same vectors)
-          if (n > cap) {
-            used = mx - 8.0f / c2;
-            n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
-          }
-          if (n > cap) {
-            used = mx - 6.0f / c2;
-            n = collect_masked<DT, VEC>(hits, row, used, c0, c1, cap, sm);
-          }
-          rec.cnt = min(n, cap);
-          rec.cut = n <= cap ? used : kInf;
-        }
+    const bool plain = active && !special;
+    const bool cand = plain && MODE == SV_TOPP && sp.mode == SV_TOPP;
+    PlainStats ps;
+    ps.st = 1;
+    ps.ma = -1e300;
+    if (plain) plain_stats<DT, VEC>(buf, c2, row, c0, c1, lane, ps);
+    double g = ps.ma;
+    if constexpr (MODE == SV_TOPP) {
+      // the largest chunk maximum among this work-group's chunks of the same row
+      if (lane == 0) {
+        s_key[wv] = cand ? (int)(gw / (uint32_t)S) : -1;
+        s_max[wv] = ps.st == 0 ? (float)ps.ma : -kInf;
       }
+      __syncthreads();
+      const int key = cand ? (int)(gw / (uint32_t)S) : -2;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (s_key[w] == key) g = fmax(g, (double)s_max[w]);
     }
+    if (plain) plain_finish<DT>(P, ps, c2, cand, g, buf, slot, c0, lane, rec);
   }
-
-  // publish the chunk's candidates and record
-  if (has_cands) {
-    float2* dst = P.cands + slot * (size_t)cap;
-    for (int j = tid; j < rec.cnt; j += kThreads) dst[j] = sm.cand[j];
-  }
-  if (tid == 0) P.chunks[slot] = rec;
-}
-
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
-  __shared__ SmemChunk sm;
-  const int S = P.S, R = P.R;
-  const uint32_t blk = blockIdx.x;
-  const int b = P.b_base + (int)(blk / (uint32_t)(R * S));
-  const int rem = (int)(blk % (uint32_t)(R * S));
-  const int r = rem / S, c = rem % S;
-  // each sequence is streamed by the instance of its sampling mode
-  if (raw_mode(P, b) != MODE) return;
-  const SeqParams sp = load_params(P, b);
-  if (!sp.valid) return;
-  bool tgt;
-  int t;
-  if (!decode_row(P, sp, r, &tgt, &t)) return;  // padding row: never read
-  const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
-  const size_t slot = ((size_t)b * R + r) * S + c;
-  const int c0 = c * P.L;
-  const int c1 = min(P.V, c0 + P.L);
-  uint4 buf[kLoads];
-  load_chunk<DT, VEC>(buf, row, c0, c1);
-  chunk_pass<DT, VEC, MODE>(P, sp, buf, slot, c0, c1, row, sm);
+  if (active && lane == 0) P.chunks[slot] = rec;
 }
 
 // ======================================================= merge kernel ====
 
 struct SmemMerge {
-  ChunkRec crec[kMaxChunks];
+  int pre[kMaxChunks];  // first flat candidate index of each chunk
   float cx[kMergeCache];
   int cidx[kMergeCache];
   unsigned long long cm[kMergeCache];
@@ -785,14 +822,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
   const int mode = sp.mode;
   const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
 
-  for (int s = tid; s < S; s += kThreads) sm.crec[s] = P.chunks[slot0 + s];
-  __syncthreads();
-
+  const ChunkRec* crec = P.chunks + slot0;
   float m_s = -kInf;
   int f_s = 0;
   for (int s = tid; s < S; s += kThreads) {
-    m_s = fmaxf(m_s, sm.crec[s].m);
-    f_s |= (int)sm.crec[s].flags;
+    m_s = fmaxf(m_s, crec[s].m);
+    f_s |= (int)crec[s].flags;
   }
   const float M = block_max(m_s, sm.red);
   const int cflags = block_max_i(f_s, sm.red);
@@ -814,7 +849,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
   if (!(rr.flags & kErrBits) && (mode == SV_PLAIN || mode == SV_TOPP)) {
     double term = 0.0;
     for (int s = tid; s < S; s += kThreads) {
-      const ChunkRec& c = sm.crec[s];
+      const ChunkRec c = crec[s];
       if (c.m > -kInf) term += c.z * exp2(((double)c.m - (double)M) * sp.c2);
     }
     Z = block_sum(term, sm.red);
@@ -828,7 +863,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
     } else if (mode == SV_GREEDY) {
       int best = 0x7fffffff;
       for (int s = tid; s < S; s += kThreads)
-        if (sm.crec[s].m == M) best = min(best, sm.crec[s].arg);
+        if (crec[s].m == M) best = min(best, crec[s].arg);
       rr.g = block_min_i(best, sm.red);
       rr.T = M;
       rr.n_keep = 1;
@@ -836,7 +871,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
       // candidates >= C, where C = max over chunks of the chunk cuts: every
       // logit >= C of the row is among them
       float cmax = -kInf;
-      for (int s = tid; s < S; s += kThreads) cmax = fmaxf(cmax, sm.crec[s].cut);
+      for (int s = tid; s < S; s += kThreads) cmax = fmaxf(cmax, crec[s].cut);
       const float C = block_max(cmax, sm.red);
       const bool by_mass = mode == SV_TOPP;
       unsigned long long target;
@@ -848,20 +883,44 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
       }
       bool fast = C < kInf;
       if (fast) {
-        __syncthreads();
+        // one flat index over the chunks' lists: thread t counts chunks 4t..4t+3
+        int cn[4], ls = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int s = 4 * tid + q;
+          cn[q] = s < S ? crec[s].cnt : 0;
+          ls += cn[q];
+        }
+        double tot;
+        int run = (int)block_exclusive_scan((double)ls, &tot, sm.red);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (4 * tid + q < S) sm.pre[4 * tid + q] = run;
+          run += cn[q];
+        }
         if (tid == 0) sm.n = 0;
         __syncthreads();
-        for (int s = 0; s < S; ++s) {
-          const float2* cl = P.cands + (slot0 + s) * (size_t)P.cap;
-          const int cn = sm.crec[s].cnt;
-          for (int j = tid; j < cn; j += kThreads) {
-            const float2 v = cl[j];
-            if (v.x >= C) {
+        const int total = (int)tot;
+        const float Cf = fmaxf(C, -kMaxFinite);
+        for (int f = tid; f < total; f += kThreads) {
+          int lo = 0, hi = S - 1;  // the last chunk whose list starts at or before f
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm.pre[mid] <= f) lo = mid;
+            else hi = mid - 1;
+          }
+          const size_t at = (slot0 + lo) * (size_t)P.cap + (f - sm.pre[lo]);
+          const uint4 v = P.cvec[at];
+          const int e0 = P.cidx[at];
+#pragma unroll
+          for (int k = 0; k < Fmt<DT>::VE; ++k) {
+            const float x = elem<DT>(v, k);
+            if (x >= Cf) {  // -inf padding past the row end never passes
               const int pos = atomicAdd(&sm.n, 1);
               if (pos < kMergeCache) {
-                sm.cx[pos] = v.x;
-                sm.cidx[pos] = __float_as_int(v.y);
-                sm.cm[pos] = fixed_mass(exp2(((double)v.x - (double)M) * sp.c2));
+                sm.cx[pos] = x;
+                sm.cidx[pos] = e0 + k;
+                sm.cm[pos] = fixed_mass(exp2(((double)x - (double)M) * sp.c2));
               }
             }
           }
@@ -1281,7 +1340,8 @@ void launch_all(const KParams& p, int nseq, hipStream_t stream) {
   // one streaming instance per sampling mode that can occur
   for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode) {
     if (!p.mode && mode != p.dmode) continue;
-    launch_chunk<DT, VEC>(p, mode, dim3((unsigned)((size_t)nseq * p.R * p.S)), stream);
+    const size_t waves = (size_t)nseq * p.R * p.S;
+    launch_chunk<DT, VEC>(p, mode, dim3((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave))), stream);
   }
   hipLaunchKernelGGL((merge_kernel<DT, VEC>), dim3((unsigned)((size_t)nseq * p.R)), block, 0, stream, p);
   hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)nseq), block, 0, stream, p);
