@@ -5,15 +5,16 @@ One step = one spec_verify_run call over a batch of B=64 sequences, K=4
 draft tokens, V=128256 bf16 logits, nucleus top-p 0.8 at temperature 0.8 on
 both models (target N(0, 4^2) plus +8 on 20 tokens per position, draft =
 target + N(0, 0.7^2)): the whole hot path (filter thresholds, softmax
-statistics, accept walk, resample / bonus draw) in the library's kernel.
+statistics, accept walk, resample / bonus draw) in the library's kernels.
 
 Inputs are synthetic and resident in HBM before timing; R input sets rotate
 so the 256 MB Infinity Cache cannot serve repeated reads.  Draft tokens are
 drawn by the library itself (the step with K = 0 on the draft rows).
 
 Prints one JSON line: value = rows/s; roofline = algorithmic logit bytes per
-launch / average kernel time (HIP events on the launch stream) against the
-8 TB/s HBM peak; cpu_baseline = the fp64 oracle on a bounded sample.
+call / average time of the streaming kernel (HIP events the library records
+around its stages on the launch stream) against the 8 TB/s HBM peak;
+cpu_baseline = the fp64 oracle on a bounded sample.
 """
 import argparse
 import hashlib
@@ -40,7 +41,7 @@ def kernel_source_hash():
 def stored_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"verify_kernel_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -64,6 +65,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets (>= 4 defeats the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run --steps plain device copies of BYTES bytes (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
@@ -71,6 +74,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy, args.steps)
+        return
 
     from speculative_sampling_amd import binding, workloads
 
@@ -108,26 +115,29 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: events around every launch (one kernel per call here)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: torch events on the launch stream bracket the K calls
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(i)
-        ends[i].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    avg_kernel_ms = sum(per) / len(per)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = t0.elapsed_time(t1) / args.steps
     rows_per_s = B / (ms_per_step * 1e-3)
     gbs_step = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = alg_bytes / (avg_kernel_ms * 1e-3) / 1e9
+
+    # the same K calls again with the library's stage events (HIP events it
+    # records on the launch stream before, between and after its two
+    # stages); kept apart because recording them lengthens each call
+    binding.spec_verify_profile_begin(v.handle, args.steps)
+    for i in range(args.steps):
+        step(i)
+    runs, (stage0_ms, stage1_ms) = binding.spec_verify_profile_end(v.handle)
+    stream_ms = stage0_ms / runs        # the streaming pass (chunk kernel)
+    seq_ms = stage1_ms / runs           # per-sequence merge, accept walk, draw
+    achieved = alg_bytes / (stream_ms * 1e-3) / 1e9
 
     # acceptance actually achieved by the synthetic draft (context)
     acc = torch.cat([o[0] for o in outs]).float()
@@ -156,16 +166,29 @@ def main():
                    "input_sets": len(sets), "parallelism": "single-gpu"},
         "logits_GBps": gbs_step,
         "pct_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS,
-        "kernel_ms": {"avg": avg_kernel_ms, "p10": per[len(per) // 10], "p50": per[len(per) // 2],
-                      "p90": per[(9 * len(per)) // 10]},
+        "stage_ms": {"stream": stream_ms, "sequence": seq_ms},
         "mean_accepted": alpha_tokens,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+        "roofline": {"bound": "hbm", "kernel": "chunk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
     v.close()
     print(json.dumps(line), flush=True)
+
+
+def calibrate_copy(torch, nbytes, steps):
+    """A plain device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE counters give the scale factors from counter units to bytes."""
+    dev = torch.device("cuda", 0)
+    src = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(4)]
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        torch.add(src[i % 4], 1, out=dst)  # one elementwise kernel: reads and writes nbytes
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                      "launches": steps}), flush=True)
 
 
 def cpu_baseline(w, budget_s):

@@ -169,6 +169,19 @@ int spec_verify_validate(const sv_config* cfg, const sv_args* args);
  * cfg is invalid.  Host-only. */
 uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 
+/* Stage timing, for measurement.  After spec_verify_profile_begin(h, n),
+ * the next n calls of spec_verify_run on h record HIP events on their own
+ * stream around the two stages of the first launch batch (B <= 2^16 is one
+ * batch): stage 0 is the streaming pass over the logits, stage 1 the
+ * per-sequence merge, accept walk and draw.  The events are created here,
+ * so run still allocates nothing.  spec_verify_profile_end waits for the
+ * last recorded event, writes the summed milliseconds of stage i to ms[i]
+ * for i < min(n_stages, 2), releases the events and returns the number of
+ * calls recorded (negative code on error).  Calling begin again discards an
+ * unfinished profile. */
+int spec_verify_profile_begin(sv_handle_t h, int max_calls);
+int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages);
+
 /* Text of the last error reported on the calling thread ("" if none). */
 const char* spec_verify_last_error(void);
 

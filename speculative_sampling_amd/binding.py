@@ -25,7 +25,8 @@ ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 
 # Every function the header declares.
 EXPORTS = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy",
-           "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_last_error")
+           "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_profile_begin",
+           "spec_verify_profile_end", "spec_verify_last_error")
 
 
 class SvConfig(ctypes.Structure):
@@ -69,6 +70,10 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_validate.restype = ctypes.c_int
     lib.spec_verify_workspace_bytes.argtypes = [ctypes.POINTER(SvConfig)]
     lib.spec_verify_workspace_bytes.restype = ctypes.c_uint64
+    lib.spec_verify_profile_begin.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.spec_verify_profile_begin.restype = ctypes.c_int
+    lib.spec_verify_profile_end.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    lib.spec_verify_profile_end.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -179,6 +184,21 @@ def spec_verify_run(handle: int, args: SvArgs, stream=None) -> None:
     rc = load_library().spec_verify_run(ctypes.c_void_p(handle), ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_run")
+
+
+def spec_verify_profile_begin(handle: int, max_calls: int) -> None:
+    rc = load_library().spec_verify_profile_begin(ctypes.c_void_p(handle), max_calls)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_profile_begin")
+
+
+def spec_verify_profile_end(handle: int):
+    """Returns (calls recorded, [stage-0 ms summed, stage-1 ms summed])."""
+    ms = (ctypes.c_double * 2)()
+    rc = load_library().spec_verify_profile_end(ctypes.c_void_p(handle), ms, 2)
+    if rc < 0:
+        raise SpecVerifyError(rc, "spec_verify_profile_end")
+    return rc, [ms[0], ms[1]]
 
 
 class Verifier:

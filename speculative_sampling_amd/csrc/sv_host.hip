@@ -1,7 +1,7 @@
 // Host side of libspec_verify: the C ABI declared in include/spec_verify.h.
 //
 // create  allocates the device workspace once (chunk records, candidate
-//         lists, row records, kept lists);
+//         vector lists, kept lists);
 // run     validates on the host, then enqueues the kernels of the step for
 //         batches of at most kMaxBlocksPerLaunch work-groups on the caller's
 //         stream;
@@ -15,6 +15,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "spec_verify.h"
 #include "sv_internal.h"
@@ -25,12 +26,13 @@ struct sv_handle_s {
   void* ws;
   size_t ws_bytes;
   sv::ChunkRec* chunks;
-  uint4* cvec;
   int32_t* cidx;
-  sv::RowRec* rows;
   sv::KeptEntry* kept;
   hipEvent_t last;
   bool has_run;
+  // stage timing (spec_verify_profile_begin / _end)
+  std::vector<hipEvent_t> prof;
+  int prof_max, prof_next;
 };
 
 namespace {
@@ -46,7 +48,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, cap, R_max;
-  size_t off_chunks, off_cvec, off_cidx, off_rows, off_kept, total;
+  size_t off_chunks, off_cidx, off_kept, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -76,12 +78,8 @@ Geometry geometry(const sv_config* cfg) {
   size_t off = 0;
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
-  g.off_cvec = off;
-  off = align_up(off + rows * g.S * (size_t)g.cap * 16, 256);
   g.off_cidx = off;
   off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int32_t), 256);
-  g.off_rows = off;
-  off = align_up(off + rows * sizeof(sv::RowRec), 256);
   g.off_kept = off;
   off = align_up(off + rows * sv::kListMax * sizeof(sv::KeptEntry), 256);
   g.total = off;
@@ -158,9 +156,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   }
   char* base = static_cast<char*>(h->ws);
   h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
-  h->cvec = reinterpret_cast<uint4*>(base + g.off_cvec);
   h->cidx = reinterpret_cast<int32_t*>(base + g.off_cidx);
-  h->rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
   h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -171,6 +167,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     return fail(SV_EHIP, std::string("workspace initialisation failed: ") + hipGetErrorString(e));
   }
   h->has_run = false;
+  h->prof_max = h->prof_next = 0;
   (void)hipSetDevice(prev);
   *out = h;
   return SV_OK;
@@ -216,9 +213,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.status = a->row_status;
   p.diag = a->diag;
   p.chunks = h->chunks;
-  p.cvec = h->cvec;
   p.cidx = h->cidx;
-  p.rows = h->rows;
   p.kept = h->kept;
 
   int prev = 0;
@@ -233,13 +228,67 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
     p.b_base = b0;
     const int nseq = std::min(seq_per_launch, a->B - b0);
     p.b_end = b0 + nseq;
-    e = sv::launch_verify(p, cfg.dtype, vec, nseq, s);
+    hipEvent_t* ev = nullptr;
+    if (b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[3 * (size_t)h->prof_next++];
+    e = sv::launch_verify(p, cfg.dtype, vec, nseq, s, ev);
   }
   if (e == hipSuccess) e = hipEventRecord(h->last, s);
   if (e == hipSuccess) h->has_run = true;
   if (prev != cfg.device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(SV_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return SV_OK;
+}
+
+namespace {
+void release_profile(sv_handle_t h) {
+  for (hipEvent_t e : h->prof) (void)hipEventDestroy(e);
+  h->prof.clear();
+  h->prof_max = h->prof_next = 0;
+}
+}  // namespace
+
+int spec_verify_profile_begin(sv_handle_t h, int max_calls) {
+  if (!h) return fail(SV_EINVAL, "handle is NULL");
+  if (max_calls < 1 || max_calls > 1000000) return fail(SV_EINVAL, "max_calls must be in [1, 10^6]");
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
+  if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return fail(SV_EHIP, "hipSetDevice failed");
+  if (h->has_run) (void)hipEventSynchronize(h->last);
+  release_profile(h);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 3 * max_calls && e == hipSuccess; ++i) {
+    hipEvent_t ev;
+    e = hipEventCreate(&ev);
+    if (e == hipSuccess) h->prof.push_back(ev);
+  }
+  if (prev != h->cfg.device) (void)hipSetDevice(prev);
+  if (e != hipSuccess) {
+    release_profile(h);
+    return fail(SV_EHIP, std::string("hipEventCreate failed: ") + hipGetErrorString(e));
+  }
+  h->prof_max = max_calls;
+  h->prof_next = 0;
+  return SV_OK;
+}
+
+int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages) {
+  if (!h) return fail(SV_EINVAL, "handle is NULL");
+  if (n_stages > 0 && !ms) return fail(SV_EINVAL, "ms is NULL");
+  const int runs = h->prof_next;
+  double sum[2] = {0.0, 0.0};
+  hipError_t e = hipSuccess;
+  if (runs > 0) e = hipEventSynchronize(h->prof[3 * (size_t)(runs - 1) + 2]);
+  for (int i = 0; i < runs && e == hipSuccess; ++i) {
+    float a = 0.0f, b = 0.0f;
+    e = hipEventElapsedTime(&a, h->prof[3 * (size_t)i], h->prof[3 * (size_t)i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, h->prof[3 * (size_t)i + 1], h->prof[3 * (size_t)i + 2]);
+    sum[0] += a;
+    sum[1] += b;
+  }
+  release_profile(h);
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("reading the stage events failed: ") + hipGetErrorString(e));
+  for (int i = 0; i < n_stages && i < 2; ++i) ms[i] = sum[i];
+  return runs;
 }
 
 int spec_verify_destroy(sv_handle_t h) {
@@ -250,6 +299,7 @@ int spec_verify_destroy(sv_handle_t h) {
   hipError_t e = hipSuccess;
   if (h->has_run) e = hipEventSynchronize(h->last);
   (void)hipEventDestroy(h->last);
+  release_profile(h);
   (void)hipFree(h->ws);
   (void)hipSetDevice(prev);
   delete h;

@@ -19,8 +19,6 @@ constexpr int kLoads = 16;
 // that may hold a token near the maximum, kept for the top-k / nucleus
 // threshold search (fewer per chunk when a row has many chunks).
 constexpr int kCandVecs = 256;
-// Candidates of one row the merge kernel caches in LDS.
-constexpr int kMergeCache = 2048;
 // Largest kept set the final draw takes from the merged kept list without
 // re-reading the logit rows.
 constexpr int kListMax = 512;
@@ -45,7 +43,8 @@ struct ChunkRec {
 };
 constexpr uint32_t kCfNonFinite = 1u;
 
-// Per logit row (one model at one position of one sequence) after merging.
+// Per logit row (one model at one position of one sequence) after merging;
+// held in LDS by the sequence kernel.
 struct RowRec {
   float M;          // row maximum (raw logit)
   float T;          // kept set is {x >= T}; -inf for plain
@@ -91,15 +90,16 @@ struct KParams {
   uint32_t* status;
   float* diag;
   ChunkRec* chunks;
-  uint4* cvec;     // [row][chunk][cap] candidate vectors (raw logits)
-  int32_t* cidx;   // [row][chunk][cap] index of each vector's first logit
-  RowRec* rows;
+  int32_t* cidx;   // [row][chunk][cap] first logit index of each candidate vector
   KeptEntry* kept;  // [rows][kListMax]
 };
 
 // Enqueues the kernels of one call for sequences
 // [p.b_base, p.b_base + nseq): the streaming chunk pass (one instance per
 // sampling mode present), the row merge and the per-sequence finalize.
-hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream);
+// When ev is not NULL, ev[0], ev[1] and ev[2] are recorded on the stream
+// before the streaming pass, between the two stages and after the last.
+hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream,
+                         hipEvent_t* ev = nullptr);
 
 }  // namespace sv

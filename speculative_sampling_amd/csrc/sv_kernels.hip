@@ -1,24 +1,23 @@
 // gfx950 kernels of the verify-and-resample step of speculative sampling.
 //
-// A call runs three kernels on the caller's stream; the kernel boundaries
-// order them, so no work-group ever waits for another:
+// A call runs two stages on the caller's stream; the kernel boundary orders
+// them, so no work-group ever waits for another:
 //
-//   chunk_kernel    grid (sequence, logit row, chunk).  Every used logit row
+//   chunk_kernel    one wave per chunk of a logit row.  Every used row
 //                   (target positions 0..K_b, draft positions 0..K_b-1) is
-//                   split into S chunks of at most 32768 bf16 / 16384 fp32
-//                   logits; each work-group streams its chunk from HBM into
-//                   registers exactly once and reduces it: maximum, sum of
-//                   2^((x - m) c2), the candidate list of the nucleus / top-k
-//                   threshold search, the greedy argmax.  One instance per
-//                   sampling mode keeps the registers of each mode's loop
-//                   minimal.
-//   merge_kernel    grid (sequence, logit row).  Log-sum-exp merge of the
-//                   chunks, radix selection of the threshold over the
-//                   candidates (cached in LDS), kept mass, the probability of
-//                   the row's draft token, and for target rows the kept set
-//                   in vocabulary order with its probabilities.
-//   final_kernel    grid (sequence).  Accept walk, first rejection, resample
-//                   from normalize((q - p)+) or the bonus draw, outputs.
+//                   split into chunks of 8192 bf16 / 4096 fp32 logits; each
+//                   wave streams its chunk from HBM into registers exactly
+//                   once and reduces it: the sum of the terms 2^((x - m) c2)
+//                   and the maximum, the candidate vectors of the nucleus /
+//                   top-k threshold search, the greedy argmax.  One instance
+//                   per sampling mode keeps each mode's registers minimal.
+//   seq_kernel      one work-group per sequence.  Each wave merges one row:
+//                   log-sum-exp over the chunks, radix selection of the
+//                   threshold over the candidates cached in LDS, kept mass,
+//                   the probability of the row's draft token and, for target
+//                   rows, the kept set in vocabulary order.  Then the accept
+//                   walk, the first rejection, the resample from
+//                   normalize((q - p)+) or the bonus draw, and the outputs.
 //
 // The step follows the pages' rule (FDE Interviews breakdown of Chen et al.,
 // section 01 and its figure; paperlayer.ai summary of arXiv 2302.01318,
@@ -475,11 +474,10 @@ __device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, 
   return acc;
 }
 
-// Lists the vectors flagged in `mask` (whole, from the registers) with the
-// index of their first logit, in (vector, lane) order; returns how many
+// Lists the index of the first logit of each vector flagged in `mask`, in
+// (vector, lane) order, i.e. increasing vocabulary index; returns how many
 // there are (entries beyond cap are dropped).
-__device__ __forceinline__ int list_vectors(uint4* dv, int32_t* di, uint32_t mask, const uint4 (&buf)[kLoads],
-                                            int c0, int ve, int cap, int lane) {
+__device__ __forceinline__ int list_vectors(int32_t* di, uint32_t mask, int c0, int ve, int cap, int lane) {
   const uint64_t below = (1ull << lane) - 1ull;
   int n = 0;
 #pragma unroll
@@ -488,10 +486,7 @@ __device__ __forceinline__ int list_vectors(uint4* dv, int32_t* di, uint32_t mas
     const uint64_t bal = __ballot(h);
     if (h) {
       const int pos = n + __popcll(bal & below);
-      if (pos < cap) {
-        dv[pos] = buf[i];
-        di[pos] = c0 + (i * kWave + lane) * ve;
-      }
+      if (pos < cap) di[pos] = c0 + (i * kWave + lane) * ve;
     }
     n += __popcll(bal);
   }
@@ -554,8 +549,7 @@ __device__ __forceinline__ void plain_stats(uint4 (&buf)[kLoads], float c2, cons
 // with a 2^-8 margin in the exponent, a superset of those holding one.
 template <int DT>
 __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats& ps, float c2, bool cand,
-                                             double g, const uint4 (&buf)[kLoads], size_t slot, int c0, int lane,
-                                             ChunkRec& rec) {
+                                             double g, size_t slot, int c0, int lane, ChunkRec& rec) {
   if (ps.st == 2) {
     rec.flags |= kCfNonFinite;
     return;
@@ -570,7 +564,6 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
   // refer the sum to m: 2^(x c2 - o) = 2^((x - m) c2) 2^(m c2 - o)
   rec.z = ps.zw * exp2((double)ps.o - (double)m * (double)c2);
   if (cand) {
-    uint4* dv = P.cvec + slot * (size_t)P.cap;
     int32_t* di = P.cidx + slot * (size_t)P.cap;
     int n = 0;
     float cut = kInf;
@@ -581,7 +574,7 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
       uint32_t mask = 0;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) mask |= ps.emax[i] >= thr ? (1u << i) : 0u;
-      n = list_vectors(dv, di, mask, buf, c0, Fmt<DT>::VE, P.cap, lane);
+      n = list_vectors(di, mask, c0, Fmt<DT>::VE, P.cap, lane);
       if (n <= P.cap) break;
     }
     rec.cnt = n <= P.cap ? n : 0;
@@ -651,8 +644,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
       float cut = kInf;
       if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, cap);
       if (cut != kInf) {
-        const int n = list_vectors(P.cvec + slot * (size_t)cap, P.cidx + slot * (size_t)cap,
-                                   vectors_ge<DT>(buf, cut), buf, c0, VE, cap, lane);
+        const int n = list_vectors(P.cidx + slot * (size_t)cap, vectors_ge<DT>(buf, cut), c0, VE, cap, lane);
         rec.cnt = min(n, cap);
         rec.cut = n <= cap ? cut : kInf;
       }
@@ -678,25 +670,72 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
       for (int w = 0; w < kWaves; ++w)
         if (s_key[w] == key) g = fmax(g, (double)s_max[w]);
     }
-    if (plain) plain_finish<DT>(P, ps, c2, cand, g, buf, slot, c0, lane, rec);
+    if (plain) plain_finish<DT>(P, ps, c2, cand, g, slot, c0, lane, rec);
   }
   if (active && lane == 0) P.chunks[slot] = rec;
 }
 
-// ======================================================= merge kernel ====
+// ===================================================== sequence kernel ====
+//
+// One work-group per sequence.  Wave w merges rows w, w + kSeqWaves, ... of
+// the sequence with wave-level operations only: log-sum-exp over the chunk
+// records, the top-k / nucleus threshold by radix selection over the
+// candidates cached in LDS, the probability of the row's draft token and,
+// for target rows, the kept set in vocabulary order.  After one barrier the
+// work-group runs the accept walk, finds the first rejection and draws the
+// resampled or bonus token.
 
-struct SmemMerge {
-  int pre[kMaxChunks];  // first flat candidate index of each chunk
-  float cx[kMergeCache];
-  int cidx[kMergeCache];
-  unsigned long long cm[kMergeCache];
-  uint32_t hc[256];
+constexpr int kSeqWaves = 12;
+constexpr int kSeqThreads = kSeqWaves * kWave;
+constexpr int kRowCache = 1024;  // candidates of one row held in LDS
+constexpr int kMaxRows = 2 * kMaxK + 1;
+
+// Orders the wave's LDS accesses (and keeps the compiler from moving them).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned long long y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+struct WaveSmem {
+  float cx[kRowCache];  // cached candidates: logit and vocabulary index
+  int ci[kRowCache];
+  uint32_t hc[256];     // radix histogram: counts and fixed-point masses
   unsigned long long hm[256];
-  alignas(16) int kidx[kListMax + 4];
-  unsigned long long km[kListMax];
-  int n, nk;
-  uint32_t sel_digit, sel_hit;
-  Red red;
+  int pre[kWave];       // list start of each chunk of the current batch
+};
+
+struct SmemSeq {
+  WaveSmem w[kSeqWaves];
+  RowRec rows[kMaxRows];
+  double rd[kSeqWaves];
+  int ri[kSeqWaves];
+  uint32_t misc[4];
 };
 
 struct SelOut {
@@ -706,88 +745,91 @@ struct SelOut {
   unsigned long long m_keep, m_above;
 };
 
-// MSB-first radix selection over order-preserving keys.  Finds the largest
-// logit value T whose inclusive descending cumulative count (top-k) or mass
-// (nucleus, fixed point) reaches `target`.  Histograms hold counts and
-// fixed-point masses, so the result does not depend on atomic order.
-// `each(f)` calls f(x, mass) for this thread's share of the elements.
+// MSB-first radix selection (8-bit digits) over order-preserving keys: the
+// largest logit value T whose inclusive descending cumulative count (top-k)
+// or fixed-point mass (nucleus) reaches `target`.  Integer histograms make
+// the result independent of the order of the atomic additions.  each(f)
+// calls f(x, mass) for this lane's share of the elements.
 template <int DT, class Each>
-__device__ __forceinline__ SelOut radix_select(Each&& each, bool by_mass, unsigned long long target,
-                                               SmemMerge& sm) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigned long long target, WaveSmem& ws,
+                                              int lane) {
   const int levels = DT == SV_BF16 ? 2 : 4;
   uint32_t pkey = 0, pmask = 0;
-  unsigned long long above_c = 0, above_m = 0;
+  unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
   bool reached = true;
-  unsigned long long last_c = 0, last_m = 0;
   for (int lv = 0; lv < levels; ++lv) {
     const int shift = 24 - 8 * lv;
-    __syncthreads();
-    sm.hc[tid] = 0;
-    sm.hm[tid] = 0;
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ws.hc[lane + kWave * j] = 0;
+      ws.hm[lane + kWave * j] = 0;
+    }
+    wave_sync();
     each([&](float x, unsigned long long m) {
       const uint32_t key = fkey(x);
       if ((key & pmask) == pkey) {
         const uint32_t dg = (key >> shift) & 255u;
-        atomicAdd(&sm.hc[dg], 1u);
-        atomicAdd(&sm.hm[dg], m);
+        atomicAdd(&ws.hc[dg], 1u);
+        atomicAdd(&ws.hm[dg], m);
       }
     });
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 4l..4l+3; suffix sums run from digit 255 down
-      const int lane = tid;
-      unsigned long long c[4], m[4];
+    wave_sync();
+    // lane l holds digits 255 - 4l - j, j = 0..3: descending over the wave
+    unsigned long long c[4], m[4], lc = 0, lm = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = sm.hc[4 * lane + j];
-        m[j] = sm.hm[4 * lane + j];
-      }
-      const unsigned long long lc = c[0] + c[1] + c[2] + c[3];
-      const unsigned long long lm = m[0] + m[1] + m[2] + m[3];
-      unsigned long long sc = lc, sms = lm;  // inclusive suffix over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long yc = __shfl_down(sc, o);
-        const unsigned long long ym = __shfl_down(sms, o);
-        if (lane + o < 64) {
-          sc += yc;
-          sms += ym;
-        }
-      }
-      unsigned long long rc = sc - lc, rm = sms - lm;  // digits of higher lanes
-      int best = -1;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        rc += c[j];
-        rm += m[j];
-        const bool ok = by_mass ? (above_m + rm >= target) : (above_c + rc >= target);
-        if (ok && best < 0) best = 4 * lane + j;
-      }
-      const int hit = wave_max_i(best);
-      int lowest = 256;
-#pragma unroll
-      for (int j = 3; j >= 0; --j)
-        if (c[j] > 0) lowest = 4 * lane + j;
-      const int low = wave_min_i(lowest);
-      if (lane == 0) {
-        sm.sel_hit = hit >= 0 ? 1u : 0u;
-        sm.sel_digit = hit >= 0 ? (uint32_t)hit : (low < 256 ? (uint32_t)low : 0u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      c[j] = ws.hc[255 - 4 * lane - j];
+      m[j] = ws.hm[255 - 4 * lane - j];
+      lc += c[j];
+      lm += m[j];
     }
-    __syncthreads();
-    const uint32_t dg = sm.sel_digit;
-    if (!sm.sel_hit) reached = false;
-    // everything strictly above the chosen digit joins the "above" totals
-    const unsigned long long add_c = block_sum_u64((int)tid > (int)dg ? sm.hc[tid] : 0ull, sm.red);
-    const unsigned long long add_m = block_sum_u64((int)tid > (int)dg ? sm.hm[tid] : 0ull, sm.red);
-    above_c += add_c;
-    above_m += add_m;
-    last_c = sm.hc[dg];
-    last_m = sm.hm[dg];
-    pkey |= dg << shift;
+    const unsigned long long ec = wave_incl_scan_u64(lc, lane) - lc, em = wave_incl_scan_u64(lm, lane) - lm;
+    // the first digit (from the top) whose inclusive cumulative reaches the target
+    int bj = -1, nj = -1;
+    unsigned long long xc = 0, xm = 0, yc = 0, ym = 0;  // exclusive sums at the hit / last non-empty digit
+    unsigned long long rc = ec, rm = em;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = by_mass ? (above_m + rm + m[j] >= target) : (above_c + rc + c[j] >= target);
+      if (ok && bj < 0) {
+        bj = j;
+        xc = rc;
+        xm = rm;
+      }
+      if (c[j] > 0) {
+        nj = j;
+        yc = rc;
+        ym = rm;
+      }
+      rc += c[j];
+      rm += m[j];
+    }
+    const uint64_t hit = __ballot(bj >= 0);
+    int L, J;
+    unsigned long long ac, am, cc, cm;
+    if (hit) {
+      L = __ffsll((long long)hit) - 1;
+      J = __shfl(bj, L);
+      ac = __shfl(xc, L);
+      am = __shfl(xm, L);
+    } else {
+      reached = false;  // keep everything: the lowest non-empty digit
+      const uint64_t ne = __ballot(nj >= 0);
+      L = ne ? 63 - __clzll((long long)ne) : kWave - 1;
+      J = ne ? __shfl(nj, L) : 3;
+      ac = __shfl(yc, L);
+      am = __shfl(ym, L);
+    }
+    const int dg = 255 - 4 * L - J;
+    cc = ws.hc[dg];
+    cm = ws.hm[dg];
+    above_c += ac;
+    above_m += am;
+    last_c = cc;
+    last_m = cm;
+    pkey |= (uint32_t)dg << shift;
     pmask |= 255u << shift;
+    wave_sync();
   }
   if (DT == SV_BF16) pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
   SelOut r;
@@ -799,80 +841,188 @@ __device__ __forceinline__ SelOut radix_select(Each&& each, bool by_mass, unsign
   return r;
 }
 
-__device__ __forceinline__ unsigned long long fixed_mass(double e) {
-  return (unsigned long long)(e * kFix + 0.5);
+// Fixed-point mass of a logit, in units of the row's largest term:
+// 2^((x - M) c2) = 2^(x c2 - oM) 2^(oM - M c2), with oM = M c2 in fp32 and
+// the second factor (fM) exact in fp64.
+__device__ __forceinline__ unsigned long long mass_of(float x, float c2, float oM, double fM) {
+  return (unsigned long long)((double)__builtin_amdgcn_exp2f(fmaf(x, c2, -oM)) * fM * kFix + 0.5);
 }
 
+// Calls f(have, v, e0) for every listed candidate vector of the row (read
+// back from the logit row), in list order (chunk, then vector, then lane:
+// increasing vocabulary index), on every lane (so that f may use wave
+// ballots); have is false for idle lanes.  Up to 8 x 64 vectors are fetched
+// together.
+template <int DT, bool VEC, class F>
+__device__ __forceinline__ void for_each_listed(const KParams& P, const char* row, size_t slot0, int lane,
+                                                WaveSmem& ws, int cnt0, F&& f) {
+  constexpr int kBatch = 8;
+  const int S = P.S;
+  const ChunkRec* crec = P.chunks + slot0;
+  for (int s0 = 0; s0 < S; s0 += kWave) {
+    const int s = s0 + lane;
+    // cnt0 >= 0: this lane's count of the first batch, already loaded
+    const int cnt = s0 == 0 && cnt0 >= 0 ? cnt0 : (s < S ? crec[s].cnt : 0);
+    const int inc = wave_incl_scan_i(cnt, lane);
+    const int tot = __shfl(inc, kWave - 1);
+    wave_sync();
+    ws.pre[lane] = inc - cnt;
+    wave_sync();
+    const int nb = min(kWave, S - s0);
+    for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
+      uint4 v[kBatch];
+      int e0[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int fi = f0 + q * kWave + lane;
+        v[q] = make_uint4(0, 0, 0, 0);
+        e0[q] = 0;
+        if (fi < tot) {
+          int lo = 0, hi = nb - 1;  // the last chunk whose list starts at or before fi
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ws.pre[mid] <= fi) lo = mid;
+            else hi = mid - 1;
+          }
+          e0[q] = P.cidx[(slot0 + s0 + lo) * (size_t)P.cap + (fi - ws.pre[lo])];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (f0 + q * kWave + lane < tot) v[q] = load_vec<DT, VEC>(row, e0[q], P.V);
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const bool have = f0 + q * kWave + lane < tot;
+        if (__ballot(have)) f(have, v[q], e0[q]);
+      }
+    }
+  }
+  wave_sync();
+}
+
+// Appends the logits >= c of one vector per lane to (dx, di) at *n, in
+// (lane, element) order; entries beyond cap are counted but not stored.
+template <int DT>
+__device__ __forceinline__ void append_ge(bool have, const uint4& v, int e0, float c, int lane, float* dx, int* di,
+                                          int cap, int* n) {
+  constexpr int VE = Fmt<DT>::VE;
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool pass[VE];
+  int before = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < VE; ++k) {
+    pass[k] = have && elem<DT>(v, k) >= c;
+    const uint64_t bal = __ballot(pass[k]);
+    before += __popcll(bal & below);  // passing logits of the lower lanes
+    total += __popcll(bal);
+  }
+  int pos = *n + before;
+#pragma unroll
+  for (int k = 0; k < VE; ++k) {
+    if (pass[k]) {
+      if (pos < cap) {
+        dx[pos] = elem<DT>(v, k);
+        di[pos] = e0 + k;
+      }
+      ++pos;
+    }
+  }
+  *n += total;
+}
+
+// Merges logit row r of sequence b into sm.rows[r] (one wave).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
-  __shared__ SmemMerge sm;
-  const int tid = threadIdx.x;
-  const int S = P.S, R = P.R;
-  const uint32_t blk = blockIdx.x;
-  const int b = P.b_base + (int)(blk / (uint32_t)R);
-  const int r = (int)(blk % (uint32_t)R);
-  const SeqParams sp = load_params(P, b);
-  if (!sp.valid) return;
+__device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp, int b, int r, int lane,
+                                          WaveSmem& ws, RowRec& out) {
+  const int S = P.S;
   bool tgt;
   int t;
-  if (!decode_row(P, sp, r, &tgt, &t)) return;
-  const void* row = row_ptr<DT>(P, b, tgt, t);
-  const size_t rowid = (size_t)b * R + r;
-  const size_t slot0 = rowid * S;
-  const int mode = sp.mode;
-  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
-
-  const ChunkRec* crec = P.chunks + slot0;
-  float m_s = -kInf;
-  int f_s = 0;
-  for (int s = tid; s < S; s += kThreads) {
-    m_s = fmaxf(m_s, crec[s].m);
-    f_s |= (int)crec[s].flags;
-  }
-  const float M = block_max(m_s, sm.red);
-  const int cflags = block_max_i(f_s, sm.red);
-
+  const bool used = decode_row(P, sp, r, &tgt, &t);
   RowRec rr;
-  rr.M = M;
+  rr.M = -kInf;
   rr.T = -kInf;
-  rr.c2 = sp.c2;
+  rr.c2 = (double)(float)sp.c2;
   rr.Zs = 1.0;
   rr.pid = __builtin_nan("");
   rr.g = -1;
   rr.n_keep = -1;
   rr.flags = 0;
   rr.pad = 0;
-  if ((cflags & kCfNonFinite) || !(M < kInf) || isnan(M)) rr.flags |= SV_ST_NONFINITE;
+  if (!used) {
+    if (lane == 0) out = rr;
+    return;
+  }
+  const void* row = row_ptr<DT>(P, b, tgt, t);
+  const size_t rowid = (size_t)b * P.R + r;
+  const size_t slot0 = rowid * S;
+  const int mode = sp.mode;
+  const float c2 = (float)sp.c2;
+  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
+  const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
+  const float xtok = tok_ok ? load_logit<DT>(row, tok) : 0.0f;  // issued early
+
+  // chunk records: held in registers when the row has at most 64 chunks
+  const ChunkRec* crec = P.chunks + slot0;
+  const bool small = S <= kWave;
+  ChunkRec mine;
+  mine.m = -kInf;
+  mine.cut = -kInf;
+  mine.z = 0.0;
+  mine.cnt = 0;
+  mine.arg = 0x7fffffff;
+  mine.flags = 0;
+  mine.pad = 0;
+  if (small && lane < S) mine = crec[lane];
+  auto recs = [&](auto&& f) {
+    if (small) {
+      if (lane < S) f(mine);
+    } else {
+      for (int s = lane; s < S; s += kWave) f(crec[s]);
+    }
+  };
+  float mx = -kInf;
+  uint32_t fl = 0;
+  recs([&](const ChunkRec& c) {
+    mx = fmaxf(mx, c.m);
+    fl |= c.flags;
+  });
+  const float M = wave_max(mx);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) fl |= (uint32_t)__shfl_xor((int)fl, o);
+  rr.M = M;
+  if ((fl & kCfNonFinite) || !(M < kInf) || isnan(M)) rr.flags |= SV_ST_NONFINITE;
   else if (M == -kInf) rr.flags |= SV_ST_EMPTY;
 
   double Z = 0.0;
   if (!(rr.flags & kErrBits) && (mode == SV_PLAIN || mode == SV_TOPP)) {
     double term = 0.0;
-    for (int s = tid; s < S; s += kThreads) {
-      const ChunkRec c = crec[s];
-      if (c.m > -kInf) term += c.z * exp2(((double)c.m - (double)M) * sp.c2);
-    }
-    Z = block_sum(term, sm.red);
+    recs([&](const ChunkRec& c) {
+      if (c.m > -kInf) term += c.z * exp2(((double)c.m - (double)M) * (double)c2);
+    });
+    Z = wave_sum(term);
     if (!(Z > 0.0) || !(Z < 1e300)) rr.flags |= SV_ST_NONFINITE;
   }
 
-  bool list_kept = false;
+  const float oM = M * c2;
+  const double fM = exp2((double)oM - (double)M * (double)c2);
+  bool list_ok = false, cached = false;
+  int n = 0;
   if (!(rr.flags & kErrBits)) {
     if (mode == SV_PLAIN) {
       rr.Zs = Z;
     } else if (mode == SV_GREEDY) {
       int best = 0x7fffffff;
-      for (int s = tid; s < S; s += kThreads)
-        if (crec[s].m == M) best = min(best, crec[s].arg);
-      rr.g = block_min_i(best, sm.red);
+      recs([&](const ChunkRec& c) {
+        if (c.m == M) best = min(best, c.arg);
+      });
+      rr.g = wave_min_i(best);
       rr.T = M;
       rr.n_keep = 1;
     } else {
-      // candidates >= C, where C = max over chunks of the chunk cuts: every
-      // logit >= C of the row is among them
-      float cmax = -kInf;
-      for (int s = tid; s < S; s += kThreads) cmax = fmaxf(cmax, crec[s].cut);
-      const float C = block_max(cmax, sm.red);
+      // every logit >= C of the row lies in a listed candidate vector
+      float cm = -kInf;
+      recs([&](const ChunkRec& c) { cm = fmaxf(cm, c.cut); });
+      const float C = wave_max(cm);
       const bool by_mass = mode == SV_TOPP;
       unsigned long long target;
       if (by_mass) {
@@ -881,75 +1031,52 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
       } else {
         target = (unsigned long long)sp.topk;
       }
+      // candidates >= C: cached in LDS when they fit, else selected
+      // straight from the lists; the full row when the lists are incomplete
+      // or the threshold falls below C
+      const float Cf = fmaxf(C, -kMaxFinite);
       bool fast = C < kInf;
       if (fast) {
-        // one flat index over the chunks' lists: thread t counts chunks 4t..4t+3
-        int cn[4], ls = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int s = 4 * tid + q;
-          cn[q] = s < S ? crec[s].cnt : 0;
-          ls += cn[q];
-        }
-        double tot;
-        int run = (int)block_exclusive_scan((double)ls, &tot, sm.red);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (4 * tid + q < S) sm.pre[4 * tid + q] = run;
-          run += cn[q];
-        }
-        if (tid == 0) sm.n = 0;
-        __syncthreads();
-        const int total = (int)tot;
-        const float Cf = fmaxf(C, -kMaxFinite);
-        for (int f = tid; f < total; f += kThreads) {
-          int lo = 0, hi = S - 1;  // the last chunk whose list starts at or before f
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sm.pre[mid] <= f) lo = mid;
-            else hi = mid - 1;
-          }
-          const size_t at = (slot0 + lo) * (size_t)P.cap + (f - sm.pre[lo]);
-          const uint4 v = P.cvec[at];
-          const int e0 = P.cidx[at];
-#pragma unroll
-          for (int k = 0; k < Fmt<DT>::VE; ++k) {
-            const float x = elem<DT>(v, k);
-            if (x >= Cf) {  // -inf padding past the row end never passes
-              const int pos = atomicAdd(&sm.n, 1);
-              if (pos < kMergeCache) {
-                sm.cx[pos] = x;
-                sm.cidx[pos] = e0 + k;
-                sm.cm[pos] = fixed_mass(exp2(((double)x - (double)M) * sp.c2));
-              }
-            }
-          }
-        }
-        __syncthreads();
-        fast = sm.n <= kMergeCache;
+        for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int e0) {
+          append_ge<DT>(have, v, e0, Cf, lane, ws.cx, ws.ci, kRowCache, &n);
+        });
       }
+      cached = fast && n <= kRowCache;
       SelOut so;
-      if (fast) {
-        const int n = sm.n;
-        so = radix_select<DT>(
+      if (cached) {
+        so = wave_select<DT>(
             [&](auto&& f) {
-              for (int j = tid; j < n; j += kThreads) f(sm.cx[j], sm.cm[j]);
-            },
-            by_mass, target, sm);
-        fast = so.reached && so.T >= C;
-      }
-      if (!fast) {
-        // full-row selection: re-read the row (rare: an incomplete or
-        // insufficient candidate window)
-        const float c2f = (float)sp.c2;
-        so = radix_select<DT>(
-            [&](auto&& f) {
-              for (int e = tid; e < P.V; e += kThreads) {
-                const float x = load_logit<DT>(row, e);
-                f(x, fixed_mass((double)__builtin_amdgcn_exp2f((x - M) * c2f)));
+              for (int j = lane; j < n; j += kWave) {
+                const float x = ws.cx[j];
+                f(x, mass_of(x, c2, oM, fM));
               }
             },
-            by_mass, target, sm);
+            by_mass, target, ws, lane);
+      } else if (fast) {
+        so = wave_select<DT>(
+            [&](auto&& f) {
+              for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int) {
+#pragma unroll
+                for (int k = 0; k < Fmt<DT>::VE; ++k) {
+                  const float x = elem<DT>(v, k);
+                  if (have && x >= Cf) f(x, mass_of(x, c2, oM, fM));
+                }
+              });
+            },
+            by_mass, target, ws, lane);
+      }
+      fast = fast && so.reached && so.T >= C;
+      if (!fast) {
+        // full-row selection: re-read the row
+        cached = false;
+        so = wave_select<DT>(
+            [&](auto&& f) {
+              for (int e = lane; e < P.V; e += kWave) {
+                const float x = load_logit<DT>(row, e);
+                f(x, mass_of(x, c2, oM, fM));
+              }
+            },
+            by_mass, target, ws, lane);
         rr.flags |= SV_ST_FULLSELECT;
       }
       rr.T = so.T;
@@ -961,157 +1088,241 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const KParams P) {
           rr.flags |= SV_ST_MARGIN;
       }
       if (!(rr.Zs > 0.0)) rr.flags |= SV_ST_EMPTY;
-      list_kept = fast && tgt && so.n_keep <= (uint32_t)kListMax;
+      list_ok = fast && tgt && so.n_keep <= (uint32_t)kListMax;
     }
   }
 
   if (tok != INT32_MIN) {  // this row scores a draft token
-    if (tok < 0 || tok >= P.V) {
+    if (!tok_ok) {
       rr.flags |= SV_ST_TOKEN;
     } else if (!(rr.flags & kErrBits)) {
-      if (mode == SV_GREEDY) {
-        rr.pid = tok == rr.g ? 1.0 : 0.0;
-      } else {
-        const float x = load_logit<DT>(row, tok);
-        rr.pid = x >= rr.T ? exp2(((double)x - (double)M) * sp.c2) / rr.Zs : 0.0;
-      }
+      if (mode == SV_GREEDY) rr.pid = tok == rr.g ? 1.0 : 0.0;
+      else rr.pid = xtok >= rr.T ? exp2(((double)xtok - (double)M) * (double)c2) / rr.Zs : 0.0;
     }
   }
 
-  if (list_kept && !(rr.flags & kErrBits)) {
-    // the target row's kept set, in vocabulary order, with probabilities:
-    // compact it, then rank each entry by its vocabulary index
+  if (list_ok && !(rr.flags & kErrBits)) {
+    // the kept set, already in vocabulary order: the cache (or the lists)
+    // filtered by x >= T
     rr.flags |= kRfListOk;
-    const int n = sm.n;
-    __syncthreads();
-    if (tid == 0) sm.nk = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += kThreads) {
-      if (sm.cx[j] >= rr.T) {
-        const int pos = atomicAdd(&sm.nk, 1);
-        sm.kidx[pos] = sm.cidx[j];
-        sm.km[pos] = sm.cm[j];
+    int nk = 0;
+    if (!cached) {
+      for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int e0) {
+        append_ge<DT>(have, v, e0, rr.T, lane, ws.cx, ws.ci, kListMax, &nk);
+      });
+    } else {
+      const uint64_t below = (1ull << lane) - 1ull;
+      for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + lane;
+        const float x = j < n ? ws.cx[j] : -kInf;
+        const int ix = j < n ? ws.ci[j] : 0;
+        const bool keep = j < n && x >= rr.T;
+        const uint64_t bal = __ballot(keep);
+        wave_sync();
+        if (keep) {
+          const int pos = nk + __popcll(bal & below);  // pos <= j: no entry is overwritten unread
+          ws.cx[pos] = x;
+          ws.ci[pos] = ix;
+        }
+        nk += __popcll(bal);
+        wave_sync();
       }
     }
-    __syncthreads();
-    const int nk = sm.nk;  // == n_keep <= kListMax
-    for (int j = nk; j < ((nk + 3) & ~3); ++j)
-      if (tid == 0) sm.kidx[j] = 0x7fffffff;  // pad to whole int4s
-    __syncthreads();
-    KeptEntry* out = P.kept + rowid * kListMax;
-    const int4* k4 = reinterpret_cast<const int4*>(sm.kidx);
-    for (int j = tid; j < nk; j += kThreads) {
-      const int my = sm.kidx[j];
-      int rank = 0;
-      for (int i = 0; i < (nk + 3) / 4; ++i) {
-        const int4 v = k4[i];
-        rank += (v.x < my) + (v.y < my) + (v.z < my) + (v.w < my);
+    if (P.R <= kSeqWaves) {
+      // the set stays in this wave's LDS for the draw, with the draft's
+      // logits at its tokens (for a resample at this position)
+      wave_sync();
+      if (t < sp.Kb) {
+        const void* drow = row_ptr<DT>(P, b, false, t);
+        for (int j = lane; j < nk; j += kWave) ws.cx[kListMax + j] = load_logit<DT>(drow, ws.ci[j]);
       }
-      KeptEntry ke;
-      ke.idx = my;
-      ke.pad = 0;
-      ke.q = (double)sm.km[j] / kFix / rr.Zs;
-      out[rank] = ke;
+    } else {
+      KeptEntry* kl = P.kept + rowid * kListMax;
+      for (int j = lane; j < nk; j += kWave) {
+        KeptEntry ke;
+        ke.idx = ws.ci[j];
+        ke.pad = 0;
+        ke.q = (double)mass_of(ws.cx[j], c2, oM, fM) / kFix / rr.Zs;
+        kl[j] = ke;
+      }
     }
   }
-  if (tid == 0) P.rows[rowid] = rr;
+  if (lane == 0) out = rr;
 }
 
-// ======================================================= final kernel ====
-
-struct SmemFinal {
-  int idx[kListMax];
-  double w[kListMax];
-  double c[kListMax];
-  Red red;
-  uint32_t misc[4];
-};
+// ------------------------------------------------------------- draws ----
 
 struct Draw {
   int y;
-  double S;
   uint32_t flags;
 };
 
-// Inverse CDF over the target's kept set (vocabulary order): w = (q - p)+
-// when resampling, else w = q.
-template <int DT>
-__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample,
-                                               const RowRec& rp, size_t rowq, const void* drow, double u,
-                                               SmemFinal& sm) {
-  const int tid = threadIdx.x;
-  const int N = rq.n_keep;  // <= kListMax
-  const KeptEntry* kl = P.kept + rowq * kListMax;
-  double qv[2];
-  int iv[2];
+__device__ __forceinline__ double seq_sum(double v, SmemSeq& sm) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.rd[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * tid + j;
-    qv[j] = 0.0;
-    iv[j] = 0;
-    if (i < N) {
-      const KeptEntry ke = kl[i];
-      qv[j] = ke.q;
-      iv[j] = ke.idx;
+  for (int w = 0; w < kSeqWaves; ++w) s += sm.rd[w];
+  return s;
+}
+__device__ __forceinline__ int seq_min_i(int v, SmemSeq& sm) {
+  v = wave_min_i(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.ri[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = sm.ri[0];
+#pragma unroll
+  for (int w = 1; w < kSeqWaves; ++w) s = min(s, sm.ri[w]);
+  return s;
+}
+__device__ __forceinline__ int seq_max_i(int v, SmemSeq& sm) {
+  v = wave_max_i(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.ri[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = sm.ri[0];
+#pragma unroll
+  for (int w = 1; w < kSeqWaves; ++w) s = max(s, sm.ri[w]);
+  return s;
+}
+// Exclusive prefix over the work-group in thread order; *total = the sum.
+__device__ __forceinline__ double seq_exclusive_scan(double v, double* total, SmemSeq& sm) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double inc = wave_incl_scan(v, lane);
+  __syncthreads();
+  if (lane == 63) sm.rd[w] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int j = 0; j < kSeqWaves; ++j) {
+    base += j < w ? sm.rd[j] : 0.0;
+    tot += sm.rd[j];
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
+// Inverse CDF over the target's kept set in vocabulary order (one wave):
+// w = (q - p)+ when resampling, else w = q.  Lane l owns entries 8l..8l+7.
+// The set is read from the LDS of the wave that merged the row (ls), or
+// from global memory.
+template <int DT>
+__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
+                                               size_t rowq, const void* drow, double u, int lane,
+                                               const WaveSmem* ls) {
+  constexpr int E = kListMax / kWave;
+  const int N = rq.n_keep;  // <= kListMax
+  double qv[E];
+  int iv[E];
+  float xp[E];
+  if (ls) {
+    const float c2q = (float)rq.c2;
+    const float oM = rq.M * c2q;
+    const double fM = exp2((double)oM - (double)rq.M * (double)c2q);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = E * lane + j;
+      qv[j] = 0.0;
+      iv[j] = 0;
+      xp[j] = -kInf;
+      if (i < N) {
+        iv[j] = ls->ci[i];
+        qv[j] = (double)mass_of(ls->cx[i], c2q, oM, fM) / kFix / rq.Zs;
+        if (resample) xp[j] = ls->cx[kListMax + i];
+      }
+    }
+  } else {
+    const KeptEntry* kl = P.kept + rowq * kListMax;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = E * lane + j;
+      qv[j] = 0.0;
+      iv[j] = 0;
+      if (i < N) {
+        const KeptEntry ke = kl[i];
+        qv[j] = ke.q;
+        iv[j] = ke.idx;
+      }
+    }
+    if (resample) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) xp[j] = E * lane + j < N ? load_logit<DT>(drow, iv[j]) : -kInf;
     }
   }
   Draw d;
   d.flags = 0;
-  double w[2];
+  double w[E];
   bool use_p = resample;
   double total = 0.0, ex = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
+    double s = 0.0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < E; ++j) {
       w[j] = qv[j];
-      if (use_p && 2 * tid + j < N) {
-        const float xp = load_logit<DT>(drow, iv[j]);
-        const double p = xp >= rp.T ? exp2(((double)xp - (double)rp.M) * rp.c2) / rp.Zs : 0.0;
+      if (use_p && E * lane + j < N) {
+        const double p = xp[j] >= rp.T ? exp2(((double)xp[j] - (double)rp.M) * rp.c2) / rp.Zs : 0.0;
         w[j] = qv[j] > p ? qv[j] - p : 0.0;
       }
+      s += w[j];
     }
-    ex = block_exclusive_scan(w[0] + w[1], &total, sm.red);
+    const double inc = wave_incl_scan(s, lane);
+    total = __shfl(inc, kWave - 1);
+    ex = inc - s;
     if (total > 0.0 || !use_p) break;
     d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
     use_p = false;
   }
-  d.S = total;
   const double target = u * total;
-  // first element whose running sum exceeds the target; last non-zero one
+  // first entry whose running sum exceeds the target; the last non-zero one
   int first = 0x7fffffff, lastnz = -1, firstnz = 0x7fffffff;
-  double c = ex;
+  double c = ex, clo = 0.0, chi = 0.0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * tid + j;
+  for (int j = 0; j < E; ++j) {
+    const int i = E * lane + j;
     const double cn = c + w[j];
-    if (i < N) {
-      sm.w[i] = w[j];
-      sm.c[i] = cn;
-      sm.idx[i] = iv[j];
-      if (w[j] > 0.0) {
-        if (cn > target) first = min(first, i);
-        lastnz = max(lastnz, i);
-        firstnz = min(firstnz, i);
+    if (i < N && w[j] > 0.0) {
+      if (cn > target && first == 0x7fffffff) {
+        first = i;
+        clo = c;
+        chi = cn;
       }
+      lastnz = max(lastnz, i);
+      firstnz = min(firstnz, i);
     }
     c = cn;
   }
-  first = block_min_i(first, sm.red);
-  lastnz = block_max_i(lastnz, sm.red);
-  firstnz = block_min_i(firstnz, sm.red);
-  int iy = first <= lastnz ? first : lastnz;
-  if (iy < 0) iy = 0;
-  d.y = N > 0 ? sm.idx[iy] : 0;
-  if (N > 0 && lastnz >= 0) {
+  const int f = wave_min_i(first);
+  const int lnz = wave_max_i(lastnz);
+  const int fnz = wave_min_i(firstnz);
+  int iy;
+  double lo, hi;
+  if (f <= lnz) {
+    iy = f;
+    const int src = f / E;
+    lo = __shfl(clo, src);
+    hi = __shfl(chi, src);
+  } else {  // rounding left no entry above the target
+    iy = lnz < 0 ? 0 : lnz;
+    lo = total;
+    hi = total;
+  }
+  const int src = iy / E;
+  int yv = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (E * lane + j == iy) yv = iv[j];
+  d.y = N > 0 ? __shfl(yv, src) : 0;
+  if (N > 0 && lnz >= 0 && total > 0.0) {
     // margins of interior CDF boundaries
-    const double hi = sm.c[iy] / d.S, lo = (sm.c[iy] - sm.w[iy]) / d.S;
-    if ((firstnz < iy && u - lo < kWindow) || (lastnz > iy && hi - u < kWindow)) d.flags |= SV_ST_MARGIN;
+    if ((fnz < iy && u - lo / total < kWindow) || (lnz > iy && hi / total - u < kWindow)) d.flags |= SV_ST_MARGIN;
   }
   return d;
 }
 
-template <int DT>
-__device__ __forceinline__ double weight(const RowRec& rq, bool use_p, const RowRec& rp, float xq, float xp) {
+// Weight of one token for the full-row draw: q, or (q - p)+.
+__device__ __forceinline__ double row_weight(const RowRec& rq, bool use_p, const RowRec& rp, float xq, float xp) {
   double q = 0.0;
   if (xq >= rq.T) q = (double)__builtin_amdgcn_exp2f((xq - rq.M) * (float)rq.c2) / rq.Zs;
   if (!use_p) return q;
@@ -1120,47 +1331,45 @@ __device__ __forceinline__ double weight(const RowRec& rq, bool use_p, const Row
   return q > p ? q - p : 0.0;
 }
 
-// Inverse CDF over full logit rows re-read from memory, in tiles of
-// 256 x 8 tokens (thread t owns tokens 8t..8t+7 of a tile).
+// Inverse CDF over full logit rows re-read from memory by the whole
+// work-group, in tiles of kSeqThreads x 8 tokens (thread i owns tokens
+// 8i..8i+7 of a tile).
 template <int DT>
-__device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample,
-                                               const RowRec& rp, const void* qrow, const void* prow,
-                                               double u, SmemFinal& sm) {
+__device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
+                                               const void* qrow, const void* prow, double u, SmemSeq& sm) {
   const int tid = threadIdx.x;
   const int V = P.V;
-  constexpr int TILE = kThreads * 8;
+  constexpr int TILE = kSeqThreads * 8;
   Draw d;
   d.flags = SV_ST_REREAD;
   d.y = 0;
-  d.S = 0.0;
   bool use_p = resample;
   for (int pass = 0; pass < 2; ++pass) {
     // total mass and the first / last token of non-zero weight
-    double S = 0.0;
+    double st = 0.0;
     int nz_lo = 0x7fffffff, nz_hi = -1;
     for (int base = 0; base < V; base += TILE) {
-      double s = 0.0;
+#pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int e = base + 8 * tid + k;
         if (e < V) {
-          const double w = weight<DT>(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f);
-          s += w;
+          const double w = row_weight(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f);
+          st += w;
           if (w > 0.0) {
             nz_lo = min(nz_lo, e);
             nz_hi = max(nz_hi, e);
           }
         }
       }
-      S += block_sum(s, sm.red);
     }
-    nz_lo = block_min_i(nz_lo, sm.red);
-    nz_hi = block_max_i(nz_hi, sm.red);
+    const double S = seq_sum(st, sm);
+    nz_lo = seq_min_i(nz_lo, sm);
+    nz_hi = seq_max_i(nz_hi, sm);
     if (!(S > 0.0) && pass == 0 && use_p) {
       d.flags |= SV_ST_ZERO_RESIDUAL;
       use_p = false;
       continue;
     }
-    d.S = S;
     const double target = u * S;
     double run = 0.0;
     int y = -1;
@@ -1171,16 +1380,16 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int e = base + 8 * tid + k;
-        wk[k] = e < V ? weight<DT>(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f) : 0.0;
+        wk[k] = e < V ? row_weight(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f)
+                      : 0.0;
         s += wk[k];
       }
       double tile;
-      const double ex = block_exclusive_scan(s, &tile, sm.red);
+      const double ex = seq_exclusive_scan(s, &tile, sm);
       if (run + tile > target) {
         // the thread whose span crosses the target finds the token
         int cand = 0x7fffffff;
-        double c = run + ex;
-        double cl = 0.0, ch = 0.0;
+        double c = run + ex, cl = 0.0, ch = 0.0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const double cn = c + wk[k];
@@ -1191,15 +1400,16 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
           }
           c = cn;
         }
-        const int ymin = block_min_i(cand, sm.red);
+        const int ymin = seq_min_i(cand, sm);
         if (ymin != 0x7fffffff) {
+          __syncthreads();
           if (cand == ymin) {
-            sm.red.d[0] = cl;  // block_min_i has returned: its slots are free
-            sm.red.d[1] = ch;
+            sm.rd[0] = cl;
+            sm.rd[1] = ch;
           }
           __syncthreads();
-          lo = sm.red.d[0];
-          hi = sm.red.d[1];
+          lo = sm.rd[0];
+          hi = sm.rd[1];
           __syncthreads();
           y = ymin;
         }
@@ -1221,19 +1431,20 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
 
 __device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st) {
   const int tid = threadIdx.x;
-  for (int i = tid; i <= P.K_max; i += kThreads) P.out_tokens[(size_t)b * (P.K_max + 1) + i] = -1;
+  for (int i = tid; i <= P.K_max; i += kSeqThreads) P.out_tokens[(size_t)b * (P.K_max + 1) + i] = -1;
   if (P.diag)
-    for (int i = tid; i < 2 * P.K_max; i += kThreads) P.diag[(size_t)b * 2 * P.K_max + i] = __builtin_nanf("");
+    for (int i = tid; i < 2 * P.K_max; i += kSeqThreads) P.diag[(size_t)b * 2 * P.K_max + i] = __builtin_nanf("");
   if (tid == 0) {
     P.accepted[b] = -1;
     if (P.status) P.status[b] = st;
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void final_kernel(const KParams P) {
-  __shared__ SmemFinal sm;
-  const int tid = threadIdx.x;
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
+  __shared__ SmemSeq sm;
+  const int tid = threadIdx.x, lane = (int)__lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int b = P.b_base + (int)blockIdx.x;
   const SeqParams sp = load_params(P, b);
   if (!sp.valid) {
@@ -1241,77 +1452,100 @@ __global__ __launch_bounds__(kThreads) void final_kernel(const KParams P) {
     return;
   }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
-  const uint64_t g = P.row_offset + (uint64_t)b;
-  const size_t rbase = (size_t)b * R;
+  for (int r = wv; r < R; r += kSeqWaves) merge_row<DT, VEC>(P, sp, b, r, lane, sm.w[wv], sm.rows[r]);
+  __syncthreads();
 
   // OR of the used rows' flags
   uint32_t v = 0;
-  for (int t = tid; t <= Kb; t += kThreads) v |= P.rows[rbase + t].flags;
-  for (int t = tid; t < Kb; t += kThreads) v |= P.rows[rbase + KM + 1 + t].flags;
+  for (int t = tid; t <= Kb; t += kSeqThreads) v |= sm.rows[t].flags;
+  for (int t = tid; t < Kb; t += kSeqThreads) v |= sm.rows[KM + 1 + t].flags;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o);
+  if (lane == 0) sm.ri[wv] = (int)v;
   __syncthreads();
-  if ((tid & 63) == 0) sm.red.i[tid >> 6] = (int)v;
-  __syncthreads();
-  uint32_t st = (uint32_t)(sm.red.i[0] | sm.red.i[1] | sm.red.i[2] | sm.red.i[3]);
+  uint32_t st = 0;
+#pragma unroll
+  for (int w = 0; w < kSeqWaves; ++w) st |= (uint32_t)sm.ri[w];
   __syncthreads();
   st &= ~kRfListOk;
   if (st & kErrBits) {
     write_error(P, b, st & kErrBits);
     return;
   }
-  // accept walk (one thread; K_b <= 64)
-  if (tid == 0) {
+  const uint64_t g = P.row_offset + (uint64_t)b;
+  // accept walk: lane t scores position t0 + t; the first rejection by ballot
+  if (wv == 0) {
     int n = Kb;
-    uint32_t s2 = 0;
-    for (int t = 0; t < Kb; ++t) {
-      const double q = P.rows[rbase + t].pid, p = P.rows[rbase + KM + 1 + t].pid;
-      if (P.diag) {
-        P.diag[((size_t)b * KM + t) * 2 + 0] = (float)q;
-        P.diag[((size_t)b * KM + t) * 2 + 1] = (float)p;
+    uint32_t s_all = 0;
+    for (int t0 = 0; t0 < KM; t0 += kWave) {
+      const int t = t0 + lane;
+      bool rej = false;
+      uint32_t s2 = 0;
+      if (t < KM) {
+        double q = __builtin_nan(""), p = __builtin_nan("");
+        if (t < Kb) {
+          q = sm.rows[t].pid;
+          p = sm.rows[KM + 1 + t].pid;
+          const double u = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
+          rej = !(u * p < q);
+          if (p == 0.0) s2 |= SV_ST_PZERO;
+          if (p > 0.0) {
+            const double ratio = q / p;
+            if (ratio < 1.0 + kWindow && fabs(u - ratio) < kWindow) s2 |= SV_ST_MARGIN;
+          }
+        }
+        if (P.diag) {
+          P.diag[((size_t)b * KM + t) * 2 + 0] = (float)q;
+          P.diag[((size_t)b * KM + t) * 2 + 1] = (float)p;
+        }
       }
-      if (n < Kb) continue;
-      const double u = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
-      if (p == 0.0) s2 |= SV_ST_PZERO;
-      const bool accept = u * p < q;
-      if (p > 0.0) {
-        const double ratio = q / p;
-        if (ratio < 1.0 + kWindow && fabs(u - ratio) < kWindow) s2 |= SV_ST_MARGIN;
-      }
-      if (!accept) n = t;
+      const bool walking = n == Kb;  // no rejection in earlier batches
+      const uint64_t rb = __ballot(rej);
+      if (walking && rb) n = t0 + __ffsll((long long)rb) - 1;
+      // status bits of the positions the walk reached (up to the first rejection)
+      uint32_t s3 = (walking && t <= n && t < Kb) ? s2 : 0u;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s3 |= (uint32_t)__shfl_xor((int)s3, o);
+      s_all |= s3;
     }
-    if (P.diag)
-      for (int t = Kb; t < KM; ++t) {
-        P.diag[((size_t)b * KM + t) * 2 + 0] = __builtin_nanf("");
-        P.diag[((size_t)b * KM + t) * 2 + 1] = __builtin_nanf("");
-      }
-    sm.misc[0] = (uint32_t)n;
-    sm.misc[1] = s2;
+    if (lane == 0) {
+      sm.misc[0] = (uint32_t)n;
+      sm.misc[1] = s_all;
+    }
   }
   __syncthreads();
   const int n = (int)sm.misc[0];
   st |= sm.misc[1];
-  __syncthreads();
 
   const bool resample = n < Kb;
-  const RowRec rq = P.rows[rbase + n];
-  RowRec rp = rq;
-  if (resample) rp = P.rows[rbase + KM + 1 + n];
+  const RowRec rq = sm.rows[n];
+  const RowRec rp = resample ? sm.rows[KM + 1 + n] : rq;
   const double u = uniform24(P.seed, g, (uint32_t)n, resample ? kPurposeResample : kPurposeBonus);
   Draw d;
   if (sp.mode == SV_GREEDY) {
     d.y = rq.g;
-    d.S = 1.0;
     d.flags = (resample && rp.g == rq.g) ? SV_ST_ZERO_RESIDUAL : 0u;
   } else if (rq.flags & kRfListOk) {
-    d = draw_from_list<DT>(P, rq, resample, rp, rbase + n, resample ? row_ptr<DT>(P, b, false, n) : nullptr,
-                           u, sm);
+    d.y = 0;
+    d.flags = 0;
+    if (wv == 0) {
+      d = draw_from_list<DT>(P, rq, resample, rp, (size_t)b * R + n,
+                             resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, lane,
+                             R <= kSeqWaves ? &sm.w[n] : nullptr);
+      if (lane == 0) {
+        sm.misc[2] = (uint32_t)d.y;
+        sm.misc[3] = d.flags;
+      }
+    }
+    __syncthreads();
+    d.y = (int)sm.misc[2];
+    d.flags = sm.misc[3];
   } else {
     d = draw_from_rows<DT>(P, rq, resample, rp, row_ptr<DT>(P, b, true, n),
                            resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, sm);
   }
   st |= d.flags;
-  for (int i = tid; i <= KM; i += kThreads) {
+  for (int i = tid; i <= KM; i += kSeqThreads) {
     int val = -1;
     if (i < n) val = P.tokens[(size_t)b * KM + i];
     else if (i == n) val = d.y;
@@ -1335,30 +1569,31 @@ void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream) {
 }
 
 template <int DT, bool VEC>
-void launch_all(const KParams& p, int nseq, hipStream_t stream) {
-  const dim3 block(kThreads);
+hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], stream);
   // one streaming instance per sampling mode that can occur
-  for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode) {
+  for (int mode = SV_PLAIN; mode <= SV_GREEDY && e == hipSuccess; ++mode) {
     if (!p.mode && mode != p.dmode) continue;
     const size_t waves = (size_t)nseq * p.R * p.S;
     launch_chunk<DT, VEC>(p, mode, dim3((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave))), stream);
   }
-  hipLaunchKernelGGL((merge_kernel<DT, VEC>), dim3((unsigned)((size_t)nseq * p.R)), block, 0, stream, p);
-  hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)nseq), block, 0, stream, p);
+  if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess)
+    hipLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream, p);
+  if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
+  return e;
 }
 
 }  // namespace
 
-hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream) {
+hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream, hipEvent_t* ev) {
   if (nseq <= 0) return hipSuccess;
-  if (dtype == SV_BF16) {
-    if (vec) launch_all<SV_BF16, true>(p, nseq, stream);
-    else launch_all<SV_BF16, false>(p, nseq, stream);
-  } else {
-    if (vec) launch_all<SV_F32, true>(p, nseq, stream);
-    else launch_all<SV_F32, false>(p, nseq, stream);
-  }
-  return hipGetLastError();
+  hipError_t e;
+  if (dtype == SV_BF16) e = vec ? launch_all<SV_BF16, true>(p, nseq, stream, ev) : launch_all<SV_BF16, false>(p, nseq, stream, ev);
+  else e = vec ? launch_all<SV_F32, true>(p, nseq, stream, ev) : launch_all<SV_F32, false>(p, nseq, stream, ev);
+  const hipError_t l = hipGetLastError();
+  return e != hipSuccess ? e : l;
 }
 
 }  // namespace sv
