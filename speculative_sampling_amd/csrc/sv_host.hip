@@ -26,7 +26,7 @@ struct sv_handle_s {
   void* ws;
   size_t ws_bytes;
   sv::ChunkRec* chunks;
-  int32_t* cidx;
+  int2* cent;
   sv::KeptEntry* kept;
   hipEvent_t last;
   bool has_run;
@@ -48,7 +48,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, cap, R_max;
-  size_t off_chunks, off_cidx, off_kept, total;
+  size_t off_chunks, off_cent, off_kept, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -78,8 +78,8 @@ Geometry geometry(const sv_config* cfg) {
   size_t off = 0;
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
-  g.off_cidx = off;
-  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int32_t), 256);
+  g.off_cent = off;
+  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int2), 256);
   g.off_kept = off;
   off = align_up(off + rows * sv::kListMax * sizeof(sv::KeptEntry), 256);
   g.total = off;
@@ -156,7 +156,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   }
   char* base = static_cast<char*>(h->ws);
   h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
-  h->cidx = reinterpret_cast<int32_t*>(base + g.off_cidx);
+  h->cent = reinterpret_cast<int2*>(base + g.off_cent);
   h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -213,7 +213,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.status = a->row_status;
   p.diag = a->diag;
   p.chunks = h->chunks;
-  p.cidx = h->cidx;
+  p.cent = h->cent;
   p.kept = h->kept;
 
   int prev = 0;

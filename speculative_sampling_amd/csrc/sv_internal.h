@@ -39,7 +39,7 @@ struct ChunkRec {
   int32_t cnt;     // candidate vectors stored
   int32_t arg;     // lowest index whose logit equals m      (greedy)
   uint32_t flags;  // kCfNonFinite
-  int32_t pad;
+  float o;         // listed vectors' keys are terms 2^(x c2 - o) (nucleus)
 };
 constexpr uint32_t kCfNonFinite = 1u;
 
@@ -90,7 +90,7 @@ struct KParams {
   uint32_t* status;
   float* diag;
   ChunkRec* chunks;
-  int32_t* cidx;   // [row][chunk][cap] first logit index of each candidate vector
+  int2* cent;      // [row][chunk][cap] candidate vectors: first logit index and key
   KeptEntry* kept;  // [rows][kListMax]
 };
 

@@ -376,19 +376,21 @@ __device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut) {
   return n;
 }
 
-// Per-lane bitmask of the vectors holding an element >= cut.
+// Per-lane bitmask of the vectors holding an element >= cut, and each
+// vector's largest logit (vmax[i]).
 template <int DT>
-__device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut) {
+__device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut, float (&vmax)[kLoads]) {
   constexpr int VE = Fmt<DT>::VE;
   const float c = fmaxf(cut, -kMaxFinite);
   fence_regs(buf);
   uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    bool any = false;
+    float m = -kInf;
 #pragma unroll
-    for (int k = 0; k < VE; ++k) any |= elem<DT>(buf[i], k) >= c;
-    mask |= any ? (1u << i) : 0u;
+    for (int k = 0; k < VE; ++k) m = fmaxf(m, elem<DT>(buf[i], k));
+    vmax[i] = m;
+    mask |= m >= c ? (1u << i) : 0u;
   }
   return mask;
 }
@@ -474,10 +476,12 @@ __device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, 
   return acc;
 }
 
-// Lists the index of the first logit of each vector flagged in `mask`, in
-// (vector, lane) order, i.e. increasing vocabulary index; returns how many
-// there are (entries beyond cap are dropped).
-__device__ __forceinline__ int list_vectors(int32_t* di, uint32_t mask, int c0, int ve, int cap, int lane) {
+// Lists each vector flagged in `mask` as (index of its first logit, key),
+// in (vector, lane) order, i.e. increasing vocabulary index; returns how
+// many there are (entries beyond cap are dropped).  key[i] is the vector's
+// largest term 2^(x c2 - o) (nucleus) or its largest logit (top-k).
+__device__ __forceinline__ int list_vectors(int2* de, uint32_t mask, const float* key, int c0, int ve, int cap,
+                                            int lane) {
   const uint64_t below = (1ull << lane) - 1ull;
   int n = 0;
 #pragma unroll
@@ -486,7 +490,7 @@ __device__ __forceinline__ int list_vectors(int32_t* di, uint32_t mask, int c0, 
     const uint64_t bal = __ballot(h);
     if (h) {
       const int pos = n + __popcll(bal & below);
-      if (pos < cap) di[pos] = c0 + (i * kWave + lane) * ve;
+      if (pos < cap) de[pos] = make_int2(c0 + (i * kWave + lane) * ve, __float_as_int(key[i]));
     }
     n += __popcll(bal);
   }
@@ -561,10 +565,11 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
   }
   const float m = (float)ps.ma;
   rec.m = m;
+  rec.o = ps.o;
   // refer the sum to m: 2^(x c2 - o) = 2^((x - m) c2) 2^(m c2 - o)
   rec.z = ps.zw * exp2((double)ps.o - (double)m * (double)c2);
   if (cand) {
-    int32_t* di = P.cidx + slot * (size_t)P.cap;
+    int2* de = P.cent + slot * (size_t)P.cap;
     int n = 0;
     float cut = kInf;
     for (int attempt = 0; attempt < 3; ++attempt) {
@@ -574,7 +579,7 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
       uint32_t mask = 0;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) mask |= ps.emax[i] >= thr ? (1u << i) : 0u;
-      n = list_vectors(di, mask, c0, Fmt<DT>::VE, P.cap, lane);
+      n = list_vectors(de, mask, ps.emax, c0, Fmt<DT>::VE, P.cap, lane);
       if (n <= P.cap) break;
     }
     rec.cnt = n <= P.cap ? n : 0;
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
   rec.cnt = 0;
   rec.arg = -1;
   rec.flags = 0;
-  rec.pad = 0;
+  rec.o = 0.0f;
   uint4 buf[kLoads];
   if (active) load_chunk<DT, VEC>(buf, row, c0, c1, lane);
 
@@ -642,9 +647,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
     } else {
       const int need = sp.topk, cap = P.cap;
       float cut = kInf;
-      if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, cap);
+      // at most about 2k candidates per chunk keep the row's list short
+      if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, min(cap, max(2 * need, 64)));
       if (cut != kInf) {
-        const int n = list_vectors(P.cidx + slot * (size_t)cap, vectors_ge<DT>(buf, cut), c0, VE, cap, lane);
+        float vmax[kLoads];
+        const uint32_t mask = vectors_ge<DT>(buf, cut, vmax);
+        const int n = list_vectors(P.cent + slot * (size_t)cap, mask, vmax, c0, VE, cap, lane);
         rec.cnt = min(n, cap);
         rec.cut = n <= cap ? cut : kInf;
       }
@@ -687,7 +695,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
 
 constexpr int kSeqWaves = 12;
 constexpr int kSeqThreads = kSeqWaves * kWave;
-constexpr int kRowCache = 1024;  // candidates of one row held in LDS
+constexpr int kRowCache = 768;  // candidate logits of one row held in LDS
+constexpr int kVecList = 768;   // candidate vectors of one row that pass the row's cut
 constexpr int kMaxRows = 2 * kMaxK + 1;
 
 // Orders the wave's LDS accesses (and keeps the compiler from moving them).
@@ -723,11 +732,14 @@ __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
 }
 
 struct WaveSmem {
-  float cx[kRowCache];  // cached candidates: logit and vocabulary index
-  int ci[kRowCache];
+  float cx[kRowCache];  // cached candidates: logit and vocabulary index;
+  int ci[kRowCache];    //   afterwards the kept set in vocabulary order
+  int vi[kVecList];     // first index of each candidate vector; afterwards
+                        //   the draft's logits at the kept set (float bits)
   uint32_t hc[256];     // radix histogram: counts and fixed-point masses
   unsigned long long hm[256];
   int pre[kWave];       // list start of each chunk of the current batch
+  float thr[kWave];     // key threshold of each chunk of the current batch
 };
 
 struct SmemSeq {
@@ -848,35 +860,45 @@ __device__ __forceinline__ unsigned long long mass_of(float x, float c2, float o
   return (unsigned long long)((double)__builtin_amdgcn_exp2f(fmaf(x, c2, -oM)) * fM * kFix + 0.5);
 }
 
-// Calls f(have, v, e0) for every listed candidate vector of the row (read
-// back from the logit row), in list order (chunk, then vector, then lane:
-// increasing vocabulary index), on every lane (so that f may use wave
-// ballots); have is false for idle lanes.  Up to 8 x 64 vectors are fetched
-// together.
-template <int DT, bool VEC, class F>
-__device__ __forceinline__ void for_each_listed(const KParams& P, const char* row, size_t slot0, int lane,
-                                                WaveSmem& ws, int cnt0, F&& f) {
-  constexpr int kBatch = 8;
+// Collects, in list order (chunk, vector, lane: increasing vocabulary
+// index), the first index of every listed candidate vector of the row whose
+// key reaches the threshold of its chunk for the cut Cu, into ws.vi;
+// returns how many there are (entries beyond kVecList are counted only).
+// keep_keys also stores each kept entry's key in ws.cx.  The key of a
+// nucleus vector is its largest term 2^(x c2 - o_chunk) (the
+// threshold 2^(Cu c2 - o_chunk - 2^-8) keeps every vector holding x >= Cu);
+// that of a top-k vector its largest logit (threshold Cu).
+template <class RecAt>
+__device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, RecAt&& rec_at, float Cu, float c2,
+                                             bool terms, int lane, WaveSmem& ws, bool keep_keys = false) {
+  constexpr int kBatch = 4;
   const int S = P.S;
-  const ChunkRec* crec = P.chunks + slot0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nv = 0;
   for (int s0 = 0; s0 < S; s0 += kWave) {
     const int s = s0 + lane;
-    // cnt0 >= 0: this lane's count of the first batch, already loaded
-    const int cnt = s0 == 0 && cnt0 >= 0 ? cnt0 : (s < S ? crec[s].cnt : 0);
+    int cnt = 0;
+    float th = -kInf;
+    if (s < S) {
+      const ChunkRec c = rec_at(s);
+      cnt = c.cnt;
+      th = terms ? exp2f((float)((double)Cu * (double)c2 - (double)c.o) - 0.00390625f) : Cu;
+    }
     const int inc = wave_incl_scan_i(cnt, lane);
     const int tot = __shfl(inc, kWave - 1);
     wave_sync();
     ws.pre[lane] = inc - cnt;
+    ws.thr[lane] = th;
     wave_sync();
     const int nb = min(kWave, S - s0);
     for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
-      uint4 v[kBatch];
-      int e0[kBatch];
+      int2 ent[kBatch];
+      int ch[kBatch];
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int fi = f0 + q * kWave + lane;
-        v[q] = make_uint4(0, 0, 0, 0);
-        e0[q] = 0;
+        ent[q] = make_int2(0, 0);
+        ch[q] = 0;
         if (fi < tot) {
           int lo = 0, hi = nb - 1;  // the last chunk whose list starts at or before fi
           while (lo < hi) {
@@ -884,20 +906,43 @@ __device__ __forceinline__ void for_each_listed(const KParams& P, const char* ro
             if (ws.pre[mid] <= fi) lo = mid;
             else hi = mid - 1;
           }
-          e0[q] = P.cidx[(slot0 + s0 + lo) * (size_t)P.cap + (fi - ws.pre[lo])];
+          ch[q] = lo;
+          ent[q] = P.cent[(slot0 + s0 + lo) * (size_t)P.cap + (fi - ws.pre[lo])];
         }
       }
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q)
-        if (f0 + q * kWave + lane < tot) v[q] = load_vec<DT, VEC>(row, e0[q], P.V);
-#pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const bool have = f0 + q * kWave + lane < tot;
-        if (__ballot(have)) f(have, v[q], e0[q]);
+        const bool pass = f0 + q * kWave + lane < tot && __int_as_float(ent[q].y) >= ws.thr[ch[q]];
+        const uint64_t bal = __ballot(pass);
+        if (pass) {
+          const int pos = nv + __popcll(bal & below);
+          if (pos < kVecList) {
+            ws.vi[pos] = ent[q].x;
+            if (keep_keys) ws.cx[pos] = __int_as_float(ent[q].y);  // kRowCache >= kVecList
+          }
+        }
+        nv += __popcll(bal);
       }
     }
+    wave_sync();
   }
-  wave_sync();
+  return nv;
+}
+
+// Loads candidate vectors ws.vi[j0 + q * 64 + lane] (< nv) into registers.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_candidates(const KParams& P, const char* row, int j0, int nv, int lane,
+                                                const WaveSmem& ws, uint4 (&v)[4], int (&e0)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = j0 + q * kWave + lane;
+    e0[q] = j < nv ? ws.vi[j] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = make_uint4(0, 0, 0, 0);
+    if (j0 + q * kWave + lane < nv) v[q] = load_vec<DT, VEC>(row, e0[q], P.V);
+  }
 }
 
 // Appends the logits >= c of one vector per lane to (dx, di) at *n, in
@@ -971,7 +1016,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
   mine.cnt = 0;
   mine.arg = 0x7fffffff;
   mine.flags = 0;
-  mine.pad = 0;
+  mine.o = 0.0f;
   if (small && lane < S) mine = crec[lane];
   auto recs = [&](auto&& f) {
     if (small) {
@@ -1005,8 +1050,11 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
 
   const float oM = M * c2;
   const double fM = exp2((double)oM - (double)M * (double)c2);
-  bool list_ok = false, cached = false;
-  int n = 0;
+  bool list_ok = false;
+  int src = 0;  // where the candidates >= the final cut lie: 1 registers, 2 LDS cache
+  int n = 0, nv = 0;
+  uint4 rv[4];  // candidate vectors held in registers (src 1)
+  int re[4];
   if (!(rr.flags & kErrBits)) {
     if (mode == SV_PLAIN) {
       rr.Zs = Z;
@@ -1031,44 +1079,78 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
       } else {
         target = (unsigned long long)sp.topk;
       }
-      // candidates >= C: cached in LDS when they fit, else selected
-      // straight from the lists; the full row when the lists are incomplete
-      // or the threshold falls below C
-      const float Cf = fmaxf(C, -kMaxFinite);
-      bool fast = C < kInf;
-      if (fast) {
-        for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int e0) {
-          append_ge<DT>(have, v, e0, Cf, lane, ws.cx, ws.ci, kRowCache, &n);
-        });
-      }
-      cached = fast && n <= kRowCache;
+      const char* rowc = static_cast<const char*>(row);
+      auto rec_at = [&](int s) { return small ? mine : crec[s]; };  // s = lane when small
+      // A nucleus first tries the cut 8 log2 units below the row maximum
+      // (its lists reach 10), then C.  The candidates >= the cut are held
+      // in registers (up to 256 vectors) or cached in LDS; the full row is
+      // re-read when they do not fit or the threshold falls below C.
       SelOut so;
-      if (cached) {
-        so = wave_select<DT>(
+      bool ok = false;
+      float C1 = by_mass ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
+      if (!by_mass && C < kInf) {
+        // top-k: the k-th largest logit is at least the k-th largest vector
+        // maximum (every vector holds its maximum), so that key bounds it
+        const int nk0 = min(filter_listed(P, slot0, rec_at, C, c2, false, lane, ws, true), kVecList);
+        const SelOut sk = wave_select<DT>(
             [&](auto&& f) {
-              for (int j = lane; j < n; j += kWave) {
-                const float x = ws.cx[j];
-                f(x, mass_of(x, c2, oM, fM));
-              }
+              for (int j = lane; j < nk0; j += kWave) f(ws.cx[j], 0ull);
             },
-            by_mass, target, ws, lane);
-      } else if (fast) {
-        so = wave_select<DT>(
-            [&](auto&& f) {
-              for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int) {
-#pragma unroll
-                for (int k = 0; k < Fmt<DT>::VE; ++k) {
-                  const float x = elem<DT>(v, k);
-                  if (have && x >= Cf) f(x, mass_of(x, c2, oM, fM));
-                }
-              });
-            },
-            by_mass, target, ws, lane);
+            false, target, ws, lane);
+        if (sk.reached) C1 = fmaxf(C, sk.T);
       }
-      fast = fast && so.reached && so.T >= C;
-      if (!fast) {
+      for (int pass = 0; pass < 2 && !ok && C < kInf; ++pass) {
+        const float Cu = pass == 0 ? C1 : C;
+        if (pass == 1 && !(C1 > C)) break;
+        const float Cuf = fmaxf(Cu, -kMaxFinite);  // -inf padding never passes
+        nv = filter_listed(P, slot0, rec_at, Cu, c2, by_mass, lane, ws);
+        src = 0;
+        if (nv <= 4 * kWave) {
+          load_candidates<DT, VEC>(P, rowc, 0, nv, lane, ws, rv, re);
+          so = wave_select<DT>(
+              [&](auto&& f) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const bool have = q * kWave + lane < nv;
+                  if (__ballot(have)) {
+#pragma unroll
+                    for (int k = 0; k < Fmt<DT>::VE; ++k) {
+                      const float x = elem<DT>(rv[q], k);
+                      if (have && x >= Cuf) f(x, mass_of(x, c2, oM, fM));
+                    }
+                  }
+                }
+              },
+              by_mass, target, ws, lane);
+          src = 1;
+        } else if (nv <= kVecList) {
+          n = 0;
+          for (int j0 = 0; j0 < nv; j0 += 4 * kWave) {
+            load_candidates<DT, VEC>(P, rowc, j0, nv, lane, ws, rv, re);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool have = j0 + q * kWave + lane < nv;
+              if (__ballot(have)) append_ge<DT>(have, rv[q], re[q], Cuf, lane, ws.cx, ws.ci, kRowCache, &n);
+            }
+          }
+          if (n <= kRowCache) {
+            wave_sync();
+            so = wave_select<DT>(
+                [&](auto&& f) {
+                  for (int j = lane; j < n; j += kWave) {
+                    const float x = ws.cx[j];
+                    f(x, mass_of(x, c2, oM, fM));
+                  }
+                },
+                by_mass, target, ws, lane);
+            src = 2;
+          }
+        }
+        ok = src != 0 && so.reached && so.T >= Cu;
+      }
+      if (!ok) {
         // full-row selection: re-read the row
-        cached = false;
+        src = 0;
         so = wave_select<DT>(
             [&](auto&& f) {
               for (int e = lane; e < P.V; e += kWave) {
@@ -1088,7 +1170,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
           rr.flags |= SV_ST_MARGIN;
       }
       if (!(rr.Zs > 0.0)) rr.flags |= SV_ST_EMPTY;
-      list_ok = fast && tgt && so.n_keep <= (uint32_t)kListMax;
+      list_ok = ok && tgt && so.n_keep <= (uint32_t)kListMax;
     }
   }
 
@@ -1102,16 +1184,19 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
   }
 
   if (list_ok && !(rr.flags & kErrBits)) {
-    // the kept set, already in vocabulary order: the cache (or the lists)
-    // filtered by x >= T
+    // the kept set, in vocabulary order: the candidates >= T, compacted in
+    // list order
     rr.flags |= kRfListOk;
     int nk = 0;
-    if (!cached) {
-      for_each_listed<DT, VEC>(P, static_cast<const char*>(row), slot0, lane, ws, small ? mine.cnt : -1, [&](bool have, const uint4& v, int e0) {
-        append_ge<DT>(have, v, e0, rr.T, lane, ws.cx, ws.ci, kListMax, &nk);
-      });
+    const uint64_t below = (1ull << lane) - 1ull;
+    wave_sync();
+    if (src == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool have = q * kWave + lane < nv;
+        if (__ballot(have)) append_ge<DT>(have, rv[q], re[q], rr.T, lane, ws.cx, ws.ci, kListMax, &nk);
+      }
     } else {
-      const uint64_t below = (1ull << lane) - 1ull;
       for (int j0 = 0; j0 < n; j0 += kWave) {
         const int j = j0 + lane;
         const float x = j < n ? ws.cx[j] : -kInf;
@@ -1128,13 +1213,13 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
         wave_sync();
       }
     }
+    wave_sync();
     if (P.R <= kSeqWaves) {
       // the set stays in this wave's LDS for the draw, with the draft's
       // logits at its tokens (for a resample at this position)
-      wave_sync();
       if (t < sp.Kb) {
         const void* drow = row_ptr<DT>(P, b, false, t);
-        for (int j = lane; j < nk; j += kWave) ws.cx[kListMax + j] = load_logit<DT>(drow, ws.ci[j]);
+        for (int j = lane; j < nk; j += kWave) ws.vi[j] = __float_as_int(load_logit<DT>(drow, ws.ci[j]));
       }
     } else {
       KeptEntry* kl = P.kept + rowid * kListMax;
@@ -1230,7 +1315,7 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
       if (i < N) {
         iv[j] = ls->ci[i];
         qv[j] = (double)mass_of(ls->cx[i], c2q, oM, fM) / kFix / rq.Zs;
-        if (resample) xp[j] = ls->cx[kListMax + i];
+        if (resample) xp[j] = __int_as_float(ls->vi[i]);
       }
     }
   } else {
