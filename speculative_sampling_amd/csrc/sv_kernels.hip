@@ -748,6 +748,7 @@ struct SmemSeq {
   double rd[kSeqWaves];
   int ri[kSeqWaves];
   uint32_t misc[4];
+  double rx[2];
 };
 
 struct SelOut {
@@ -1406,111 +1407,287 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
   return d;
 }
 
-// Weight of one token for the full-row draw: q, or (q - p)+.
-__device__ __forceinline__ double row_weight(const RowRec& rq, bool use_p, const RowRec& rp, float xq, float xp) {
-  double q = 0.0;
-  if (xq >= rq.T) q = (double)__builtin_amdgcn_exp2f((xq - rq.M) * (float)rq.c2) / rq.Zs;
-  if (!use_p) return q;
-  double p = 0.0;
-  if (xp >= rp.T) p = (double)__builtin_amdgcn_exp2f((xp - rp.M) * (float)rp.c2) / rp.Zs;
-  return q > p ? q - p : 0.0;
+// Probability of a logit under one row's filtered distribution, with the
+// terms computed as for the kept masses (mass_of): 2^(x c2 - oM) fM / Zs.
+// fp32 weights (relative error ~1e-7, far inside the 1e-6 decision window),
+// summed in fp64.
+struct RowW {
+  float c2, oM, T, sc;  // sc = fM / Zs
+};
+__device__ __forceinline__ RowW row_w(const RowRec& r) {
+  RowW w;
+  w.c2 = (float)r.c2;
+  w.oM = r.M * w.c2;
+  w.sc = (float)(exp2((double)w.oM - (double)r.M * (double)w.c2) / r.Zs);
+  w.T = r.T;
+  return w;
+}
+__device__ __forceinline__ float prob(const RowW& w, float x) {
+  return x >= w.T ? __builtin_amdgcn_exp2f(fmaf(x, w.c2, -w.oM)) * w.sc : 0.0f;
 }
 
-// Inverse CDF over full logit rows re-read from memory by the whole
-// work-group, in tiles of kSeqThreads x 8 tokens (thread i owns tokens
-// 8i..8i+7 of a tile).
+// Raw logits of the 8 tokens e..e+7 of one row, in 1 (bf16) or 2 (fp32)
+// 16-byte vectors (-inf past V).
+template <int DT, bool VEC>
+__device__ __forceinline__ void load8(const KParams& P, const char* row, int e, uint4 (&r)[2]) {
+  constexpr int VE = Fmt<DT>::VE;
+  const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    r[h] = make_uint4(ninf, ninf, ninf, ninf);
+    if (h * VE < 8 && e + h * VE < P.V) r[h] = load_vec<DT, VEC>(row, e + h * VE, P.V);  // whole vectors when VEC
+  }
+}
+
+// Weights of the 8 tokens e..e+7 (those >= hi weigh 0): q, or (q - p)+.
 template <int DT>
+__device__ __forceinline__ void weights8(const RowW& wq, bool use_p, const RowW& wp, const uint4 (&rq)[2],
+                                         const uint4 (&rp)[2], int e, int hi, double (&w)[8]) {
+  constexpr int VE = Fmt<DT>::VE;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float xq = elem<DT>(rq[k / VE], k % VE), xp = elem<DT>(rp[k / VE], k % VE);
+    float q = e + k < hi ? prob(wq, xq) : 0.0f;
+    if (use_p) {
+      const float pp = e + k < hi ? prob(wp, xp) : 0.0f;
+      q = q > pp ? q - pp : 0.0f;
+    }
+    w[k] = (double)q;
+  }
+}
+
+// Inverse CDF over logit rows re-read from memory by the whole work-group.
+// The range [lo, hi) (the whole row, or for a plain bonus draw the chunk
+// that the chunk records place the target in) is split into one segment
+// per wave; pass 1 sums the weights of each 512-token tile into LDS, pass 2
+// scans the one tile that holds the target.
+template <int DT, bool VEC>
 __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
-                                               const void* qrow, const void* prow, double u, SmemSeq& sm) {
+                                               const char* qrow, const char* prow, double u, SmemSeq& sm, int lane,
+                                               int wv, const ChunkRec* qrec) {
+  constexpr int kTileCap = (int)(kRowCache * sizeof(float) / sizeof(double));
   const int tid = threadIdx.x;
-  const int V = P.V;
-  constexpr int TILE = kSeqThreads * 8;
   Draw d;
   d.flags = SV_ST_REREAD;
   d.y = 0;
+  const RowW wq = row_w(rq), wp = row_w(rp);
   bool use_p = resample;
-  for (int pass = 0; pass < 2; ++pass) {
-    // total mass and the first / last token of non-zero weight
-    double st = 0.0;
-    int nz_lo = 0x7fffffff, nz_hi = -1;
-    for (int base = 0; base < V; base += TILE) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = base + 8 * tid + k;
-        if (e < V) {
-          const double w = row_weight(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f);
-          st += w;
-          if (w > 0.0) {
-            nz_lo = min(nz_lo, e);
-            nz_hi = max(nz_hi, e);
-          }
-        }
+  int lo = 0, hi = P.V;
+  double base = 0.0;  // weight before lo (chunk-located draws)
+  bool located = false, force_last = false;
+  if (!resample && qrec && rq.T == -kInf) {
+    // plain bonus draw: the chunk sums give the chunk holding u
+    const int S = P.S;
+    double wc[2];
+    int cnt = 0;
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * tid + j;
+      wc[j] = 0.0;
+      if (c < S) {
+        const ChunkRec r = qrec[c];
+        if (r.m > -kInf) wc[j] = r.z * exp2(((double)r.m - (double)rq.M) * (double)wq.c2) / rq.Zs;
       }
     }
-    const double S = seq_sum(st, sm);
-    nz_lo = seq_min_i(nz_lo, sm);
-    nz_hi = seq_max_i(nz_hi, sm);
-    if (!(S > 0.0) && pass == 0 && use_p) {
-      d.flags |= SV_ST_ZERO_RESIDUAL;
+    (void)cnt;
+    double tot;
+    const double ex = seq_exclusive_scan(wc[0] + wc[1], &tot, sm);
+    int cstar = 0x7fffffff, clast = -1;
+    double cb = 0.0;
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * tid + j;
+      const double before = ex + (j ? wc[0] : 0.0);
+      if (c < S && wc[j] > 0.0) {
+        if (before + wc[j] > u && cstar == 0x7fffffff) {
+          cstar = c;
+          cb = before;
+        }
+        clast = c;
+      }
+    }
+    const int cs = seq_min_i(cstar, sm);
+    const int cl = seq_max_i(clast, sm);
+    if (cs != 0x7fffffff || cl >= 0) {
+      const int c = cs != 0x7fffffff ? cs : cl;
+      __syncthreads();
+      if (cs != 0x7fffffff ? (cstar == cs) : false) sm.rd[0] = cb;
+      __syncthreads();
+      base = cs != 0x7fffffff ? sm.rd[0] : 0.0;
+      __syncthreads();
+      lo = c * P.L;
+      hi = min(P.V, lo + P.L);
+      located = true;
+      force_last = cs == 0x7fffffff;  // u beyond the rounded total: the last token of the last chunk
+    }
+  }
+  double* tsum = reinterpret_cast<double*>(sm.w[wv].cx);  // this wave's tile sums
+  double S = 0.0;
+  int nzlo = 0x7fffffff, nzhi = -1, per = 0, v0 = 0, v1 = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int n8 = (hi - lo + 7) / 8;
+    per = (n8 + kSeqWaves - 1) / kSeqWaves;
+    v0 = min(n8, wv * per);
+    v1 = min(n8, v0 + per);
+    double seg = 0.0;
+    int zl = 0x7fffffff, zh = -1, nt = 0;
+    for (int t0 = v0; t0 < v1; t0 += 4 * kWave) {
+      // the loads of 4 tiles are in flight together
+      uint4 rq[4][2], rp[4][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int vi = t0 + g * kWave + lane;
+        const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+        rq[g][0] = rq[g][1] = rp[g][0] = rp[g][1] = make_uint4(ninf, ninf, ninf, ninf);
+        if (vi < v1) {
+          load8<DT, VEC>(P, qrow, lo + 8 * vi, rq[g]);
+          if (use_p) load8<DT, VEC>(P, prow, lo + 8 * vi, rp[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (t0 + g * kWave >= v1) break;
+        const int vi = t0 + g * kWave + lane;
+        double sl = 0.0;
+        if (vi < v1) {
+          double w[8];
+          weights8<DT>(wq, use_p, wp, rq[g], rp[g], lo + 8 * vi, hi, w);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            sl += w[k];
+            if (w[k] > 0.0) {
+              zl = min(zl, lo + 8 * vi + k);
+              zh = max(zh, lo + 8 * vi + k);
+            }
+          }
+        }
+        sl = wave_sum(sl);
+        if (lane == 0 && nt < kTileCap) tsum[nt] = sl;
+        seg += sl;
+        ++nt;
+      }
+    }
+    zl = wave_min_i(zl);
+    zh = wave_max_i(zh);
+    __syncthreads();
+    if (lane == 0) {
+      sm.rd[wv] = seg;
+      sm.ri[wv] = zl;
+    }
+    __syncthreads();
+    S = 0.0;
+    nzlo = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < kSeqWaves; ++w) {
+      S += sm.rd[w];
+      nzlo = min(nzlo, sm.ri[w]);
+    }
+    __syncthreads();
+    if (lane == 0) sm.ri[wv] = zh;
+    __syncthreads();
+    nzhi = -1;
+#pragma unroll
+    for (int w = 0; w < kSeqWaves; ++w) nzhi = max(nzhi, sm.ri[w]);
+    if (!(S > 0.0) && use_p) {
+      d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
       use_p = false;
+      __syncthreads();
       continue;
     }
-    const double target = u * S;
-    double run = 0.0;
-    int y = -1;
-    double lo = 0.0, hi = 0.0;
-    for (int base = 0; base < V && y < 0; base += TILE) {
-      double wk[8];
-      double s = 0.0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = base + 8 * tid + k;
-        wk[k] = e < V ? row_weight(rq, use_p, rp, load_logit<DT>(qrow, e), use_p ? load_logit<DT>(prow, e) : 0.f)
-                      : 0.0;
-        s += wk[k];
-      }
-      double tile;
-      const double ex = seq_exclusive_scan(s, &tile, sm);
-      if (run + tile > target) {
-        // the thread whose span crosses the target finds the token
-        int cand = 0x7fffffff;
-        double c = run + ex, cl = 0.0, ch = 0.0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const double cn = c + wk[k];
-          if (cn > target && wk[k] > 0.0 && cand == 0x7fffffff) {
-            cand = base + 8 * tid + k;
-            cl = c;
-            ch = cn;
-          }
-          c = cn;
-        }
-        const int ymin = seq_min_i(cand, sm);
-        if (ymin != 0x7fffffff) {
-          __syncthreads();
-          if (cand == ymin) {
-            sm.rd[0] = cl;
-            sm.rd[1] = ch;
-          }
-          __syncthreads();
-          lo = sm.rd[0];
-          hi = sm.rd[1];
-          __syncthreads();
-          y = ymin;
-        }
-      }
-      run += tile;
-    }
-    if (y < 0) {  // rounding left no token above the target
-      y = nz_hi < 0 ? 0 : nz_hi;
-      lo = S;
-      hi = S;
-    }
-    d.y = y;
-    if (nz_lo < y && u - lo / S < kWindow) d.flags |= SV_ST_MARGIN;
-    if (nz_hi > y && hi / S - u < kWindow) d.flags |= SV_ST_MARGIN;
     break;
   }
+  // the target: u * S over the whole row, or u - base within the located chunk
+  const double target = located ? (force_last ? kInf : u - base) : u * S;
+  // the wave segment, then the tile, holding the target
+  int ws_ = -1;
+  double before = 0.0;
+  {
+    double c = 0.0;
+    for (int w = 0; w < kSeqWaves; ++w) {
+      const double sw = sm.rd[w];
+      if (ws_ < 0 && sw > 0.0 && c + sw > target) {
+        ws_ = w;
+        before = c;
+      }
+      c += sw;
+    }
+  }
+  int y = -1;
+  double clo = 0.0, chi = 0.0;
+  if (ws_ >= 0 && wv == ws_) {
+    const int n8 = (hi - lo + 7) / 8;
+    const int a0 = min(n8, ws_ * per), a1 = min(n8, a0 + per);
+    int t = 0;
+    double c = before;
+    const int ntile = (a1 - a0 + kWave - 1) / kWave;
+    if (ntile <= kTileCap) {
+      while (t < ntile - 1 && !(tsum[t] > 0.0 && c + tsum[t] > target)) c += tsum[t++];
+    }
+    // scan tiles from t (usually just one) until the target is crossed
+    for (; t < ntile && y < 0; ++t) {
+      const int vi = a0 + t * kWave + lane;
+      double w[8];
+      double sl = 0.0;
+      if (vi < a1) {
+        uint4 aq[2], ap[2];
+        const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+        ap[0] = ap[1] = make_uint4(ninf, ninf, ninf, ninf);
+        load8<DT, VEC>(P, qrow, lo + 8 * vi, aq);
+        if (use_p) load8<DT, VEC>(P, prow, lo + 8 * vi, ap);
+        weights8<DT>(wq, use_p, wp, aq, ap, lo + 8 * vi, hi, w);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl += w[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = 0.0;
+      }
+      const double inc = wave_incl_scan(sl, lane);
+      const double tile = __shfl(inc, kWave - 1);
+      if (c + tile > target) {
+        int cand = 0x7fffffff;
+        double r = c + inc - sl, cl = 0.0, ch = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const double rn = r + w[k];
+          if (rn > target && w[k] > 0.0 && cand == 0x7fffffff) {
+            cand = lo + 8 * vi + k;
+            cl = r;
+            ch = rn;
+          }
+          r = rn;
+        }
+        const int ym = wave_min_i(cand);
+        if (ym != 0x7fffffff) {
+          const uint64_t who = __ballot(cand == ym);
+          const int src = __ffsll((long long)who) - 1;
+          y = ym;
+          clo = __shfl(cl, src);
+          chi = __shfl(ch, src);
+        }
+      }
+      c += tile;
+    }
+    if (lane == 0) {
+      sm.misc[2] = (uint32_t)y;
+      sm.rx[0] = clo;
+      sm.rx[1] = chi;
+    }
+  }
+  __syncthreads();
+  if (ws_ >= 0) {
+    y = (int)sm.misc[2];
+    clo = sm.rx[0];
+    chi = sm.rx[1];
+  }
+  __syncthreads();
+  if (y < 0) {  // rounding left no token above the target
+    y = nzhi < 0 ? 0 : nzhi;
+    clo = chi = S;
+  }
+  d.y = y;
+  // the CDF just below and at y, in probability units
+  const double plo = located ? base + clo : clo / S, phi = located ? base + chi : chi / S;
+  if (nzlo < y && u - plo < kWindow) d.flags |= SV_ST_MARGIN;
+  if (nzhi > y && phi - u < kWindow) d.flags |= SV_ST_MARGIN;
+  (void)tid;
   return d;
 }
 
@@ -1626,8 +1803,9 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
     d.y = (int)sm.misc[2];
     d.flags = sm.misc[3];
   } else {
-    d = draw_from_rows<DT>(P, rq, resample, rp, row_ptr<DT>(P, b, true, n),
-                           resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, sm);
+    d = draw_from_rows<DT, VEC>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
+                                resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr, u, sm,
+                                lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
   }
   st |= d.flags;
   for (int i = tid; i <= KM; i += kSeqThreads) {
