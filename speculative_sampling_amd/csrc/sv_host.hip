@@ -71,8 +71,10 @@ Geometry geometry(const sv_config* cfg) {
   // whole chunks of chunk_cap logits, the row's remainder in the last one
   g.S = (V + chunk_cap - 1) / chunk_cap;
   g.L = chunk_cap;
-  (void)ve;
-  g.cap = std::max(32, std::min(sv::kCandVecs, 4096 / g.S));
+  // candidate vectors per chunk: fewer per chunk when a row has many, and
+  // never more than a chunk holds
+  const int chunk_vecs = (std::min(g.L, V) + ve - 1) / ve;
+  g.cap = std::min(std::max(32, std::min(sv::kCandVecs, 4096 / g.S)), chunk_vecs);
   g.R_max = 2 * cfg->max_k + 1;
   const size_t rows = (size_t)cfg->max_batch * g.R_max;
   size_t off = 0;
@@ -80,8 +82,10 @@ Geometry geometry(const sv_config* cfg) {
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
   g.off_cent = off;
   off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int2), 256);
+  // kept lists go through global memory only for sequences of more rows
+  // than the sequence kernel has waves
   g.off_kept = off;
-  off = align_up(off + rows * sv::kListMax * sizeof(sv::KeptEntry), 256);
+  if (g.R_max > sv::kSeqWaves) off = align_up(off + rows * std::min(sv::kListMax, V) * sizeof(sv::KeptEntry), 256);
   g.total = off;
   return g;
 }

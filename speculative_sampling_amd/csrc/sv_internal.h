@@ -22,6 +22,9 @@ constexpr int kCandVecs = 256;
 // Largest kept set the final draw takes from the merged kept list without
 // re-reading the logit rows.
 constexpr int kListMax = 512;
+// Waves of the per-sequence kernel (one logit row each); sequences of more
+// rows keep their kept lists in global memory.
+constexpr int kSeqWaves = 12;
 // Largest number of chunks per row (V <= 2^22 with 4096 fp32 per chunk).
 constexpr int kMaxChunks = 1024;
 constexpr int kMaxK = 64;

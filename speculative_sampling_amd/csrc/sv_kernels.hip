@@ -693,7 +693,6 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
 // work-group runs the accept walk, finds the first rejection and draws the
 // resampled or bonus token.
 
-constexpr int kSeqWaves = 12;
 constexpr int kSeqThreads = kSeqWaves * kWave;
 constexpr int kRowCache = 768;  // candidate logits of one row held in LDS
 constexpr int kVecList = 768;   // candidate vectors of one row that pass the row's cut
@@ -1223,7 +1222,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
         for (int j = lane; j < nk; j += kWave) ws.vi[j] = __float_as_int(load_logit<DT>(drow, ws.ci[j]));
       }
     } else {
-      KeptEntry* kl = P.kept + rowid * kListMax;
+      KeptEntry* kl = P.kept + rowid * (size_t)min(kListMax, P.V);  // n_keep <= min(kListMax, V)
       for (int j = lane; j < nk; j += kWave) {
         KeptEntry ke;
         ke.idx = ws.ci[j];
@@ -1320,7 +1319,7 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
       }
     }
   } else {
-    const KeptEntry* kl = P.kept + rowq * kListMax;
+    const KeptEntry* kl = P.kept + rowq * (size_t)min(kListMax, P.V);
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int i = E * lane + j;

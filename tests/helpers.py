@@ -104,3 +104,18 @@ def compare(gpu: dict, ref: dict, dtype: str, label: str = "", rate_bound: bool 
 
 def with_oracle_drafts(w: workloads.Workload) -> workloads.Workload:
     return workloads.draw_draft_tokens(w, oracle_sampler)
+
+
+def gpu_sampler(rows, mode, temperature, top_k, top_p, dmode, dtemp, dtopk, dtopp, seed):
+    """The library's K = 0 step as a draft sampler (rows on the GPU)."""
+    dev = rows.device
+
+    def d(x):
+        return None if x is None else x.to(dev)
+    v = Verifier(rows.shape[0], 0, rows.shape[-1], rows.dtype, dev.index or 0)
+    toks, _ = v.sample(rows, seed=seed, mode=d(mode), temperature=d(temperature), top_k=d(top_k),
+                       top_p=d(top_p), default_mode=dmode, default_temperature=dtemp,
+                       default_top_k=dtopk, default_top_p=dtopp)
+    torch.cuda.synchronize()
+    v.close()
+    return toks.reshape(-1).to(torch.int32)

@@ -1,0 +1,123 @@
+"""GPU statistics on the pages' worked example: 10^6 sequences of K = 4 draft
+tokens over a four-word vocabulary, target q = [0.5, 0.25, 0.15, 0.10] and
+draft p = [0.3, 0.4, 0.2, 0.1] at every position (roadtointelligence.com
+"Speculative Decoding", section "Why the output doesn't change"; the
+letters are swapped there).
+
+What the pages fix, checked on the library's own outputs:
+  * acceptance sum_v min(p, q) = 0.8 per position;
+  * the accepted count follows a^k (1 - a), and E[tokens per pass] =
+    (1 - a^(K+1)) / (1 - a) = 3.3616 (same page, "How much faster");
+  * every emitted token is distributed as the target (the paperlayer.ai
+    summary's Theorem 1);
+  * a rejection resamples from normalize((q - p)+) = [1, 0, 0, 0].
+
+The draft tokens come from the library's own K = 0 step (a draw from the
+filtered draft). The first 20,000 sequences are also compared with the oracle
+element by element.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+from helpers import compare, run_gpu, run_oracle
+from speculative_sampling_amd import workloads
+from speculative_sampling_amd.binding import ST_ERRORS, Verifier
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+Q = np.array([0.5, 0.25, 0.15, 0.10])
+P = np.array([0.3, 0.4, 0.2, 0.1])
+A = 0.8
+
+
+@pytest.fixture(scope="module")
+def run():
+    dev = torch.device("cuda", 0)
+    B, K = 1_000_000, 4
+    w = workloads.worked_example(B, K, device=dev, seed=1, draft_seed=1001)
+    print(f"[worked_example_gpu] B={B} K={K}: drawing drafts", flush=True)
+    sampler = Verifier(B * K, 0, 4, torch.float32)
+    toks, st = sampler.sample(w.draft.reshape(-1, 4), seed=w.draft_seed)
+    torch.cuda.synchronize()
+    sampler.close()
+    assert int(((st & ST_ERRORS) != 0).sum()) == 0
+    w.draft_tokens = toks.reshape(B, K).to(torch.int32).contiguous()
+    print("[worked_example_gpu] verifying", flush=True)
+    out = run_gpu(w)
+    return w, out
+
+
+def test_draft_tokens_follow_p(run):
+    w, _ = run
+    toks = w.draft_tokens.cpu().numpy().ravel()
+    counts = np.bincount(toks, minlength=4)
+    _, pval = stats.chisquare(counts, P * toks.size)
+    assert pval > 1e-3
+
+
+def test_per_position_acceptance(run):
+    _, out = run
+    n = out["accepted"]
+    for t in range(4):
+        reached = np.count_nonzero(n >= t)
+        acc = np.count_nonzero(n > t) / reached
+        assert abs(acc - A) < 4 * np.sqrt(A * (1 - A) / reached), (t, acc)
+
+
+def test_accepted_count_law(run):
+    _, out = run
+    n = out["accepted"]
+    law = np.array([A ** k * (1 - A) for k in range(4)] + [A ** 4])
+    _, pval = stats.chisquare(np.bincount(n, minlength=5), law * n.size)
+    assert pval > 1e-3
+
+
+def test_expected_tokens_per_pass(run):
+    _, out = run
+    emitted = out["accepted"] + 1
+    e_tokens = (1 - A ** 5) / (1 - A)
+    assert round(e_tokens, 4) == 3.3616
+    assert abs(emitted.mean() - e_tokens) < 4 * emitted.std() / np.sqrt(emitted.size)
+
+
+def test_emitted_tokens_follow_target(run):
+    _, out = run
+    toks = out["out_tokens"]
+    for i in range(5):
+        col = toks[:, i]
+        col = col[col >= 0]
+        _, pval = stats.chisquare(np.bincount(col, minlength=4), Q * col.size)
+        assert pval > 1e-3, i
+
+
+def test_every_rejection_emits_token_0(run):
+    _, out = run
+    n = out["accepted"]
+    y = out["out_tokens"][np.arange(n.size), n]
+    assert np.all(y[n < 4] == 0)
+
+
+def test_emission_invariants(run):
+    w, out = run
+    n = out["accepted"]
+    toks = out["out_tokens"]
+    drafts = w.draft_tokens.cpu().numpy()
+    idx = np.arange(5)[None, :]
+    assert n.min() >= 0 and n.max() <= 4
+    assert np.all(toks[idx > n[:, None]] == -1) and np.all(toks[idx <= n[:, None]] >= 0)
+    prefix = idx[:, :4] < n[:, None]
+    assert np.all(toks[:, :4][prefix] == drafts[prefix])
+    assert np.all(out["row_status"] & ST_ERRORS == 0)
+
+
+def test_first_sequences_match_oracle(run):
+    w, out = run
+    m = 20_000
+    sub = workloads.Workload(w.name, m, w.K_max, w.V, w.dtype, w.target[:m], w.draft[:m], w.draft_tokens[:m],
+                             default_mode=w.default_mode, default_temperature=w.default_temperature,
+                             seed=w.seed)
+    ref = run_oracle(sub)
+    compare({k: v[:m] for k, v in out.items()}, ref, "f32", "worked_example_gpu_first")
