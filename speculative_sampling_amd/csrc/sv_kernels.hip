@@ -871,7 +871,7 @@ __device__ __forceinline__ unsigned long long mass_of(float x, float c2, float o
 template <class RecAt>
 __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, RecAt&& rec_at, float Cu, float c2,
                                              bool terms, int lane, WaveSmem& ws, bool keep_keys = false) {
-  constexpr int kBatch = 4;
+  constexpr int kBatch = 8;
   const int S = P.S;
   const uint64_t below = (1ull << lane) - 1ull;
   int nv = 0;
@@ -1289,123 +1289,6 @@ __device__ __forceinline__ double seq_exclusive_scan(double v, double* total, Sm
   return base + inc - v;
 }
 
-// Inverse CDF over the target's kept set in vocabulary order (one wave):
-// w = (q - p)+ when resampling, else w = q.  Lane l owns entries 8l..8l+7.
-// The set is read from the LDS of the wave that merged the row (ls), or
-// from global memory.
-template <int DT>
-__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
-                                               size_t rowq, const void* drow, double u, int lane,
-                                               const WaveSmem* ls) {
-  constexpr int E = kListMax / kWave;
-  const int N = rq.n_keep;  // <= kListMax
-  double qv[E];
-  int iv[E];
-  float xp[E];
-  if (ls) {
-    const float c2q = (float)rq.c2;
-    const float oM = rq.M * c2q;
-    const double fM = exp2((double)oM - (double)rq.M * (double)c2q);
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = E * lane + j;
-      qv[j] = 0.0;
-      iv[j] = 0;
-      xp[j] = -kInf;
-      if (i < N) {
-        iv[j] = ls->ci[i];
-        qv[j] = (double)mass_of(ls->cx[i], c2q, oM, fM) / kFix / rq.Zs;
-        if (resample) xp[j] = __int_as_float(ls->vi[i]);
-      }
-    }
-  } else {
-    const KeptEntry* kl = P.kept + rowq * (size_t)min(kListMax, P.V);
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = E * lane + j;
-      qv[j] = 0.0;
-      iv[j] = 0;
-      if (i < N) {
-        const KeptEntry ke = kl[i];
-        qv[j] = ke.q;
-        iv[j] = ke.idx;
-      }
-    }
-    if (resample) {
-#pragma unroll
-      for (int j = 0; j < E; ++j) xp[j] = E * lane + j < N ? load_logit<DT>(drow, iv[j]) : -kInf;
-    }
-  }
-  Draw d;
-  d.flags = 0;
-  double w[E];
-  bool use_p = resample;
-  double total = 0.0, ex = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    double s = 0.0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      w[j] = qv[j];
-      if (use_p && E * lane + j < N) {
-        const double p = xp[j] >= rp.T ? exp2(((double)xp[j] - (double)rp.M) * rp.c2) / rp.Zs : 0.0;
-        w[j] = qv[j] > p ? qv[j] - p : 0.0;
-      }
-      s += w[j];
-    }
-    const double inc = wave_incl_scan(s, lane);
-    total = __shfl(inc, kWave - 1);
-    ex = inc - s;
-    if (total > 0.0 || !use_p) break;
-    d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
-    use_p = false;
-  }
-  const double target = u * total;
-  // first entry whose running sum exceeds the target; the last non-zero one
-  int first = 0x7fffffff, lastnz = -1, firstnz = 0x7fffffff;
-  double c = ex, clo = 0.0, chi = 0.0;
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int i = E * lane + j;
-    const double cn = c + w[j];
-    if (i < N && w[j] > 0.0) {
-      if (cn > target && first == 0x7fffffff) {
-        first = i;
-        clo = c;
-        chi = cn;
-      }
-      lastnz = max(lastnz, i);
-      firstnz = min(firstnz, i);
-    }
-    c = cn;
-  }
-  const int f = wave_min_i(first);
-  const int lnz = wave_max_i(lastnz);
-  const int fnz = wave_min_i(firstnz);
-  int iy;
-  double lo, hi;
-  if (f <= lnz) {
-    iy = f;
-    const int src = f / E;
-    lo = __shfl(clo, src);
-    hi = __shfl(chi, src);
-  } else {  // rounding left no entry above the target
-    iy = lnz < 0 ? 0 : lnz;
-    lo = total;
-    hi = total;
-  }
-  const int src = iy / E;
-  int yv = 0;
-#pragma unroll
-  for (int j = 0; j < E; ++j)
-    if (E * lane + j == iy) yv = iv[j];
-  d.y = N > 0 ? __shfl(yv, src) : 0;
-  if (N > 0 && lnz >= 0 && total > 0.0) {
-    // margins of interior CDF boundaries
-    if ((fnz < iy && u - lo / total < kWindow) || (lnz > iy && hi / total - u < kWindow)) d.flags |= SV_ST_MARGIN;
-  }
-  return d;
-}
-
 // Probability of a logit under one row's filtered distribution, with the
 // terms computed as for the kept masses (mass_of): 2^(x c2 - oM) fM / Zs.
 // fp32 weights (relative error ~1e-7, far inside the 1e-6 decision window),
@@ -1423,6 +1306,125 @@ __device__ __forceinline__ RowW row_w(const RowRec& r) {
 }
 __device__ __forceinline__ float prob(const RowW& w, float x) {
   return x >= w.T ? __builtin_amdgcn_exp2f(fmaf(x, w.c2, -w.oM)) * w.sc : 0.0f;
+}
+
+// Inverse CDF over the target's kept set in vocabulary order (one wave):
+// w = (q - p)+ when resampling, else w = q.  Entry i sits in slot i / 64 of
+// lane i % 64, so a set of up to 64 tokens costs one wave step per stage.
+// The set is read from the LDS of the wave that merged the row (ls), or
+// from global memory.  The draft's weights are fp32 terms as in prob().
+template <int DT>
+__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
+                                               size_t rowq, const void* drow, double u, int lane,
+                                               const WaveSmem* ls) {
+  constexpr int E = kListMax / kWave;
+  const int N = rq.n_keep;  // <= kListMax
+  const int ns = (N + kWave - 1) / kWave;
+  const RowW wp = row_w(rp);
+  double qv[E];
+  float pv[E];
+  int iv[E];
+  if (ls) {
+    const float c2q = (float)rq.c2;
+    const float oM = rq.M * c2q;
+    const double fM = exp2((double)oM - (double)rq.M * (double)c2q);
+    const double inv = 1.0 / (rq.Zs * kFix);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = j * kWave + lane;
+      qv[j] = 0.0;
+      pv[j] = 0.0f;
+      iv[j] = 0;
+      if (j < ns && i < N) {
+        iv[j] = ls->ci[i];
+        qv[j] = (double)mass_of(ls->cx[i], c2q, oM, fM) * inv;
+        if (resample) pv[j] = prob(wp, __int_as_float(ls->vi[i]));
+      }
+    }
+  } else {
+    const KeptEntry* kl = P.kept + rowq * (size_t)min(kListMax, P.V);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = j * kWave + lane;
+      qv[j] = 0.0;
+      pv[j] = 0.0f;
+      iv[j] = 0;
+      if (j < ns && i < N) {
+        const KeptEntry ke = kl[i];
+        qv[j] = ke.q;
+        iv[j] = ke.idx;
+      }
+    }
+    if (resample) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (j < ns && j * kWave + lane < N) pv[j] = prob(wp, load_logit<DT>(drow, iv[j]));
+    }
+  }
+  Draw d;
+  d.flags = 0;
+  double w[E], ex[E];
+  bool use_p = resample;
+  double total = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    total = 0.0;  // running sum in vocabulary order: slot by slot, lanes in order
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      w[j] = 0.0;
+      ex[j] = total;
+      if (j < ns) {
+        w[j] = use_p ? fmax(qv[j] - (double)pv[j], 0.0) : qv[j];
+        const double inc = wave_incl_scan(w[j], lane);
+        ex[j] = total + (inc - w[j]);
+        total += __shfl(inc, kWave - 1);
+      }
+    }
+    if (total > 0.0 || !use_p) break;
+    d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
+    use_p = false;
+  }
+  const double target = u * total;
+  // first entry whose running sum exceeds the target; the last non-zero one
+  int first = 0x7fffffff, lastnz = -1, firstnz = 0x7fffffff;
+  double clo = 0.0, chi = 0.0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int i = j * kWave + lane;
+    const double cn = ex[j] + w[j];
+    if (j < ns && i < N && w[j] > 0.0) {
+      if (cn > target && first == 0x7fffffff) {
+        first = i;
+        clo = ex[j];
+        chi = cn;
+      }
+      lastnz = max(lastnz, i);
+      firstnz = min(firstnz, i);
+    }
+  }
+  const int f = wave_min_i(first);
+  const int lnz = wave_max_i(lastnz);
+  const int fnz = wave_min_i(firstnz);
+  int iy;
+  double lo, hi;
+  if (f <= lnz) {
+    iy = f;
+    lo = __shfl(clo, f % kWave);
+    hi = __shfl(chi, f % kWave);
+  } else {  // rounding left no entry above the target
+    iy = lnz < 0 ? 0 : lnz;
+    lo = total;
+    hi = total;
+  }
+  int yv = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (j * kWave + lane == iy) yv = iv[j];
+  d.y = N > 0 ? __shfl(yv, iy % kWave) : 0;
+  if (N > 0 && lnz >= 0 && total > 0.0) {
+    // margins of interior CDF boundaries
+    if ((fnz < iy && u - lo / total < kWindow) || (lnz > iy && hi / total - u < kWindow)) d.flags |= SV_ST_MARGIN;
+  }
+  return d;
 }
 
 // Raw logits of the 8 tokens e..e+7 of one row, in 1 (bf16) or 2 (fp32)
