@@ -32,6 +32,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -705,29 +707,42 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const unsigned long long y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+// Inclusive wave scans by DPP lane moves: shifts of 1, 2, 4 and 8 lanes
+// within each row of 16, then the last lane of row 0 / rows 0-1 broadcast
+// into the rows above.  Lanes with no source take the identity.  Called
+// with the whole wave active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v, 0u), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32), 0u);
+  return ((unsigned long long)hi << 32) | lo;
+}
+template <class T, class Shift>
+__device__ __forceinline__ T dpp_scan(T v, Shift&& sh) {
+  v += sh(v, std::integral_constant<int, 0x111>(), std::integral_constant<int, 0xf>());  // row_shr:1
+  v += sh(v, std::integral_constant<int, 0x112>(), std::integral_constant<int, 0xf>());  // row_shr:2
+  v += sh(v, std::integral_constant<int, 0x114>(), std::integral_constant<int, 0xf>());  // row_shr:4
+  v += sh(v, std::integral_constant<int, 0x118>(), std::integral_constant<int, 0xf>());  // row_shr:8
+  v += sh(v, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xa>());  // row_bcast:15
+  v += sh(v, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xc>());  // row_bcast:31
   return v;
 }
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  return v;
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int) {
+  return dpp_scan(v, [](unsigned long long x, auto c, auto r) { return dpp_u64<decltype(c)::value, decltype(r)::value>(x); });
 }
-__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  return v;
+__device__ __forceinline__ double wave_incl_scan(double v, int) {
+  return dpp_scan(v, [](double x, auto c, auto r) {
+    return __longlong_as_double((long long)dpp_u64<decltype(c)::value, decltype(r)::value>(
+        (unsigned long long)__double_as_longlong(x)));
+  });
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v, int) {
+  return dpp_scan(v, [](int x, auto c, auto r) {
+    return (int)dpp_u32<decltype(c)::value, decltype(r)::value>((uint32_t)x, 0u);
+  });
 }
 
 struct WaveSmem {
@@ -757,6 +772,78 @@ struct SelOut {
   unsigned long long m_keep, m_above;
 };
 
+// One digit of a selection: scans the 256-bin histogram in ws from the top
+// digit down, with the counts and masses above it (above_c, above_m), for
+// the first digit whose inclusive cumulative count (top-k) or fixed-point
+// mass (nucleus) reaches `target`; without one (not reached), the lowest
+// non-empty digit.  Adds the exclusive sums at the digit to above_*, and
+// returns the digit with its own count and mass in last_*.
+__device__ __forceinline__ int pick_digit(const WaveSmem& ws, bool by_mass, unsigned long long target,
+                                          unsigned long long& above_c, unsigned long long& above_m,
+                                          unsigned long long& last_c, unsigned long long& last_m, bool& reached,
+                                          int lane) {
+  // lane l holds digits 255 - 4l - j, j = 0..3: descending over the wave
+  unsigned long long c[4], m[4], lc = 0, lm = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = ws.hc[255 - 4 * lane - j];
+    m[j] = ws.hm[255 - 4 * lane - j];
+    lc += c[j];
+    lm += m[j];
+  }
+  const unsigned long long ec = wave_incl_scan_u64(lc, lane) - lc, em = wave_incl_scan_u64(lm, lane) - lm;
+  int bj = -1, nj = -1;
+  unsigned long long xc = 0, xm = 0, yc = 0, ym = 0;  // exclusive sums at the hit / last non-empty digit
+  unsigned long long rc = ec, rm = em;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = by_mass ? (above_m + rm + m[j] >= target) : (above_c + rc + c[j] >= target);
+    if (ok && bj < 0) {
+      bj = j;
+      xc = rc;
+      xm = rm;
+    }
+    if (c[j] > 0) {
+      nj = j;
+      yc = rc;
+      ym = rm;
+    }
+    rc += c[j];
+    rm += m[j];
+  }
+  const uint64_t hit = __ballot(bj >= 0);
+  int L, J;
+  unsigned long long ac, am;
+  if (hit) {
+    L = __ffsll((long long)hit) - 1;
+    J = __shfl(bj, L);
+    ac = __shfl(xc, L);
+    am = __shfl(xm, L);
+  } else {
+    reached = false;  // keep everything: the lowest non-empty digit
+    const uint64_t ne = __ballot(nj >= 0);
+    L = ne ? 63 - __clzll((long long)ne) : kWave - 1;
+    J = ne ? __shfl(nj, L) : 3;
+    ac = __shfl(yc, L);
+    am = __shfl(ym, L);
+  }
+  const int dg = 255 - 4 * L - J;
+  above_c += ac;
+  above_m += am;
+  last_c = ws.hc[dg];
+  last_m = ws.hm[dg];
+  return dg;
+}
+
+__device__ __forceinline__ void clear_histogram(WaveSmem& ws, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ws.hc[lane + kWave * j] = 0;
+    ws.hm[lane + kWave * j] = 0;
+  }
+  wave_sync();
+}
+
 // MSB-first radix selection (8-bit digits) over order-preserving keys: the
 // largest logit value T whose inclusive descending cumulative count (top-k)
 // or fixed-point mass (nucleus) reaches `target`.  Integer histograms make
@@ -771,12 +858,7 @@ __device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigne
   bool reached = true;
   for (int lv = 0; lv < levels; ++lv) {
     const int shift = 24 - 8 * lv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ws.hc[lane + kWave * j] = 0;
-      ws.hm[lane + kWave * j] = 0;
-    }
-    wave_sync();
+    clear_histogram(ws, lane);
     each([&](float x, unsigned long long m) {
       const uint32_t key = fkey(x);
       if ((key & pmask) == pkey) {
@@ -786,59 +868,7 @@ __device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigne
       }
     });
     wave_sync();
-    // lane l holds digits 255 - 4l - j, j = 0..3: descending over the wave
-    unsigned long long c[4], m[4], lc = 0, lm = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = ws.hc[255 - 4 * lane - j];
-      m[j] = ws.hm[255 - 4 * lane - j];
-      lc += c[j];
-      lm += m[j];
-    }
-    const unsigned long long ec = wave_incl_scan_u64(lc, lane) - lc, em = wave_incl_scan_u64(lm, lane) - lm;
-    // the first digit (from the top) whose inclusive cumulative reaches the target
-    int bj = -1, nj = -1;
-    unsigned long long xc = 0, xm = 0, yc = 0, ym = 0;  // exclusive sums at the hit / last non-empty digit
-    unsigned long long rc = ec, rm = em;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = by_mass ? (above_m + rm + m[j] >= target) : (above_c + rc + c[j] >= target);
-      if (ok && bj < 0) {
-        bj = j;
-        xc = rc;
-        xm = rm;
-      }
-      if (c[j] > 0) {
-        nj = j;
-        yc = rc;
-        ym = rm;
-      }
-      rc += c[j];
-      rm += m[j];
-    }
-    const uint64_t hit = __ballot(bj >= 0);
-    int L, J;
-    unsigned long long ac, am, cc, cm;
-    if (hit) {
-      L = __ffsll((long long)hit) - 1;
-      J = __shfl(bj, L);
-      ac = __shfl(xc, L);
-      am = __shfl(xm, L);
-    } else {
-      reached = false;  // keep everything: the lowest non-empty digit
-      const uint64_t ne = __ballot(nj >= 0);
-      L = ne ? 63 - __clzll((long long)ne) : kWave - 1;
-      J = ne ? __shfl(nj, L) : 3;
-      ac = __shfl(yc, L);
-      am = __shfl(ym, L);
-    }
-    const int dg = 255 - 4 * L - J;
-    cc = ws.hc[dg];
-    cm = ws.hm[dg];
-    above_c += ac;
-    above_m += am;
-    last_c = cc;
-    last_m = cm;
+    const int dg = pick_digit(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
     pkey |= (uint32_t)dg << shift;
     pmask |= 255u << shift;
     wave_sync();
@@ -851,6 +881,51 @@ __device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigne
   r.m_keep = above_m + last_m;
   r.m_above = above_m;
   return r;
+}
+
+// Whether bf16 elements known to lie in [lo, hi] span fewer than 256
+// 16-bit keys: then one histogram level over the keys themselves gives the
+// selection (select_narrow).
+__device__ __forceinline__ bool narrow_range(float lo, float hi) {
+  return lo <= hi && (fkey(hi) >> 16) - (fkey(lo) >> 16) < 256u;
+}
+
+// The same selection as wave_select in one level, for bf16 elements in
+// [lo, hi] with narrow_range(lo, hi): digit 255 - (key(hi) - key).
+template <class Each>
+__device__ __forceinline__ SelOut select_narrow(Each&& each, bool by_mass, unsigned long long target, WaveSmem& ws,
+                                                int lane, float hi) {
+  const uint32_t kb = (fkey(hi) >> 16) - 255u;  // the key of digit 0
+  unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
+  bool reached = true;
+  clear_histogram(ws, lane);
+  each([&](float x, unsigned long long m) {
+    const uint32_t dg = min(255u, (fkey(x) >> 16) - kb);  // the bound only guards the index
+    atomicAdd(&ws.hc[dg], 1u);
+    atomicAdd(&ws.hm[dg], m);
+  });
+  wave_sync();
+  const int dg = pick_digit(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+  wave_sync();
+  uint32_t pkey = (kb + (uint32_t)dg) << 16;
+  pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
+  SelOut r;
+  r.T = key_value(pkey);
+  r.reached = reached;
+  r.n_keep = (uint32_t)(above_c + last_c);
+  r.m_keep = above_m + last_m;
+  r.m_above = above_m;
+  return r;
+}
+
+// Selection over elements known to lie in [lo, hi].
+template <int DT, class Each>
+__device__ __forceinline__ SelOut select_bounded(Each&& each, bool by_mass, unsigned long long target,
+                                                 WaveSmem& ws, int lane, float lo, float hi) {
+  if constexpr (DT == SV_BF16) {
+    if (narrow_range(lo, hi)) return select_narrow(each, by_mass, target, ws, lane, hi);
+  }
+  return wave_select<DT>(each, by_mass, target, ws, lane);
 }
 
 // Fixed-point mass of a logit, in units of the row's largest term:
@@ -891,24 +966,29 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
     ws.thr[lane] = th;
     wave_sync();
     const int nb = min(kWave, S - s0);
+    int top = 1;  // the largest power of two below nb (nb >= 2), else 0
+    while (2 * top < nb) top *= 2;
+    if (nb < 2) top = 0;
     for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
       int2 ent[kBatch];
       int ch[kBatch];
+      // the last chunk whose list starts at or before fi: a search of fixed
+      // depth, the kBatch searches interleaved (ws.pre is non-decreasing)
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) ch[q] = 0;
+      for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int fi = f0 + q * kWave + lane;
+          const int m = ch[q] + step;
+          if (m < nb && ws.pre[m] <= fi) ch[q] = m;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int fi = f0 + q * kWave + lane;
         ent[q] = make_int2(0, 0);
-        ch[q] = 0;
-        if (fi < tot) {
-          int lo = 0, hi = nb - 1;  // the last chunk whose list starts at or before fi
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (ws.pre[mid] <= fi) lo = mid;
-            else hi = mid - 1;
-          }
-          ch[q] = lo;
-          ent[q] = P.cent[(slot0 + s0 + lo) * (size_t)P.cap + (fi - ws.pre[lo])];
-        }
+        if (fi < tot) ent[q] = P.cent[(slot0 + s0 + ch[q]) * (size_t)P.cap + min(fi - ws.pre[ch[q]], P.cap - 1)];
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
@@ -1087,16 +1167,19 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
       // re-read when they do not fit or the threshold falls below C.
       SelOut so;
       bool ok = false;
+      // an upper bound of every logit of the row: M comes from the chunks'
+      // largest terms, within a few ulps of the largest logit
+      const float Mhi = M + (fabsf(M) + 1.0f) * 0.001953125f;
       float C1 = by_mass ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
       if (!by_mass && C < kInf) {
         // top-k: the k-th largest logit is at least the k-th largest vector
         // maximum (every vector holds its maximum), so that key bounds it
         const int nk0 = min(filter_listed(P, slot0, rec_at, C, c2, false, lane, ws, true), kVecList);
-        const SelOut sk = wave_select<DT>(
+        const SelOut sk = select_bounded<DT>(
             [&](auto&& f) {
               for (int j = lane; j < nk0; j += kWave) f(ws.cx[j], 0ull);
             },
-            false, target, ws, lane);
+            false, target, ws, lane, C, Mhi);
         if (sk.reached) C1 = fmaxf(C, sk.T);
       }
       for (int pass = 0; pass < 2 && !ok && C < kInf; ++pass) {
@@ -1107,7 +1190,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
         src = 0;
         if (nv <= 4 * kWave) {
           load_candidates<DT, VEC>(P, rowc, 0, nv, lane, ws, rv, re);
-          so = wave_select<DT>(
+          so = select_bounded<DT>(
               [&](auto&& f) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -1121,7 +1204,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
                   }
                 }
               },
-              by_mass, target, ws, lane);
+              by_mass, target, ws, lane, Cuf, Mhi);
           src = 1;
         } else if (nv <= kVecList) {
           n = 0;
@@ -1135,14 +1218,14 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
           }
           if (n <= kRowCache) {
             wave_sync();
-            so = wave_select<DT>(
+            so = select_bounded<DT>(
                 [&](auto&& f) {
                   for (int j = lane; j < n; j += kWave) {
                     const float x = ws.cx[j];
                     f(x, mass_of(x, c2, oM, fM));
                   }
                 },
-                by_mass, target, ws, lane);
+                by_mass, target, ws, lane, Cuf, Mhi);
             src = 2;
           }
         }
