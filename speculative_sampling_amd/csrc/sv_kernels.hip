@@ -32,8 +32,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "sv_internal.h"
 
 namespace sv {
@@ -146,106 +144,67 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 // --------------------------------------------------------- reductions ----
-// Fixed-order butterflies: every lane ends with bit-identical results.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Wave scans and reductions by DPP lane moves: shifts of 1, 2, 4 and 8
+// lanes within each row of 16, then the last lane of row 0 / rows 0-1
+// broadcast into the rows above; lanes with no source take the identity.
+// Callers run them with the whole wave active.  Reductions read the result
+// from lane 63, so every lane gets the same bits.
+template <int CTRL, int ROWS, class T>
+__device__ __forceinline__ T dpp_move(T v, T id) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                             CTRL, ROWS, 0xf, false));
+  } else {
+    const unsigned long long a = __builtin_bit_cast(unsigned long long, v);
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, id);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)b, (int)(uint32_t)a, CTRL, ROWS, 0xf, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(b >> 32), (int)(uint32_t)(a >> 32), CTRL, ROWS, 0xf, false);
+    return __builtin_bit_cast(T, ((unsigned long long)hi << 32) | lo);
+  }
+}
+template <class T, class Op>
+__device__ __forceinline__ T wave_scan(T v, T id, Op op) {
+  v = op(v, dpp_move<0x111, 0xf>(v, id));  // row_shr:1
+  v = op(v, dpp_move<0x112, 0xf>(v, id));  // row_shr:2
+  v = op(v, dpp_move<0x114, 0xf>(v, id));  // row_shr:4
+  v = op(v, dpp_move<0x118, 0xf>(v, id));  // row_shr:8
+  v = op(v, dpp_move<0x142, 0xa>(v, id));  // row_bcast:15
+  v = op(v, dpp_move<0x143, 0xc>(v, id));  // row_bcast:31
   return v;
+}
+// The value of lane L (wave-uniform) for every lane.
+template <class T>
+__device__ __forceinline__ T lane_at(T v, int L) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), L));
+  } else {
+    const unsigned long long a = __builtin_bit_cast(unsigned long long, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, L);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), L);
+    return __builtin_bit_cast(T, ((unsigned long long)hi << 32) | lo);
+  }
+}
+template <class T>
+__device__ __forceinline__ T lane63(T v) {
+  return lane_at(v, kWave - 1);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return lane63(wave_scan(v, -kInf, [](float a, float b) { return fmaxf(a, b); }));
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return lane63(wave_scan(v, 0.0, [](double a, double b) { return a + b; }));
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return lane63(wave_scan(v, 0x7fffffff, [](int a, int b) { return min(a, b); }));
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  return lane63(wave_scan(v, (int)0x80000000, [](int a, int b) { return max(a, b); }));
 }
-
-struct Red {
-  float f[8];
-  double d[4];
-  int i[4];
-  unsigned long long u[4];
-};
-
-__device__ __forceinline__ float block_max(float v, Red& r) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.f[w] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(r.f[0], r.f[1]), fmaxf(r.f[2], r.f[3]));
-}
-__device__ __forceinline__ double block_sum(double v, Red& r) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.d[w] = v;
-  __syncthreads();
-  return (r.d[0] + r.d[1]) + (r.d[2] + r.d[3]);
-}
-__device__ __forceinline__ int block_sum_i(int v, Red& r) {
-  v = wave_sum_i(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.i[w] = v;
-  __syncthreads();
-  return (r.i[0] + r.i[1]) + (r.i[2] + r.i[3]);
-}
-__device__ __forceinline__ int block_min_i(int v, Red& r) {
-  v = wave_min_i(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.i[w] = v;
-  __syncthreads();
-  return min(min(r.i[0], r.i[1]), min(r.i[2], r.i[3]));
-}
-__device__ __forceinline__ int block_max_i(int v, Red& r) {
-  v = wave_max_i(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.i[w] = v;
-  __syncthreads();
-  return max(max(r.i[0], r.i[1]), max(r.i[2], r.i[3]));
-}
-__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, Red& r) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) r.u[w] = v;
-  __syncthreads();
-  return (r.u[0] + r.u[1]) + (r.u[2] + r.u[3]);
-}
-
-// Exclusive prefix sum over the work-group in thread order (fp64).
-__device__ __forceinline__ double block_exclusive_scan(double v, double* total, Red& r) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  __syncthreads();
-  if (lane == 63) r.d[w] = inc;
-  __syncthreads();
-  double base = 0.0;
-  for (int j = 0; j < w; ++j) base += r.d[j];
-  *total = ((r.d[0] + r.d[1]) + r.d[2]) + r.d[3];
-  return base + inc - v;
+__device__ __forceinline__ uint32_t wave_or_u(uint32_t v) {
+  return lane63(wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
 }
 
 // ---------------------------------------------------- per-sequence params --
@@ -707,42 +666,14 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Inclusive wave scans by DPP lane moves: shifts of 1, 2, 4 and 8 lanes
-// within each row of 16, then the last lane of row 0 / rows 0-1 broadcast
-// into the rows above.  Lanes with no source take the identity.  Called
-// with the whole wave active.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t id) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v, 0u), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32), 0u);
-  return ((unsigned long long)hi << 32) | lo;
-}
-template <class T, class Shift>
-__device__ __forceinline__ T dpp_scan(T v, Shift&& sh) {
-  v += sh(v, std::integral_constant<int, 0x111>(), std::integral_constant<int, 0xf>());  // row_shr:1
-  v += sh(v, std::integral_constant<int, 0x112>(), std::integral_constant<int, 0xf>());  // row_shr:2
-  v += sh(v, std::integral_constant<int, 0x114>(), std::integral_constant<int, 0xf>());  // row_shr:4
-  v += sh(v, std::integral_constant<int, 0x118>(), std::integral_constant<int, 0xf>());  // row_shr:8
-  v += sh(v, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xa>());  // row_bcast:15
-  v += sh(v, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xc>());  // row_bcast:31
-  return v;
-}
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int) {
-  return dpp_scan(v, [](unsigned long long x, auto c, auto r) { return dpp_u64<decltype(c)::value, decltype(r)::value>(x); });
+  return wave_scan(v, 0ull, [](unsigned long long a, unsigned long long b) { return a + b; });
 }
 __device__ __forceinline__ double wave_incl_scan(double v, int) {
-  return dpp_scan(v, [](double x, auto c, auto r) {
-    return __longlong_as_double((long long)dpp_u64<decltype(c)::value, decltype(r)::value>(
-        (unsigned long long)__double_as_longlong(x)));
-  });
+  return wave_scan(v, 0.0, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ int wave_incl_scan_i(int v, int) {
-  return dpp_scan(v, [](int x, auto c, auto r) {
-    return (int)dpp_u32<decltype(c)::value, decltype(r)::value>((uint32_t)x, 0u);
-  });
+  return wave_scan(v, 0, [](int a, int b) { return a + b; });
 }
 
 struct WaveSmem {
@@ -816,16 +747,16 @@ __device__ __forceinline__ int pick_digit(const WaveSmem& ws, bool by_mass, unsi
   unsigned long long ac, am;
   if (hit) {
     L = __ffsll((long long)hit) - 1;
-    J = __shfl(bj, L);
-    ac = __shfl(xc, L);
-    am = __shfl(xm, L);
+    J = lane_at(bj, L);
+    ac = lane_at(xc, L);
+    am = lane_at(xm, L);
   } else {
     reached = false;  // keep everything: the lowest non-empty digit
     const uint64_t ne = __ballot(nj >= 0);
     L = ne ? 63 - __clzll((long long)ne) : kWave - 1;
-    J = ne ? __shfl(nj, L) : 3;
-    ac = __shfl(yc, L);
-    am = __shfl(ym, L);
+    J = ne ? lane_at(nj, L) : 3;
+    ac = lane_at(yc, L);
+    am = lane_at(ym, L);
   }
   const int dg = 255 - 4 * L - J;
   above_c += ac;
@@ -960,7 +891,7 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
       th = terms ? exp2f((float)((double)Cu * (double)c2 - (double)c.o) - 0.00390625f) : Cu;
     }
     const int inc = wave_incl_scan_i(cnt, lane);
-    const int tot = __shfl(inc, kWave - 1);
+    const int tot = lane63(inc);
     wave_sync();
     ws.pre[lane] = inc - cnt;
     ws.thr[lane] = th;
@@ -977,11 +908,13 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) ch[q] = 0;
       for (int step = top; step > 0; step >>= 1) {
+        int pv[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-          const int fi = f0 + q * kWave + lane;
           const int m = ch[q] + step;
-          if (m < nb && ws.pre[m] <= fi) ch[q] = m;
+          if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
         }
       }
 #pragma unroll
@@ -990,9 +923,12 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
         ent[q] = make_int2(0, 0);
         if (fi < tot) ent[q] = P.cent[(slot0 + s0 + ch[q]) * (size_t)P.cap + min(fi - ws.pre[ch[q]], P.cap - 1)];
       }
+      float th[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) th[q] = ws.thr[ch[q]];
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const bool pass = f0 + q * kWave + lane < tot && __int_as_float(ent[q].y) >= ws.thr[ch[q]];
+        const bool pass = f0 + q * kWave + lane < tot && __int_as_float(ent[q].y) >= th[q];
         const uint64_t bal = __ballot(pass);
         if (pass) {
           const int pos = nv + __popcll(bal & below);
@@ -1112,8 +1048,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
     fl |= c.flags;
   });
   const float M = wave_max(mx);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) fl |= (uint32_t)__shfl_xor((int)fl, o);
+  fl = wave_or_u(fl);
   rr.M = M;
   if ((fl & kCfNonFinite) || !(M < kInf) || isnan(M)) rr.flags |= SV_ST_NONFINITE;
   else if (M == -kInf) rr.flags |= SV_ST_EMPTY;
@@ -1459,7 +1394,7 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
         w[j] = use_p ? fmax(qv[j] - (double)pv[j], 0.0) : qv[j];
         const double inc = wave_incl_scan(w[j], lane);
         ex[j] = total + (inc - w[j]);
-        total += __shfl(inc, kWave - 1);
+        total += lane63(inc);
       }
     }
     if (total > 0.0 || !use_p) break;
@@ -1491,8 +1426,8 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
   double lo, hi;
   if (f <= lnz) {
     iy = f;
-    lo = __shfl(clo, f % kWave);
-    hi = __shfl(chi, f % kWave);
+    lo = lane_at(clo, f % kWave);
+    hi = lane_at(chi, f % kWave);
   } else {  // rounding left no entry above the target
     iy = lnz < 0 ? 0 : lnz;
     lo = total;
@@ -1502,7 +1437,7 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
 #pragma unroll
   for (int j = 0; j < E; ++j)
     if (j * kWave + lane == iy) yv = iv[j];
-  d.y = N > 0 ? __shfl(yv, iy % kWave) : 0;
+  d.y = N > 0 ? lane_at(yv, iy % kWave) : 0;
   if (N > 0 && lnz >= 0 && total > 0.0) {
     // margins of interior CDF boundaries
     if ((fnz < iy && u - lo / total < kWindow) || (lnz > iy && hi / total - u < kWindow)) d.flags |= SV_ST_MARGIN;
@@ -1724,7 +1659,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         for (int k = 0; k < 8; ++k) w[k] = 0.0;
       }
       const double inc = wave_incl_scan(sl, lane);
-      const double tile = __shfl(inc, kWave - 1);
+      const double tile = lane63(inc);
       if (c + tile > target) {
         int cand = 0x7fffffff;
         double r = c + inc - sl, cl = 0.0, ch = 0.0;
@@ -1743,8 +1678,8 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
           const uint64_t who = __ballot(cand == ym);
           const int src = __ffsll((long long)who) - 1;
           y = ym;
-          clo = __shfl(cl, src);
-          chi = __shfl(ch, src);
+          clo = lane_at(cl, src);
+          chi = lane_at(ch, src);
         }
       }
       c += tile;
@@ -1805,8 +1740,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   uint32_t v = 0;
   for (int t = tid; t <= Kb; t += kSeqThreads) v |= sm.rows[t].flags;
   for (int t = tid; t < Kb; t += kSeqThreads) v |= sm.rows[KM + 1 + t].flags;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o);
+  v = wave_or_u(v);
   if (lane == 0) sm.ri[wv] = (int)v;
   __syncthreads();
   uint32_t st = 0;
@@ -1850,8 +1784,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
       if (walking && rb) n = t0 + __ffsll((long long)rb) - 1;
       // status bits of the positions the walk reached (up to the first rejection)
       uint32_t s3 = (walking && t <= n && t < Kb) ? s2 : 0u;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s3 |= (uint32_t)__shfl_xor((int)s3, o);
+      s3 = wave_or_u(s3);
       s_all |= s3;
     }
     if (lane == 0) {
