@@ -14,7 +14,10 @@ drawn by the library itself (the step with K = 0 on the draft rows).
 Prints one JSON line: value = rows/s; roofline = algorithmic logit bytes per
 call / average time of the streaming kernel (HIP events the library records
 around its stages on the launch stream) against the 8 TB/s HBM peak;
-cpu_baseline = the fp64 oracle on a bounded sample.
+streaming_ceiling = the read rate of the library's read-only probe over the
+same rotating logits; per_call_us = p10 / median / p90 of single calls;
+cpu_baseline = the fp64 oracle on a bounded sample, on one thread and on
+disjoint sequences in up to 16 threads.
 """
 import argparse
 import hashlib
@@ -139,13 +142,48 @@ def main():
     seq_ms = stage1_ms / runs           # per-sequence merge, accept walk, draw
     achieved = alg_bytes / (stream_ms * 1e-3) / 1e9
 
+    # per-call spread: each call bracketed by its own pair of events
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    pct = lambda f: per_call[min(len(per_call) - 1, int(f * len(per_call)))]
+
+    # streaming ceiling: the library's read-only probe over the same rotating
+    # logits (same access pattern as the streaming pass, no arithmetic)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe_bytes = sum(w.target.numel() * w.target.element_size() + w.draft.numel() * w.draft.element_size()
+                      for w in sets) / len(sets)
+
+    def probe(i):
+        w = sets[i % len(sets)]
+        for x in (w.target, w.draft):
+            binding.spec_verify_stream_probe(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(),
+                                             stream.cuda_stream)
+
+    for i in range(args.warmup):
+        probe(i)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        probe(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe_bytes / (t0.elapsed_time(t1) / args.steps * 1e-3) / 1e9
+
     # acceptance actually achieved by the synthetic draft (context)
     acc = torch.cat([o[0] for o in outs]).float()
     alpha_tokens = float(acc.mean().item())
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu:
         cpu = cpu_baseline(sets[0], args.cpu_seconds)
+        cpu_all = cpu_baseline(sets[0], args.cpu_seconds, threads=min(16, os.cpu_count() or 1))
 
     traffic = stored_traffic(name)
     line = {
@@ -167,11 +205,18 @@ def main():
         "logits_GBps": gbs_step,
         "pct_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS,
         "stage_ms": {"stream": stream_ms, "sequence": seq_ms},
+        "per_call_us": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
+                        "note": "each call bracketed by its own events"},
+        "streaming_ceiling": {"GBps": ceiling, "kernel": "stream_probe_kernel",
+                              "pct_hbm_peak": 100.0 * ceiling / HBM_PEAK_GBS,
+                              "chunk_kernel_frac_of_ceiling": achieved / ceiling,
+                              "value_frac_of_ceiling": gbs_step / ceiling},
         "mean_accepted": alpha_tokens,
         "roofline": {"bound": "hbm", "kernel": "chunk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     v.close()
     print(json.dumps(line), flush=True)
@@ -191,25 +236,45 @@ def calibrate_copy(torch, nbytes, steps):
                       "launches": steps}), flush=True)
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, threads=1):
     """The oracle, as it stands, on whole sequences of the same workload until
-    the time budget is spent; reported in rows/s (sequences per second)."""
+    the time budget is spent; reported in rows/s (sequences per second).
+    With threads > 1 the same single-threaded oracle runs on disjoint
+    sequences in that many threads (its calls release the GIL)."""
+    import threading
     import oracle
     from speculative_sampling_amd import workloads
 
     tgt = workloads.host_array(w.target)
     drf = workloads.host_array(w.draft)
     toks = w.draft_tokens.cpu().numpy()
-    done = 0
+    lock = threading.Lock()
+    state = {"next": 0, "done": 0}
     t0 = time.perf_counter()
-    while done < w.B and time.perf_counter() - t0 < budget_s:
-        oracle.verify(tgt[done:done + 1], drf[done:done + 1], toks[done:done + 1],
-                      default_mode=w.default_mode, default_temperature=w.default_temperature,
-                      default_top_p=w.default_top_p, seed=w.seed, row_offset=done)
-        done += 1
+
+    def worker():
+        while True:
+            with lock:
+                b = state["next"]
+                if b >= w.B or time.perf_counter() - t0 >= budget_s:
+                    return
+                state["next"] = b + 1
+            oracle.verify(tgt[b:b + 1], drf[b:b + 1], toks[b:b + 1],
+                          default_mode=w.default_mode, default_temperature=w.default_temperature,
+                          default_top_p=w.default_top_p, seed=w.seed, row_offset=b)
+            with lock:
+                state["done"] += 1
+
+    pool = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.B} sequences of input set 0 ({el:.1f} s, single-threaded fp64)"}
+    done = state["done"]
+    kind = "single-threaded fp64" if threads == 1 else f"fp64 oracle on disjoint sequences, {threads} threads"
+    return {"value": done / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of input set 0 ({el:.1f} s, {kind})"}
 
 
 if __name__ == "__main__":

@@ -182,6 +182,17 @@ uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 int spec_verify_profile_begin(sv_handle_t h, int max_calls);
 int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages);
 
+/* Streaming ceiling, for measurement: reads the first floor(bytes / 16384)
+ * whole 16 KB blocks at data (a 16-byte aligned device pointer) once, with
+ * the streaming pass's access pattern (one 16 KB block per wave, 16-byte
+ * vectors, constant offsets) and no arithmetic beyond an xor fold, on the
+ * given stream (NULL = the default stream), asynchronously.  out is a device
+ * pointer to at least 4 bytes; it is written only when the fold hits a
+ * fixed value.  Allocates nothing.  Returns SV_OK, or SV_EINVAL / SV_EHIP
+ * with spec_verify_last_error set.  It computes nothing of the method: it
+ * gives the read rate the streaming pass is measured against. */
+int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* stream);
+
 /* Text of the last error reported on the calling thread ("" if none). */
 const char* spec_verify_last_error(void);
 

@@ -26,7 +26,7 @@ ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 # Every function the header declares.
 EXPORTS = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy",
            "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_profile_begin",
-           "spec_verify_profile_end", "spec_verify_last_error")
+           "spec_verify_profile_end", "spec_verify_stream_probe", "spec_verify_last_error")
 
 
 class SvConfig(ctypes.Structure):
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_profile_begin.restype = ctypes.c_int
     lib.spec_verify_profile_end.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
     lib.spec_verify_profile_end.restype = ctypes.c_int
+    lib.spec_verify_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_verify_stream_probe.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -199,6 +201,15 @@ def spec_verify_profile_end(handle: int):
     if rc < 0:
         raise SpecVerifyError(rc, "spec_verify_profile_end")
     return rc, [ms[0], ms[1]]
+
+
+def spec_verify_stream_probe(data_ptr: int, nbytes: int, out_ptr: int, stream: int = 0) -> None:
+    """Reads nbytes // 16384 whole 16 KB blocks at data_ptr once (a
+    measurement of the streaming ceiling; see the header)."""
+    rc = load_library().spec_verify_stream_probe(ctypes.c_void_p(data_ptr), nbytes, ctypes.c_void_p(out_ptr),
+                                                 ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_stream_probe")
 
 
 class Verifier:

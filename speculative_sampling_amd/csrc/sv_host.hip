@@ -295,6 +295,14 @@ int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages) {
   return runs;
 }
 
+int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* stream) {
+  if (!data || !out) return fail(SV_EINVAL, "stream probe: data and out must be device pointers");
+  if (reinterpret_cast<uintptr_t>(data) % 16 != 0) return fail(SV_EINVAL, "stream probe: data must be 16-byte aligned");
+  const hipError_t e = sv::launch_stream_probe(data, bytes, static_cast<uint32_t*>(out), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("stream probe launch failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}
+
 int spec_verify_destroy(sv_handle_t h) {
   if (!h) return SV_OK;
   int prev = 0;

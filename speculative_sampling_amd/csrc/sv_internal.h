@@ -104,5 +104,7 @@ struct KParams {
 // before the streaming pass, between the two stages and after the last.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream,
                          hipEvent_t* ev = nullptr);
+// Reads the first bytes / 16384 whole 16 KB blocks of data once (see spec_verify_stream_probe).
+hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hipStream_t stream);
 
 }  // namespace sv

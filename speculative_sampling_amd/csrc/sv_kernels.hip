@@ -444,16 +444,19 @@ __device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, 
 __device__ __forceinline__ int list_vectors(int2* de, uint32_t mask, const float* key, int c0, int ve, int cap,
                                             int lane) {
   const uint64_t below = (1ull << lane) - 1ull;
+  const int e0 = c0 + lane * ve;  // first index of the lane's vector in slot 0
   int n = 0;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const bool h = (mask >> i) & 1u;
     const uint64_t bal = __ballot(h);
-    if (h) {
-      const int pos = n + __popcll(bal & below);
-      if (pos < cap) de[pos] = make_int2(c0 + (i * kWave + lane) * ve, __float_as_int(key[i]));
+    if (bal) {  // slots with no listed vector cost one ballot
+      if (h) {
+        const int pos = n + __popcll(bal & below);
+        if (pos < cap) de[pos] = make_int2(e0 + i * kWave * ve, __float_as_int(key[i]));
+      }
+      n += __popcll(bal);
     }
-    n += __popcll(bal);
   }
   return n;
 }
@@ -504,7 +507,7 @@ __device__ __forceinline__ void plain_stats(uint4 (&buf)[kLoads], float c2, cons
   ps.o = o;
   ps.zw = wave_sum((double)zt);
   // the largest term 2^a belongs to the chunk maximum x = (a + o) / c2
-  ps.ma = ps.st == 0 ? ((double)log2f(em) + (double)o) / (double)c2 : -1e300;
+  ps.ma = ps.st == 0 ? ((double)log2f(em) + (double)o) * (1.0 / (double)c2) : -1e300;
 }
 
 // Finishes a plain / nucleus chunk.  A nucleus chunk lists every logit
@@ -528,13 +531,16 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
   rec.m = m;
   rec.o = ps.o;
   // refer the sum to m: 2^(x c2 - o) = 2^((x - m) c2) 2^(m c2 - o)
-  rec.z = ps.zw * exp2((double)ps.o - (double)m * (double)c2);
+  // (the exponent is -log2 of the largest term, within [-2^7, 0]: fp32
+  // exp2 keeps the ~1e-7 relative error of the terms themselves)
+  rec.z = ps.zw * (double)exp2f((float)((double)ps.o - (double)m * (double)c2));
   if (cand) {
     int2* de = P.cent + slot * (size_t)P.cap;
     int n = 0;
     float cut = kInf;
+    const double ic2 = 1.0 / (double)c2;
     for (int attempt = 0; attempt < 3; ++attempt) {
-      cut = (float)(g - (attempt == 0 ? kCandLog2 : attempt == 1 ? 8.0f : 6.0f) / (double)c2);
+      cut = (float)(g - (attempt == 0 ? kCandLog2 : attempt == 1 ? 8.0 : 6.0) * ic2);
       // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
       const float thr = exp2f((float)((double)cut * (double)c2 - (double)ps.o) - 0.00390625f);
       uint32_t mask = 0;
@@ -892,8 +898,9 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
     }
     const int inc = wave_incl_scan_i(cnt, lane);
     const int tot = lane63(inc);
+    const int pre = inc - cnt;  // list start of chunk s0 + lane
     wave_sync();
-    ws.pre[lane] = inc - cnt;
+    ws.pre[lane] = pre;
     ws.thr[lane] = th;
     wave_sync();
     const int nb = min(kWave, S - s0);
@@ -907,14 +914,24 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
       // depth, the kBatch searches interleaved (ws.pre is non-decreasing)
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) ch[q] = 0;
-      for (int step = top; step > 0; step >>= 1) {
-        int pv[kBatch];
+      if (nb <= 32) {
+        // count the list starts at or before fi, each start read once into
+        // a scalar register
+        for (int m = 1; m < nb; ++m) {
+          const int st = lane_at(pre, m);
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
+          for (int q = 0; q < kBatch; ++q) ch[q] += st <= f0 + q * kWave + lane ? 1 : 0;
+        }
+      } else {
+        for (int step = top; step > 0; step >>= 1) {
+          int pv[kBatch];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int m = ch[q] + step;
-          if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
+          for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int m = ch[q] + step;
+            if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
+          }
         }
       }
 #pragma unroll
@@ -1710,14 +1727,32 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   return d;
 }
 
-__device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i <= P.K_max; i += kSeqThreads) P.out_tokens[(size_t)b * (P.K_max + 1) + i] = -1;
+// An error row: accepted = -1, every token -1, diagnostics NaN (threads
+// first, first + stride, ... of the caller's group).
+__device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st, int first, int stride) {
+  for (int i = first; i <= P.K_max; i += stride) P.out_tokens[(size_t)b * (P.K_max + 1) + i] = -1;
   if (P.diag)
-    for (int i = tid; i < 2 * P.K_max; i += kSeqThreads) P.diag[(size_t)b * 2 * P.K_max + i] = __builtin_nanf("");
-  if (tid == 0) {
+    for (int i = first; i < 2 * P.K_max; i += stride) P.diag[(size_t)b * 2 * P.K_max + i] = __builtin_nanf("");
+  if (first == 0) {
     P.accepted[b] = -1;
     if (P.status) P.status[b] = st;
+  }
+}
+
+// Accepted drafts d_0..d_{n-1}, then y, then -1 (threads first, first +
+// stride, ...).
+__device__ __forceinline__ void write_tokens(const KParams& P, int b, int n, int y, uint32_t st, int first,
+                                             int stride) {
+  const int KM = P.K_max;
+  for (int i = first; i <= KM; i += stride) {
+    int val = -1;
+    if (i < n) val = P.tokens[(size_t)b * KM + i];
+    else if (i == n) val = y;
+    P.out_tokens[(size_t)b * (KM + 1) + i] = val;
+  }
+  if (first == 0) {
+    P.accepted[b] = n;
+    if (P.status) P.status[b] = st & ~kRfListOk;
   }
 }
 
@@ -1729,112 +1764,105 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   const int b = P.b_base + (int)blockIdx.x;
   const SeqParams sp = load_params(P, b);
   if (!sp.valid) {
-    write_error(P, b, SV_ST_PARAM);
+    write_error(P, b, SV_ST_PARAM, tid, kSeqThreads);
     return;
   }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
   for (int r = wv; r < R; r += kSeqWaves) merge_row<DT, VEC>(P, sp, b, r, lane, sm.w[wv], sm.rows[r]);
   __syncthreads();
 
-  // OR of the used rows' flags
-  uint32_t v = 0;
-  for (int t = tid; t <= Kb; t += kSeqThreads) v |= sm.rows[t].flags;
-  for (int t = tid; t < Kb; t += kSeqThreads) v |= sm.rows[KM + 1 + t].flags;
-  v = wave_or_u(v);
-  if (lane == 0) sm.ri[wv] = (int)v;
-  __syncthreads();
-  uint32_t st = 0;
-#pragma unroll
-  for (int w = 0; w < kSeqWaves; ++w) st |= (uint32_t)sm.ri[w];
-  __syncthreads();
-  st &= ~kRfListOk;
-  if (st & kErrBits) {
-    write_error(P, b, st & kErrBits);
-    return;
-  }
+  // Wave 0: the rows' flags, the accept walk, and the draw when it needs no
+  // more than the kept set in LDS.  The work-group joins only for a draw
+  // from the rows.
   const uint64_t g = P.row_offset + (uint64_t)b;
-  // accept walk: lane t scores position t0 + t; the first rejection by ballot
   if (wv == 0) {
-    int n = Kb;
-    uint32_t s_all = 0;
-    for (int t0 = 0; t0 < KM; t0 += kWave) {
-      const int t = t0 + lane;
-      bool rej = false;
-      uint32_t s2 = 0;
-      if (t < KM) {
-        double q = __builtin_nan(""), p = __builtin_nan("");
+    uint32_t st = 0;
+    for (int t = lane; t <= Kb; t += kWave) st |= sm.rows[t].flags;
+    for (int t = lane; t < Kb; t += kWave) st |= sm.rows[KM + 1 + t].flags;
+    st = wave_or_u(st) & ~kRfListOk;
+    int job = 0;  // 0 done, 1 draw from the rows
+    if (st & kErrBits) {
+      write_error(P, b, st & kErrBits, lane, kWave);
+    } else {
+      if (P.diag) {
+        for (int t = lane; t < KM; t += kWave) {
+          float q = __builtin_nanf(""), p = __builtin_nanf("");
+          if (t < Kb) {
+            q = (float)sm.rows[t].pid;
+            p = (float)sm.rows[KM + 1 + t].pid;
+          }
+          P.diag[((size_t)b * KM + t) * 2 + 0] = q;
+          P.diag[((size_t)b * KM + t) * 2 + 1] = p;
+        }
+      }
+      // lane t scores position t0 + t; the first rejection by ballot.  The
+      // same lanes draw the uniform of a resample at t (t < K_b) or of the
+      // bonus (t = K_b), so the draw's uniform is ready with n.
+      int n = Kb;
+      double u = 0.0;
+      for (int t0 = 0; t0 <= Kb; t0 += kWave) {
+        const int t = t0 + lane;
+        bool rej = false;
+        uint32_t s2 = 0;
+        double ud = 0.0;
         if (t < Kb) {
-          q = sm.rows[t].pid;
-          p = sm.rows[KM + 1 + t].pid;
-          const double u = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
-          rej = !(u * p < q);
+          const double q = sm.rows[t].pid, p = sm.rows[KM + 1 + t].pid;
+          const double ua = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
+          rej = !(ua * p < q);
           if (p == 0.0) s2 |= SV_ST_PZERO;
           if (p > 0.0) {
             const double ratio = q / p;
-            if (ratio < 1.0 + kWindow && fabs(u - ratio) < kWindow) s2 |= SV_ST_MARGIN;
+            if (ratio < 1.0 + kWindow && fabs(ua - ratio) < kWindow) s2 |= SV_ST_MARGIN;
           }
         }
-        if (P.diag) {
-          P.diag[((size_t)b * KM + t) * 2 + 0] = (float)q;
-          P.diag[((size_t)b * KM + t) * 2 + 1] = (float)p;
+        if (t <= Kb) ud = uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
+        const uint64_t rb = __ballot(rej);
+        const int end = rb ? t0 + __ffsll((long long)rb) - 1 : Kb;  // the walk stops here if < t0 + 64
+        // status bits of the positions the walk reached (up to the first rejection)
+        st |= wave_or_u((t <= end && t < Kb) ? s2 : 0u);
+        if (end < t0 + kWave) {
+          n = end;
+          u = lane_at(ud, n - t0);
+          break;
         }
       }
-      const bool walking = n == Kb;  // no rejection in earlier batches
-      const uint64_t rb = __ballot(rej);
-      if (walking && rb) n = t0 + __ffsll((long long)rb) - 1;
-      // status bits of the positions the walk reached (up to the first rejection)
-      uint32_t s3 = (walking && t <= n && t < Kb) ? s2 : 0u;
-      s3 = wave_or_u(s3);
-      s_all |= s3;
+      const bool resample = n < Kb;
+      const RowRec& rq = sm.rows[n];
+      const RowRec& rp = resample ? sm.rows[KM + 1 + n] : sm.rows[n];
+      if (sp.mode == SV_GREEDY) {
+        const int y = rq.g;
+        if (resample && rp.g == rq.g) st |= SV_ST_ZERO_RESIDUAL;
+        write_tokens(P, b, n, y, st, lane, kWave);
+      } else if (rq.flags & kRfListOk) {
+        const Draw d = draw_from_list<DT>(P, rq, resample, rp, (size_t)b * R + n,
+                                          resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, lane,
+                                          R <= kSeqWaves ? &sm.w[n] : nullptr);
+        write_tokens(P, b, n, d.y, st | d.flags, lane, kWave);
+      } else {
+        job = 1;
+        if (lane == 0) {
+          sm.misc[0] = (uint32_t)n;
+          sm.misc[1] = st;
+          sm.rx[0] = u;
+        }
+      }
     }
-    if (lane == 0) {
-      sm.misc[0] = (uint32_t)n;
-      sm.misc[1] = s_all;
-    }
+    if (lane == 0) sm.misc[2] = (uint32_t)job;
   }
   __syncthreads();
+  if (sm.misc[2] == 0u) return;
+  // draw from the rows (plain mode, or a kept set not held as a list)
   const int n = (int)sm.misc[0];
-  st |= sm.misc[1];
-
+  uint32_t st = sm.misc[1];
+  const double u = sm.rx[0];
   const bool resample = n < Kb;
   const RowRec rq = sm.rows[n];
   const RowRec rp = resample ? sm.rows[KM + 1 + n] : rq;
-  const double u = uniform24(P.seed, g, (uint32_t)n, resample ? kPurposeResample : kPurposeBonus);
-  Draw d;
-  if (sp.mode == SV_GREEDY) {
-    d.y = rq.g;
-    d.flags = (resample && rp.g == rq.g) ? SV_ST_ZERO_RESIDUAL : 0u;
-  } else if (rq.flags & kRfListOk) {
-    d.y = 0;
-    d.flags = 0;
-    if (wv == 0) {
-      d = draw_from_list<DT>(P, rq, resample, rp, (size_t)b * R + n,
-                             resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, lane,
-                             R <= kSeqWaves ? &sm.w[n] : nullptr);
-      if (lane == 0) {
-        sm.misc[2] = (uint32_t)d.y;
-        sm.misc[3] = d.flags;
-      }
-    }
-    __syncthreads();
-    d.y = (int)sm.misc[2];
-    d.flags = sm.misc[3];
-  } else {
-    d = draw_from_rows<DT, VEC>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
-                                resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr, u, sm,
-                                lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
-  }
-  st |= d.flags;
-  for (int i = tid; i <= KM; i += kSeqThreads) {
-    int val = -1;
-    if (i < n) val = P.tokens[(size_t)b * KM + i];
-    else if (i == n) val = d.y;
-    P.out_tokens[(size_t)b * (KM + 1) + i] = val;
-  }
-  if (tid == 0) {
-    P.accepted[b] = n;
-    if (P.status) P.status[b] = st & ~kRfListOk;
-  }
+  __syncthreads();  // sm.misc / sm.rx are reused by the draw
+  const Draw d = draw_from_rows<DT, VEC>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
+                                         resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr,
+                                         u, sm, lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
+  write_tokens(P, b, n, d.y, st | d.flags, tid, kSeqThreads);
 }
 
 template <int DT, bool VEC>
@@ -1866,6 +1894,37 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
 }
 
 }  // namespace
+
+namespace {
+
+// Read-only streaming probe with the streaming pass's access pattern: each
+// wave reads one 16 KB block as 16 x 16-byte vectors per lane from one base
+// address with constant offsets, and folds it with xor.  out[0] is written
+// only if the fold hits a fixed value, so the loads cannot be dropped.
+__global__ __launch_bounds__(kThreads) void stream_probe_kernel(const uint4* data, size_t nblocks, uint32_t* out) {
+  const int lane = (int)__lane_id();
+  const size_t blk = (size_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (blk >= nblocks) return;
+  const uint4* base = data + blk * (size_t)(kLoads * kWave);
+  uint4 v[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) v[i] = base[i * kWave + lane];
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  if (x == 0x9e3779b9u) out[0] = x;
+}
+
+}  // namespace
+
+hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hipStream_t stream) {
+  const size_t nblocks = bytes / (kLoads * kWave * sizeof(uint4));
+  if (nblocks == 0) return hipSuccess;
+  const size_t wg = (nblocks + kThreads / kWave - 1) / (kThreads / kWave);
+  hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)wg), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(data), nblocks, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream, hipEvent_t* ev) {
   if (nseq <= 0) return hipSuccess;
