@@ -883,7 +883,7 @@ __device__ __forceinline__ unsigned long long mass_of(float x, float c2, float o
 template <class RecAt>
 __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, RecAt&& rec_at, float Cu, float c2,
                                              bool terms, int lane, WaveSmem& ws, bool keep_keys = false) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const int S = P.S;
   const uint64_t below = (1ull << lane) - 1ull;
   int nv = 0;

@@ -141,3 +141,15 @@ def test_product_path_fails_loudly_without_library(tmp_path):
             binding.load_library(missing)
     finally:
         binding._lib = saved
+
+
+@needs_lib
+def test_stream_probe_rejects_bad_pointers_on_the_host():
+    lib = binding.load_library()
+    sink = ctypes.c_uint32(0)
+    # NULL data or out, and data that is not 16-byte aligned, are refused
+    # before anything is launched
+    assert lib.spec_verify_stream_probe(None, 16384, ctypes.byref(sink), None) == SV_EINVAL
+    assert lib.spec_verify_stream_probe(ctypes.c_void_p(64), 16384, None, None) == SV_EINVAL
+    assert lib.spec_verify_stream_probe(ctypes.c_void_p(8), 16384, ctypes.byref(sink), None) == SV_EINVAL
+    assert b"aligned" in lib.spec_verify_last_error()
