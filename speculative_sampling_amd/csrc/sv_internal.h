@@ -25,8 +25,6 @@ constexpr int kListMax = 512;
 // Waves of the per-sequence kernel (one logit row each); sequences of more
 // rows keep their kept lists in global memory.
 constexpr int kSeqWaves = 12;
-// Largest number of chunks per row (V <= 2^22 with 4096 fp32 per chunk).
-constexpr int kMaxChunks = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxVocab = 1 << 22;
 

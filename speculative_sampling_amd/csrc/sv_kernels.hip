@@ -1277,16 +1277,6 @@ struct Draw {
   uint32_t flags;
 };
 
-__device__ __forceinline__ double seq_sum(double v, SmemSeq& sm) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.rd[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double s = 0.0;
-#pragma unroll
-  for (int w = 0; w < kSeqWaves; ++w) s += sm.rd[w];
-  return s;
-}
 __device__ __forceinline__ int seq_min_i(int v, SmemSeq& sm) {
   v = wave_min_i(v);
   __syncthreads();
