@@ -82,7 +82,7 @@ def main():
         calibrate_copy(torch, args.calibrate_copy, args.steps)
         return
 
-    from speculative_sampling_amd import binding, workloads
+    from speculative_sampling_amd import binding, loop_model, workloads
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -176,9 +176,22 @@ def main():
     torch.cuda.synchronize()
     ceiling = probe_bytes / (t0.elapsed_time(t1) / args.steps * 1e-3) / 1e9
 
-    # acceptance actually achieved by the synthetic draft (context)
-    acc = torch.cat([o[0] for o in outs]).float()
-    alpha_tokens = float(acc.mean().item())
+    # acceptance actually achieved by the synthetic draft (context), and the
+    # loop model: one round at the pages' model-call times (target 14.1 ms,
+    # draft 1.8 ms per token) with this verify step's measured time added
+    acc = torch.cat([o[0] for o in outs])
+    alpha_tokens = float(acc.float().mean().item())
+    mon = loop_model.AcceptanceMonitor(K)
+    mon.update(acc.cpu().numpy())
+    alphas = mon.alpha()
+    t_verify_ms = ms_per_step
+    loop = {"alpha_per_position": [round(float(a), 4) for a in alphas],
+            "tokens_per_round": mon.tokens_per_round(),
+            "predicted_tokens_per_round": mon.predicted_tokens_per_round(),
+            "t_target_ms": 14.1, "t_draft_ms": 1.8, "t_verify_ms": t_verify_ms,
+            "ms_per_token": loop_model.ms_per_token(alphas, K, 14.1, 1.8, t_verify_ms),
+            "ms_per_token_without_verify": loop_model.ms_per_token(alphas, K, 14.1, 1.8),
+            "verify_share_of_round": t_verify_ms / loop_model.round_ms(K, 14.1, 1.8, t_verify_ms)}
 
     cpu = cpu_all = None
     if not args.no_cpu:
@@ -212,6 +225,7 @@ def main():
                               "chunk_kernel_frac_of_ceiling": achieved / ceiling,
                               "value_frac_of_ceiling": gbs_step / ceiling},
         "mean_accepted": alpha_tokens,
+        "loop_model": loop,
         "roofline": {"bound": "hbm", "kernel": "chunk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes},

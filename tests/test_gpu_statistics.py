@@ -121,3 +121,17 @@ def test_first_sequences_match_oracle(run):
                              seed=w.seed)
     ref = run_oracle(sub)
     compare({k: v[:m] for k, v in out.items()}, ref, "f32", "worked_example_gpu_first")
+
+
+def test_monitor_on_library_outputs(run):
+    """The acceptance monitor fed with the library's accepted counts gives
+    0.8 at every position and the loop model's 3.3616 tokens per round."""
+    from speculative_sampling_amd import loop_model
+
+    _, out = run
+    mon = loop_model.AcceptanceMonitor(4)
+    mon.update(out["accepted"])
+    assert mon.total.errors == 0
+    assert np.all(np.abs(mon.alpha() - A) < 4 * mon.stderr())
+    pred = loop_model.expected_tokens(A, 4)
+    assert mon.tokens_per_round() == pytest.approx(pred, abs=4 * np.sqrt(loop_model.tokens_variance(A, 4) / 1e6))

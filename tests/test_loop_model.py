@@ -1,0 +1,182 @@
+"""The host-side loop model and the acceptance monitor (CPU only).
+
+Pins:
+  * roadtointelligence.com "Speculative Decoding", "How much faster": 3.36
+    tokens per target pass and a 2.8x speed-up for a = 0.8, K = 4, c = 0.05
+    (tests/golden/expected_tokens.json);
+  * fdeinterviews.com "Accelerating Large Language Model Decoding with
+    Speculative Sampling", figure "The idea, visually", panel "Latency vs K"
+    (tests/golden/loop_model_figure.json): ms per token flat from K = 3 to
+    5 at acceptance 0.75, response-time spread 48 ms at K = 2 and 106 ms at
+    K = 7;
+  * brute force: the law of tokens per round enumerated over every accept /
+    reject pattern, and the rounds-to-N moments by Monte Carlo;
+  * the monitor recovers known acceptance rates from simulated accepted
+    counts and from the oracle's outputs on the pages' worked example.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from speculative_sampling_amd import loop_model as lm
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ET = json.load(open(os.path.join(GOLDEN, "expected_tokens.json")))
+FIG = json.load(open(os.path.join(GOLDEN, "loop_model_figure.json")))
+
+
+def test_printed_tokens_and_speedup():
+    a, g, c = ET["alpha"], ET["gamma"], ET["c"]
+    assert round(lm.expected_tokens(a, g), ET["printed_decimals"]["tokens_per_pass"]) == ET["printed_tokens_per_pass"]
+    assert round(lm.speedup(a, g, c), ET["printed_decimals"]["speedup"]) == ET["printed_speedup"]
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 3, 5])
+def test_tokens_law_by_enumeration(K):
+    rng = np.random.default_rng(K)
+    a = rng.uniform(0.05, 0.95, size=K)
+    law = np.zeros(K + 1)
+    # every accept (1) / reject (0) pattern of the K positions
+    for bits in itertools.product((0, 1), repeat=K):
+        pr = np.prod([a[t] if b else 1 - a[t] for t, b in enumerate(bits)]) if K else 1.0
+        n = next((t for t, b in enumerate(bits) if not b), K)  # first rejection
+        law[n] += pr
+    np.testing.assert_allclose(lm.tokens_law(a), law, rtol=0, atol=1e-14)
+    j = np.arange(1, K + 2)
+    assert lm.expected_tokens(a) == pytest.approx(float(law @ j), abs=1e-13)
+    assert lm.tokens_variance(a) == pytest.approx(float(law @ (j * j) - (law @ j) ** 2), abs=1e-12)
+
+
+def test_closed_form_and_limits():
+    for a in (0.0, 0.3, 0.8, 0.999):
+        for K in (1, 4, 8):
+            assert lm.expected_tokens(a, K) == pytest.approx((1 - a ** (K + 1)) / (1 - a), rel=1e-12)
+    assert lm.expected_tokens(1.0, 4) == 5.0  # every draft kept, plus the bonus
+    assert lm.expected_tokens(0.0, 4) == 1.0  # one resampled token per round
+    assert lm.speedup(0.8, 4, 0.0) == pytest.approx(lm.expected_tokens(0.8, 4))
+    with pytest.raises(ValueError):
+        lm.expected_tokens(1.2, 3)
+    with pytest.raises(ValueError):
+        lm.expected_tokens([0.5, 0.5], 3)
+
+
+def test_latency_flat_from_k3_to_k5():
+    a, tt, td = FIG["alpha"], FIG["t_target_ms"], FIG["t_draft_ms"]
+    ks = range(FIG["k_range"][0], FIG["k_range"][1] + 1)
+    ms = {k: lm.ms_per_token(a, k, tt, td) for k in ks}
+    assert lm.best_k(a, tt, td, k_max=FIG["k_range"][1]) in FIG["flat_k"]
+    flat = [ms[k] for k in FIG["flat_k"]]
+    assert max(flat) / min(flat) < 1.03
+    # outside the flat stretch latency rises on both sides
+    assert ms[2] > 1.05 * min(flat) and ms[8] > 1.05 * min(flat)
+
+
+def test_response_time_spread():
+    a, tt, td = FIG["alpha"], FIG["t_target_ms"], FIG["t_draft_ms"]
+    sd2_page, sd7_page = FIG["sd_ms"]["2"], FIG["sd_ms"]["7"]
+    # the ratio does not depend on the response length
+    for n in (100, 125, 200):
+        sd2 = lm.response_time(a, 2, n, tt, td)[1]
+        sd7 = lm.response_time(a, 7, n, tt, td)[1]
+        assert sd7 / sd2 == pytest.approx(sd7_page / sd2_page, rel=0.02)
+    # the reading of the unstated length: about 125 tokens gives both values
+    assert lm.response_time(a, 2, 125, tt, td)[1] == pytest.approx(sd2_page, rel=0.03)
+    assert lm.response_time(a, 7, 125, tt, td)[1] == pytest.approx(sd7_page, rel=0.03)
+
+
+def test_rounds_moments_by_simulation():
+    rng = np.random.default_rng(7)
+    a, K, N = 0.6, 3, 40
+    law = lm.tokens_law(a, K)
+    trials = 100_000
+    rounds = np.zeros(trials, dtype=np.int64)
+    left = np.full(trials, N)
+    while np.any(left > 0):
+        live = left > 0
+        j = rng.choice(np.arange(1, K + 2), size=int(live.sum()), p=law)
+        left[live] -= j
+        rounds[live] += 1
+    mean, sd = lm.rounds_moments(a, K, N)
+    assert rounds.mean() == pytest.approx(mean, abs=4 * rounds.std() / np.sqrt(trials))
+    assert rounds.std() == pytest.approx(sd, rel=0.02)
+    assert lm.rounds_moments(a, K, 0) == (0.0, 0.0)
+    assert lm.rounds_moments(a, K, 1) == (1.0, 0.0)
+
+
+def _simulate_accepted(rng, alphas, kb):
+    """Accepted counts: position t kept with probability alphas[t], stop at the first rejection."""
+    B = len(kb)
+    keep = rng.random((B, len(alphas))) < np.asarray(alphas)[None, :]
+    n = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        row = keep[b, :kb[b]]
+        n[b] = int(np.argmin(row)) if not row.all() else kb[b]
+    return n
+
+
+def test_monitor_recovers_rates():
+    rng = np.random.default_rng(11)
+    alphas = np.array([0.9, 0.7, 0.5, 0.3])
+    mon = lm.AcceptanceMonitor(4)
+    for _ in range(5):
+        mon.update(_simulate_accepted(rng, alphas, np.full(20_000, 4)))
+    est, se = mon.alpha(), mon.stderr()
+    assert np.all(np.abs(est - alphas) < 4 * se)
+    pred = lm.expected_tokens(alphas)
+    assert mon.tokens_per_round() == pytest.approx(pred, abs=0.02)
+    assert mon.predicted_tokens_per_round() == pytest.approx(pred, abs=0.02)
+
+
+def test_monitor_ragged_rows_and_error_rows():
+    rng = np.random.default_rng(12)
+    kb = rng.integers(0, 9, size=50_000)
+    n = _simulate_accepted(rng, np.full(8, 0.6), kb)
+    n[::97] = -1  # error rows are skipped
+    mon = lm.AcceptanceMonitor(8)
+    mon.update(n, kb)
+    ok = n >= 0
+    assert mon.total.errors == int((~ok).sum())
+    assert mon.total.rounds == int(ok.sum())
+    # position t is reached only by rows with K_b > t
+    assert mon.total.reached[7] == np.count_nonzero(ok & (kb == 8) & (n >= 7))
+    est, se = mon.alpha(), mon.stderr()
+    assert np.all(np.abs(est - 0.6) < 4 * se)
+    with pytest.raises(ValueError):
+        mon.update(np.array([5]), np.array([4]))  # more accepted than drafted
+    with pytest.raises(ValueError):
+        mon.update(np.array([1]), np.array([9]))  # K_b beyond k_max
+
+
+def test_monitor_alarm_follows_a_drop():
+    rng = np.random.default_rng(13)
+    mon = lm.AcceptanceMonitor(4, decay=0.5)
+    for _ in range(10):
+        mon.update(_simulate_accepted(rng, np.full(4, 0.8), np.full(2000, 4)))
+    assert not mon.alarm(0.6)
+    for _ in range(10):  # acceptance collapses (e.g. inputs crafted to make the models disagree)
+        mon.update(_simulate_accepted(rng, np.full(4, 0.3), np.full(2000, 4)))
+    assert mon.alarm(0.6)
+    assert mon.alpha_recent()[0] < 0.4 < mon.alpha()[0]
+
+
+def test_monitor_on_the_worked_example():
+    """The oracle's accepted counts on the pages' worked example (target
+    [0.5, 0.25, 0.15, 0.10], draft [0.3, 0.4, 0.2, 0.1]): every position is
+    accepted with probability sum min(p, q) = 0.8."""
+    import oracle
+
+    WE = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    q = np.array(WE["target_q"])
+    p = np.array(WE["draft_p"])
+    B, K = 100_000, 4
+    target = np.broadcast_to(np.log(q).astype(np.float32), (B, K + 1, 4)).copy()
+    draft = np.broadcast_to(np.log(p).astype(np.float32), (B, K, 4)).copy()
+    toks = oracle.sample_rows(draft, seed=2024).astype(np.int32)
+    res = oracle.verify(target, draft, toks, seed=5)
+    mon = lm.AcceptanceMonitor(K)
+    mon.update(res["accepted"])
+    assert np.all(np.abs(mon.alpha() - WE["acceptance_sum_min"]) < 4 * mon.stderr())
+    assert mon.tokens_per_round() == pytest.approx(lm.expected_tokens(0.8, K), abs=0.03)
