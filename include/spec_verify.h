@@ -185,7 +185,8 @@ int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages);
 /* Streaming ceiling, for measurement: reads the first floor(bytes / 16384)
  * whole 16 KB blocks at data (a 16-byte aligned device pointer) once, with
  * the streaming pass's access pattern (one 16 KB block per wave, 16-byte
- * vectors, constant offsets) and no arithmetic beyond an xor fold, on the
+ * vectors, constant offsets, non-temporal loads) and no arithmetic beyond an
+ * xor fold, on the
  * given stream (NULL = the default stream), asynchronously.  out is a device
  * pointer to at least 4 bytes; it is written only when the fold hits a
  * fixed value.  Allocates nothing.  Returns SV_OK, or SV_EINVAL / SV_EHIP
