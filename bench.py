@@ -12,8 +12,9 @@ so the 256 MB Infinity Cache cannot serve repeated reads.  Draft tokens are
 drawn by the library itself (the step with K = 0 on the draft rows).
 
 Prints one JSON line: value = rows/s; roofline = algorithmic logit bytes per
-call / average time of the streaming kernel (HIP events the library records
-around its stages on the launch stream) against the 8 TB/s HBM peak;
+call / average time of the streaming kernel (HIP events the library attaches
+to that kernel's own dispatches on the launch stream) against the 8 TB/s HBM
+peak;
 streaming_ceiling = the read rate of the library's read-only probe over the
 same rotating logits; per_call_us = p10 / median / p90 of single calls;
 cpu_baseline = the fp64 oracle on a bounded sample, on one thread and on
@@ -132,8 +133,8 @@ def main():
     gbs_step = alg_bytes / (ms_per_step * 1e-3) / 1e9
 
     # the same K calls again with the library's stage events (HIP events it
-    # records on the launch stream before, between and after its two
-    # stages); kept apart because recording them lengthens each call
+    # attaches to the start and end of each stage's kernel dispatches on the
+    # launch stream); kept apart from the timed region above
     binding.spec_verify_profile_begin(v.handle, args.steps)
     for i in range(args.steps):
         step(i)

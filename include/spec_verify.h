@@ -171,9 +171,12 @@ uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 
 /* Stage timing, for measurement.  After spec_verify_profile_begin(h, n),
  * the next n calls of spec_verify_run on h record HIP events on their own
- * stream around the two stages of the first launch batch (B <= 2^16 is one
+ * stream for the two stages of the first launch batch (B <= 2^16 is one
  * batch): stage 0 is the streaming pass over the logits, stage 1 the
- * per-sequence merge, accept walk and draw.  The events are created here,
+ * per-sequence merge, accept walk and draw.  Each stage is timed from the
+ * start to the end of its kernels' own dispatches (events attached to the
+ * dispatch, so the launch gap before a kernel is not counted).  The events
+ * are created here,
  * so run still allocates nothing.  spec_verify_profile_end waits for the
  * last recorded event, writes the summed milliseconds of stage i to ms[i]
  * for i < min(n_stages, 2), releases the events and returns the number of

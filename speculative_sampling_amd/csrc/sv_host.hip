@@ -233,7 +233,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
     const int nseq = std::min(seq_per_launch, a->B - b0);
     p.b_end = b0 + nseq;
     hipEvent_t* ev = nullptr;
-    if (b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[3 * (size_t)h->prof_next++];
+    if (b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
     e = sv::launch_verify(p, cfg.dtype, vec, nseq, s, ev);
   }
   if (e == hipSuccess) e = hipEventRecord(h->last, s);
@@ -260,7 +260,7 @@ int spec_verify_profile_begin(sv_handle_t h, int max_calls) {
   if (h->has_run) (void)hipEventSynchronize(h->last);
   release_profile(h);
   hipError_t e = hipSuccess;
-  for (int i = 0; i < 3 * max_calls && e == hipSuccess; ++i) {
+  for (int i = 0; i < 4 * max_calls && e == hipSuccess; ++i) {
     hipEvent_t ev;
     e = hipEventCreate(&ev);
     if (e == hipSuccess) h->prof.push_back(ev);
@@ -281,11 +281,11 @@ int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages) {
   const int runs = h->prof_next;
   double sum[2] = {0.0, 0.0};
   hipError_t e = hipSuccess;
-  if (runs > 0) e = hipEventSynchronize(h->prof[3 * (size_t)(runs - 1) + 2]);
+  if (runs > 0) e = hipEventSynchronize(h->prof[4 * (size_t)(runs - 1) + 3]);
   for (int i = 0; i < runs && e == hipSuccess; ++i) {
     float a = 0.0f, b = 0.0f;
-    e = hipEventElapsedTime(&a, h->prof[3 * (size_t)i], h->prof[3 * (size_t)i + 1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&b, h->prof[3 * (size_t)i + 1], h->prof[3 * (size_t)i + 2]);
+    e = hipEventElapsedTime(&a, h->prof[4 * (size_t)i], h->prof[4 * (size_t)i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, h->prof[4 * (size_t)i + 2], h->prof[4 * (size_t)i + 3]);
     sum[0] += a;
     sum[1] += b;
   }

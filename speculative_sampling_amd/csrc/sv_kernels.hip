@@ -28,6 +28,7 @@
 // before the rejection step.  The pages describe no GPU kernel; everything
 // below is this library's own design for gfx950.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1864,32 +1865,33 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   write_tokens(P, b, n, d.y, st | d.flags, tid, kSeqThreads);
 }
 
+// start / stop: events recorded on the kernel's own dispatch (NULL: none).
 template <int DT, bool VEC>
-void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream) {
+void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 block(kThreads);
   switch (mode) {
-    case SV_PLAIN: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, p); break;
-    case SV_TOPK: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, p); break;
-    case SV_TOPP: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, p); break;
+    case SV_PLAIN: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPK: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPP: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, start, stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
   }
 }
 
 template <int DT, bool VEC>
 hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
-  hipError_t e = hipSuccess;
-  if (ev) e = hipEventRecord(ev[0], stream);
   // one streaming instance per sampling mode that can occur
-  for (int mode = SV_PLAIN; mode <= SV_GREEDY && e == hipSuccess; ++mode) {
-    if (!p.mode && mode != p.dmode) continue;
-    const size_t waves = (size_t)nseq * p.R * p.S;
-    launch_chunk<DT, VEC>(p, mode, dim3((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave))), stream);
-  }
-  if (ev && e == hipSuccess) e = hipEventRecord(ev[1], stream);
-  if (e == hipSuccess)
-    hipLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream, p);
-  if (ev && e == hipSuccess) e = hipEventRecord(ev[2], stream);
-  return e;
+  int modes[4];
+  int nm = 0;
+  for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode)
+    if (p.mode || mode == p.dmode) modes[nm++] = mode;
+  const size_t waves = (size_t)nseq * p.R * p.S;
+  const dim3 grid((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave)));
+  for (int i = 0; i < nm; ++i)
+    launch_chunk<DT, VEC>(p, modes[i], grid, stream, ev && i == 0 ? ev[0] : nullptr,
+                          ev && i == nm - 1 ? ev[1] : nullptr);
+  hipExtLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream,
+                        ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, p);
+  return hipSuccess;
 }
 
 }  // namespace
