@@ -921,27 +921,20 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
       int2 ent[kBatch];
       int ch[kBatch];
       // the last chunk whose list starts at or before fi: a search of fixed
-      // depth, the kBatch searches interleaved (ws.pre is non-decreasing)
+      // depth over the starts in LDS, the kBatch searches interleaved
+      // (ws.pre is non-decreasing).  It issues far fewer VALU instructions
+      // than comparing every start with every entry, which matters on the
+      // SIMD that hosts three of a sequence's rows.
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) ch[q] = 0;
-      if (nb <= 32) {
-        // count the list starts at or before fi, each start read once into
-        // a scalar register
-        for (int m = 1; m < nb; ++m) {
-          const int st = lane_at(pre, m);
+      for (int step = top; step > 0; step >>= 1) {
+        int pv[kBatch];
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) ch[q] += st <= f0 + q * kWave + lane ? 1 : 0;
-        }
-      } else {
-        for (int step = top; step > 0; step >>= 1) {
-          int pv[kBatch];
+        for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
-#pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            const int m = ch[q] + step;
-            if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
-          }
+        for (int q = 0; q < kBatch; ++q) {
+          const int m = ch[q] + step;
+          if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
         }
       }
 #pragma unroll
