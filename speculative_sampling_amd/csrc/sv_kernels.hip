@@ -325,47 +325,6 @@ __device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoads], const char* row
   }
 }
 
-// Hides the packed logits from the optimiser between passes so that each pass
-// unpacks them again instead of keeping 128 unpacked values live.
-__device__ __forceinline__ void fence_regs(uint4 (&buf)[kLoads]) {
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i)
-    asm volatile("" : "+v"(buf[i].x), "+v"(buf[i].y), "+v"(buf[i].z), "+v"(buf[i].w));
-}
-
-// Number of the chunk's elements >= cut (wave ballots).
-template <int DT>
-__device__ __forceinline__ int count_ge(uint4 (&buf)[kLoads], float cut) {
-  constexpr int VE = Fmt<DT>::VE;
-  const float c = fmaxf(cut, -kMaxFinite);  // -inf logits are never candidates
-  fence_regs(buf);
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-    for (int k = 0; k < VE; ++k) n += __popcll(__ballot(elem<DT>(buf[i], k) >= c));
-  return n;
-}
-
-// Per-lane bitmask of the vectors holding an element >= cut, and each
-// vector's largest logit (vmax[i]).
-template <int DT>
-__device__ __forceinline__ uint32_t vectors_ge(uint4 (&buf)[kLoads], float cut, float (&vmax)[kLoads]) {
-  constexpr int VE = Fmt<DT>::VE;
-  const float c = fmaxf(cut, -kMaxFinite);
-  fence_regs(buf);
-  uint32_t mask = 0;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    float m = -kInf;
-#pragma unroll
-    for (int k = 0; k < VE; ++k) m = fmaxf(m, elem<DT>(buf[i], k));
-    vmax[i] = m;
-    mask |= m >= c ? (1u << i) : 0u;
-  }
-  return mask;
-}
-
 // Exact maximum of the chunk, and whether it holds a NaN or +inf.
 template <int DT>
 __device__ __forceinline__ float chunk_max(const uint4 (&buf)[kLoads], bool* bad) {
@@ -384,24 +343,58 @@ __device__ __forceinline__ float chunk_max(const uint4 (&buf)[kLoads], bool* bad
   return wave_max(mx);
 }
 
-// Top-k window: a cut whose candidate count lies in [need, cap].  Grows the
-// window below the chunk max from d (logit units) until `need` tokens are in,
-// then bisects while the list would overflow.  +inf when none exists.
+// The largest logit of each of the lane's vectors (vmax[i]) and the chunk
+// maximum, with whether the chunk holds a NaN or +inf, in one pass.
 template <int DT>
-__device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, float d, int need, int cap) {
-  float lo = 0.0f;  // window known to hold < need tokens (or 0)
+__device__ __forceinline__ float vector_maxima(const uint4 (&buf)[kLoads], float (&vmax)[kLoads], bool* bad) {
+  constexpr int VE = Fmt<DT>::VE;
+  float mx = -kInf;
+  int nf = 0;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    float m = -kInf;
+#pragma unroll
+    for (int k = 0; k < VE; ++k) {
+      const float x = elem<DT>(buf[i], k);
+      m = fmaxf(m, x);
+      nf |= !(x < kInf);
+    }
+    vmax[i] = m;
+    mx = fmaxf(mx, m);
+  }
+  *bad = __ballot(nf) != 0;
+  return wave_max(mx);
+}
+
+// Number of the chunk's vectors whose largest logit is >= cut (wave
+// ballots over the 16 maxima of each lane).
+__device__ __forceinline__ int count_vectors_ge(const float (&vmax)[kLoads], float cut) {
+  const float c = fmaxf(cut, -kMaxFinite);  // -inf logits are never candidates
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) n += __popcll(__ballot(vmax[i] >= c));
+  return n;
+}
+
+// Top-k window: a cut such that the number of vectors holding a logit >= cut
+// lies in [need, cap].  The list holds those vectors (at most cap), and they
+// hold at least need logits >= cut.  Grows the window below the chunk max
+// from d (logit units) until `need` vectors are in, then bisects while the
+// list would overflow.  +inf when none exists.
+__device__ __forceinline__ float choose_cut(const float (&vmax)[kLoads], float mx, float d, int need, int cap) {
+  float lo = 0.0f;  // window known to hold < need vectors (or 0)
   float cut = mx - d;
-  int n = count_ge<DT>(buf, cut);
+  int n = count_vectors_ge(vmax, cut);
   for (int it = 0; n < need && it < 64; ++it) {
     lo = d;
     d *= 4.0f;
     cut = mx - d;
     if (!(cut > -kMaxFinite)) {  // the window covers every finite logit
       cut = -kInf;
-      n = count_ge<DT>(buf, cut);
+      n = count_vectors_ge(vmax, cut);
       break;
     }
-    n = count_ge<DT>(buf, cut);
+    n = count_vectors_ge(vmax, cut);
   }
   if (n <= cap) return cut;
   float hi = d;
@@ -409,7 +402,7 @@ __device__ __forceinline__ float choose_cut(uint4 (&buf)[kLoads], float mx, floa
     const float mid = 0.5f * (lo + hi);
     if (!(mid > lo && mid < hi)) break;
     const float cm = mx - mid;
-    const int nm = count_ge<DT>(buf, cm);
+    const int nm = count_vectors_ge(vmax, cm);
     if (nm < need) lo = mid;
     else if (nm > cap) hi = mid;
     else return cm;
@@ -568,7 +561,7 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
 // sequences whose sampling mode is MODE; those whose effective mode is plain
 // (top-p >= 1, top-k >= V) take the plain path.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
+__global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kernel(const KParams P) {
   constexpr int VE = Fmt<DT>::VE;
   constexpr int kWaves = kThreads / kWave;
   __shared__ float s_max[kWaves];
@@ -609,7 +602,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
   const bool special = active && (MODE == SV_TOPK || MODE == SV_GREEDY) && sp.mode == MODE;
   if (special) {
     bool bad;
-    const float mx = chunk_max<DT>(buf, &bad);
+    float vmax[kLoads];
+    const float mx = MODE == SV_TOPK ? vector_maxima<DT>(buf, vmax, &bad) : chunk_max<DT>(buf, &bad);
     rec.m = mx;
     if (bad) {
       rec.flags |= kCfNonFinite;
@@ -624,11 +618,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const KParams P) {
     } else {
       const int need = sp.topk, cap = P.cap;
       float cut = kInf;
-      // at most about 2k candidates per chunk keep the row's list short
-      if (need <= cap) cut = choose_cut<DT>(buf, mx, 2.0f, need, min(cap, max(2 * need, 64)));
+      // at most about 2k candidate vectors per chunk keep the row's list short
+      if (need <= cap) cut = choose_cut(vmax, mx, 2.0f, need, min(cap, max(2 * need, 64)));
       if (cut != kInf) {
-        float vmax[kLoads];
-        const uint32_t mask = vectors_ge<DT>(buf, cut, vmax);
+        const float c = fmaxf(cut, -kMaxFinite);
+        uint32_t mask = 0;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= c ? (1u << i) : 0u;
         const int n = list_vectors(P.cent + slot * (size_t)cap, mask, vmax, c0, VE, cap, lane);
         rec.cnt = min(n, cap);
         rec.cut = n <= cap ? cut : kInf;
