@@ -64,6 +64,19 @@ constexpr uint32_t kPurposeAccept = 0, kPurposeResample = 1, kPurposeBonus = 2;
 constexpr uint32_t kErrBits = SV_ST_TOKEN | SV_ST_NONFINITE | SV_ST_EMPTY | SV_ST_PARAM;
 
 // ------------------------------------------------------------ Philox -----
+// 2^a for |a| < 2^-14, the size of the rounding error of an fp32 product
+// such as M * c2 against its fp64 value: a Taylor polynomial in t = a ln 2,
+// whose omitted terms are below 1e-19 relative.  Larger arguments go to
+// the fp64 exp2.
+__device__ __forceinline__ double exp2_small(double a) {
+  if (fabs(a) < 6.103515625e-05) {
+    const double t = a * 0.69314718055994530942;
+    return 1.0 + t * (1.0 + t * (0.5 + t * (1.0 / 6.0)));
+  }
+  return exp2(a);
+}
+
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies whose halves are mixed with the other counter words
 // and a Weyl-sequence key.  Only word 0 of the output is used.
@@ -1080,7 +1093,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
   }
 
   const float oM = M * c2;
-  const double fM = exp2((double)oM - (double)M * (double)c2);
+  const double fM = exp2_small((double)oM - (double)M * (double)c2);
   bool list_ok = false;
   int src = 0;  // where the candidates >= the final cut lie: 1 registers, 2 LDS cache
   int n = 0, nv = 0;
@@ -1324,7 +1337,7 @@ __device__ __forceinline__ RowW row_w(const RowRec& r) {
   RowW w;
   w.c2 = (float)r.c2;
   w.oM = r.M * w.c2;
-  w.sc = (float)(exp2((double)w.oM - (double)r.M * (double)w.c2) / r.Zs);
+  w.sc = (float)(exp2_small((double)w.oM - (double)r.M * (double)w.c2) / r.Zs);
   w.T = r.T;
   return w;
 }
@@ -1351,7 +1364,7 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
   if (ls) {
     const float c2q = (float)rq.c2;
     const float oM = rq.M * c2q;
-    const double fM = exp2((double)oM - (double)rq.M * (double)c2q);
+    const double fM = exp2_small((double)oM - (double)rq.M * (double)c2q);
     const double inv = 1.0 / (rq.Zs * kFix);
 #pragma unroll
     for (int j = 0; j < E; ++j) {
