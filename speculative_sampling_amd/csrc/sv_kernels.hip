@@ -63,7 +63,6 @@ constexpr float kCandLog2 = 10.0f;
 constexpr uint32_t kPurposeAccept = 0, kPurposeResample = 1, kPurposeBonus = 2;
 constexpr uint32_t kErrBits = SV_ST_TOKEN | SV_ST_NONFINITE | SV_ST_EMPTY | SV_ST_PARAM;
 
-// ------------------------------------------------------------ Philox -----
 // 2^a for |a| < 2^-14, the size of the rounding error of an fp32 product
 // such as M * c2 against its fp64 value: a Taylor polynomial in t = a ln 2,
 // whose omitted terms are below 1e-19 relative.  Larger arguments go to
@@ -76,7 +75,7 @@ __device__ __forceinline__ double exp2_small(double a) {
   return exp2(a);
 }
 
-
+// ------------------------------------------------------------ Philox -----
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies whose halves are mixed with the other counter words
 // and a Weyl-sequence key.  Only word 0 of the output is used.
