@@ -73,7 +73,7 @@ def main():
                     help="only run --steps plain device copies of BYTES bytes (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(rows are independent; a multi-GPU run would shard B with row_offset).", file=sys.stderr)
         sys.exit(2)
 
