@@ -52,6 +52,18 @@ def test_topk_fp32_parity(sigma):
                                temperature=0.7, top_k=40, gen_seed=8, seed=6), f"topk_f32_s{sigma}")
 
 
+@pytest.mark.parametrize("k", [1, 50, 300])
+def test_topk_bf16_parity(k):
+    """bf16 top-k at the headline's vocabulary.  The streaming pass searches
+    the cut on the vectors' maxima; bf16 logits often tie at the cut (ties
+    are kept).  k = 300 exceeds a chunk's list capacity (256 vectors), so
+    every row takes the full-row selection."""
+    w, gpu, _ = check(workloads.peaked(6, 4, 128256, mode=SV_TOPK, top_k=k, gen_seed=40 + k, seed=9),
+                      f"topk_bf16_k{k}")
+    if k == 300:
+        assert np.all(gpu["row_status"][gpu["accepted"] >= 0] & ST_FULLSELECT)
+
+
 def test_greedy_fp32_parity():
     check(workloads.iid_normal(32, 8, 32000, sigma_t=3.0, sigma_d=1.0, dtype="f32", mode=SV_GREEDY,
                                temperature=0.7, gen_seed=9, seed=7), "greedy_f32")
