@@ -211,7 +211,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",  # bf16 logits decoded exactly to fp32; fp32 terms, fp64 sums
         "data": "synthetic",
         "config": {"workload": name, "B": B, "K": K, "V": V, "dtype": "bf16", "mode": "top-p",
                    "top_p": w0.default_top_p, "temperature": w0.default_temperature,
