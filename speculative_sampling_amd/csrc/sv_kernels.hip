@@ -612,9 +612,10 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
   if (active) load_chunk<DT, VEC>(buf, row, c0, c1, lane);
 
   const bool special = active && (MODE == SV_TOPK || MODE == SV_GREEDY) && sp.mode == MODE;
+  float kcut = kInf;    // top-k: this chunk's own cut (+inf: none)
+  float vmax[kLoads];   // top-k: each vector's largest logit
   if (special) {
     bool bad;
-    float vmax[kLoads];
     const float mx = MODE == SV_TOPK ? vector_maxima<DT>(buf, vmax, &bad) : chunk_max<DT>(buf, &bad);
     rec.m = mx;
     if (bad) {
@@ -629,18 +630,35 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
       rec.arg = wave_min_i(best);
     } else {
       const int need = sp.topk, cap = P.cap;
-      float cut = kInf;
       // at most about 2k candidate vectors per chunk keep the row's list short
-      if (need <= cap) cut = choose_cut(vmax, mx, 2.0f, need, min(cap, max(2 * need, 64)));
-      if (cut != kInf) {
-        const float c = fmaxf(cut, -kMaxFinite);
-        uint32_t mask = 0;
+      if (need <= cap) kcut = choose_cut(vmax, mx, 2.0f, need, min(cap, max(2 * need, 64)));
+    }
+  }
+  if constexpr (MODE == SV_TOPK) {
+    // Each chunk lists against the largest cut among this work-group's
+    // chunks of the same row: the chunk that set it holds >= k vectors at
+    // or above it, every chunk's list stays complete above it, and no list
+    // grows (the shared cut is at least the chunk's own).
+    const bool hascut = special && kcut != kInf;
+    if (lane == 0) {
+      s_key[wv] = hascut ? (int)(gw / (uint32_t)S) : -1;
+      s_max[wv] = hascut ? kcut : -kInf;
+    }
+    __syncthreads();
+    if (hascut) {
+      const int key = (int)(gw / (uint32_t)S);
+      float cut = kcut;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= c ? (1u << i) : 0u;
-        const int n = list_vectors(P.cent + slot * (size_t)cap, mask, vmax, c0, VE, cap, lane);
-        rec.cnt = min(n, cap);
-        rec.cut = n <= cap ? cut : kInf;
-      }
+      for (int w = 0; w < kWaves; ++w)
+        if (s_key[w] == key) cut = fmaxf(cut, s_max[w]);
+      const int cap = P.cap;
+      const float c = fmaxf(cut, -kMaxFinite);
+      uint32_t mask = 0;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= c ? (1u << i) : 0u;
+      const int n = list_vectors(P.cent + slot * (size_t)cap, mask, vmax, c0, VE, cap, lane);
+      rec.cnt = min(n, cap);
+      rec.cut = n <= cap ? cut : kInf;
     }
   }
   if constexpr (MODE != SV_GREEDY) {
