@@ -64,6 +64,15 @@ def test_topk_bf16_parity(k):
         assert np.all(gpu["row_status"][gpu["accepted"] >= 0] & ST_FULLSELECT)
 
 
+@pytest.mark.parametrize("V,dtype", [(20000, "f32"), (40000, "bf16")])
+def test_topk_rows_across_work_groups(V, dtype):
+    """Five chunks per row: work-groups of four chunks hold chunks of two
+    rows, and only chunks of the same row share a top-k cut."""
+    w = workloads.iid_normal(5, 3, V, sigma_t=3.0, sigma_d=1.0, dtype=dtype, mode=SV_TOPK,
+                             temperature=0.7, top_k=30, gen_seed=70, seed=13)
+    check(w, f"topk_span_{dtype}_V{V}")
+
+
 def test_greedy_fp32_parity():
     check(workloads.iid_normal(32, 8, 32000, sigma_t=3.0, sigma_d=1.0, dtype="f32", mode=SV_GREEDY,
                                temperature=0.7, gen_seed=9, seed=7), "greedy_f32")
