@@ -1494,21 +1494,23 @@ __device__ __forceinline__ void load8(const KParams& P, const char* row, int e, 
   }
 }
 
-// Weights of the 8 tokens e..e+7 (those >= hi weigh 0): q, or (q - p)+.
+// Weights of 8 tokens: q, or (q - p)+; bit k of the result is set when
+// token k weighs more than 0.  Tokens past the row end were loaded as -inf
+// and weigh 0, and a walked range never ends inside a group of 8 except at
+// the row end, so no bound test is needed.
 template <int DT>
-__device__ __forceinline__ void weights8(const RowW& wq, bool use_p, const RowW& wp, const uint4 (&rq)[2],
-                                         const uint4 (&rp)[2], int e, int hi, double (&w)[8]) {
+__device__ __forceinline__ uint32_t weights8(const RowW& wq, bool use_p, const RowW& wp, const uint4 (&rq)[2],
+                                             const uint4 (&rp)[2], double (&w)[8]) {
   constexpr int VE = Fmt<DT>::VE;
+  uint32_t pos = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float xq = elem<DT>(rq[k / VE], k % VE), xp = elem<DT>(rp[k / VE], k % VE);
-    float q = e + k < hi ? prob(wq, xq) : 0.0f;
-    if (use_p) {
-      const float pp = e + k < hi ? prob(wp, xp) : 0.0f;
-      q = q > pp ? q - pp : 0.0f;
-    }
+    float q = prob(wq, elem<DT>(rq[k / VE], k % VE));
+    if (use_p) q = fmaxf(q - prob(wp, elem<DT>(rp[k / VE], k % VE)), 0.0f);
     w[k] = (double)q;
+    pos |= q > 0.0f ? (1u << k) : 0u;
   }
+  return pos;
 }
 
 // Inverse CDF over logit rows re-read from memory by the whole work-group.
@@ -1604,14 +1606,12 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         double sl = 0.0;
         if (vi < v1) {
           double w[8];
-          weights8<DT>(wq, use_p, wp, rq[g], rp[g], lo + 8 * vi, hi, w);
+          const uint32_t pos = weights8<DT>(wq, use_p, wp, rq[g], rp[g], w);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            sl += w[k];
-            if (w[k] > 0.0) {
-              zl = min(zl, lo + 8 * vi + k);
-              zh = max(zh, lo + 8 * vi + k);
-            }
+          for (int k = 0; k < 8; ++k) sl += w[k];
+          if (pos) {
+            zl = min(zl, lo + 8 * vi + __builtin_ctz(pos));
+            zh = max(zh, lo + 8 * vi + 31 - __builtin_clz(pos));
           }
         }
         sl = wave_sum(sl);
@@ -1687,7 +1687,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         ap[0] = ap[1] = make_uint4(ninf, ninf, ninf, ninf);
         load8<DT, VEC>(P, qrow, lo + 8 * vi, aq);
         if (use_p) load8<DT, VEC>(P, prow, lo + 8 * vi, ap);
-        weights8<DT>(wq, use_p, wp, aq, ap, lo + 8 * vi, hi, w);
+        (void)weights8<DT>(wq, use_p, wp, aq, ap, w);
 #pragma unroll
         for (int k = 0; k < 8; ++k) sl += w[k];
       } else {
