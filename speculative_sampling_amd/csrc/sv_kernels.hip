@@ -940,28 +940,36 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
     ws.thr[lane] = th;
     wave_sync();
     const int nb = min(kWave, S - s0);
-    int top = 1;  // the largest power of two below nb (nb >= 2), else 0
-    while (2 * top < nb) top *= 2;
-    if (nb < 2) top = 0;
+    // The chunk of list position fi is the last non-empty chunk whose list
+    // starts at or before fi.  Non-empty chunks start at distinct positions,
+    // so with a bitmap of those starts the chunk's rank among the non-empty
+    // ones is a popcount, and a table maps the rank to the chunk.  The
+    // bitmap (ws.hm) and the table (ws.hc) borrow the histogram arrays,
+    // which every selection clears before use.
+    const bool nonempty = lane < nb && cnt > 0;
+    const uint64_t neb = __ballot(nonempty);
+    const int nne = __popcll(neb);
+    const uint64_t le = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1ull);  // lanes <= this one
+    if (nonempty) ws.hc[__popcll(neb & below)] = (uint32_t)lane;
     for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
       int2 ent[kBatch];
       int ch[kBatch];
-      // the last chunk whose list starts at or before fi: a search of fixed
-      // depth over the starts in LDS, the kBatch searches interleaved
-      // (ws.pre is non-decreasing).  It issues far fewer VALU instructions
-      // than comparing every start with every entry, which matters on the
-      // SIMD that hosts three of a sequence's rows.
+      if (lane < kBatch) ws.hm[lane] = 0ull;
+      wave_sync();
+      const int rel = pre - f0;
+      if (nonempty && rel >= 0 && rel < kBatch * kWave) atomicOr(&ws.hm[rel >> 6], 1ull << (rel & 63));
+      wave_sync();
+      int base = __popcll(__ballot(nonempty && pre < f0)) - 1;  // rank of the chunk holding f0 - 1
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) ch[q] = 0;
-      for (int step = top; step > 0; step >>= 1) {
-        int pv[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) pv[q] = ws.pre[min(ch[q] + step, nb - 1)];  // all reads in flight
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int m = ch[q] + step;
-          if (m < nb && pv[q] <= f0 + q * kWave + lane) ch[q] = m;
-        }
+      for (int q = 0; q < kBatch; ++q) {
+        const unsigned long long wq = ws.hm[q];
+        // (readfirstlane returns int: go through uint32_t, or the low word
+        // would be sign-extended)
+        const uint64_t word = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(wq >> 32)) << 32) |
+                              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wq);
+        const int r = base + __popcll(word & le);
+        ch[q] = (int)ws.hc[max(0, min(r, nne - 1))];
+        base += __popcll(word);
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
