@@ -949,7 +949,6 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
     const bool nonempty = lane < nb && cnt > 0;
     const uint64_t neb = __ballot(nonempty);
     const int nne = __popcll(neb);
-    const uint64_t le = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1ull);  // lanes <= this one
     if (nonempty) ws.hc[__popcll(neb & below)] = (uint32_t)lane;
     for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
       int2 ent[kBatch];
@@ -967,7 +966,11 @@ __device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, Rec
         // would be sign-extended)
         const uint64_t word = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(wq >> 32)) << 32) |
                               (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wq);
-        const int r = base + __popcll(word & le);
+        // set bits of the word at positions <= lane: those below it (mbcnt
+        // counts a scalar mask's bits below the lane) plus the lane's own
+        const int below_n = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
+        const int r = base + below_n + (int)((word >> lane) & 1ull);
         ch[q] = (int)ws.hc[max(0, min(r, nne - 1))];
         base += __popcll(word);
       }
