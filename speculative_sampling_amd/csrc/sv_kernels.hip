@@ -736,6 +736,8 @@ struct SmemSeq {
   int ri[kSeqWaves];
   uint32_t misc[4];
   double rx[2];
+  double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
+  double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
 };
 
 struct SelOut {
@@ -1798,13 +1800,22 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
     return;
   }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
+  const uint64_t g = P.row_offset + (uint64_t)b;
+  // With fewer rows than waves the last wave is free during the merge: it
+  // draws the walk's uniforms (they depend only on seed, sequence, position
+  // and purpose), which takes them off the path after the barrier.
+  const bool pre_u = R < kSeqWaves;
   for (int r = wv; r < R; r += kSeqWaves) merge_row<DT, VEC>(P, sp, b, r, lane, sm.w[wv], sm.rows[r]);
+  if (pre_u && wv == kSeqWaves - 1) {
+    const int t = lane;
+    if (t < Kb) sm.ua[t] = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
+    if (t <= Kb) sm.ud[t] = uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
+  }
   __syncthreads();
 
   // Wave 0: the rows' flags, the accept walk, and the draw when it needs no
   // more than the kept set in LDS.  The work-group joins only for a draw
   // from the rows.
-  const uint64_t g = P.row_offset + (uint64_t)b;
   if (wv == 0) {
     uint32_t st = 0;
     for (int t = lane; t <= Kb; t += kWave) st |= sm.rows[t].flags;
@@ -1835,17 +1846,17 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
         bool rej = false;
         uint32_t s2 = 0;
         double ud = 0.0;
+        const bool have_u = pre_u && t0 == 0;  // drawn during the merge (t < 64)
         if (t < Kb) {
           const double q = sm.rows[t].pid, p = sm.rows[KM + 1 + t].pid;
-          const double ua = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
+          const double ua = have_u ? sm.ua[t] : uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
           rej = !(ua * p < q);
           if (p == 0.0) s2 |= SV_ST_PZERO;
-          if (p > 0.0) {
-            const double ratio = q / p;
-            if (ratio < 1.0 + kWindow && fabs(ua - ratio) < kWindow) s2 |= SV_ST_MARGIN;
-          }
+          // q / p < 1 + w and |u - q / p| < w, multiplied through by p > 0
+          if (p > 0.0 && q < p * (1.0 + kWindow) && fabs(ua * p - q) < kWindow * p) s2 |= SV_ST_MARGIN;
         }
-        if (t <= Kb) ud = uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
+        if (t <= Kb)
+          ud = have_u ? sm.ud[t] : uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
         const uint64_t rb = __ballot(rej);
         const int end = rb ? t0 + __ffsll((long long)rb) - 1 : Kb;  // the walk stops here if < t0 + 64
         // status bits of the positions the walk reached (up to the first rejection)
