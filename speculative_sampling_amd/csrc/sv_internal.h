@@ -96,11 +96,12 @@ struct KParams {
 };
 
 // Enqueues the kernels of one call for sequences
-// [p.b_base, p.b_base + nseq): the streaming chunk pass (one instance per
-// sampling mode present), the row merge and the per-sequence finalize.
-// When ev is not NULL, ev[0] / ev[1] mark the start of the first and the end
-// of the last streaming instance, ev[2] / ev[3] the start and end of the
-// sequence kernel, each recorded on the kernel's own dispatch.
+// [p.b_base, p.b_base + nseq): the streaming chunk pass (the default mode's
+// instance, or the one holding every mode's path when the call gives a mode
+// per sequence), then the per-sequence merge, accept walk and draw.
+// When ev is not NULL, ev[0] / ev[1] mark the start and end of the streaming
+// kernel, ev[2] / ev[3] those of the sequence kernel, each recorded on the
+// kernel's own dispatch.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream,
                          hipEvent_t* ev = nullptr);
 // Reads the first bytes / 16384 whole 16 KB blocks of data once (see spec_verify_stream_probe).

@@ -569,15 +569,27 @@ __device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats&
   }
 }
 
+// Template mode of the streaming instance for calls with a per-sequence
+// mode array: every wave takes its own row's path, in one launch.
+constexpr int kAnyMode = 4;
+
 // Streaming pass: one wave per chunk.  The instance for MODE handles the
 // sequences whose sampling mode is MODE; those whose effective mode is plain
 // (top-p >= 1, top-k >= V) take the plain path.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kernel(const KParams P) {
+__global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3 : 1) void chunk_kernel(
+    const KParams P) {
   constexpr int VE = Fmt<DT>::VE;
   constexpr int kWaves = kThreads / kWave;
-  __shared__ float s_max[kWaves];
-  __shared__ int s_key[kWaves];
+  // which paths this instance holds
+  constexpr bool kAny = MODE == kAnyMode;
+  constexpr bool kTopk = MODE == SV_TOPK || kAny;
+  constexpr bool kGreedy = MODE == SV_GREEDY || kAny;
+  constexpr bool kTopp = MODE == SV_TOPP || kAny;
+  constexpr bool kPlain = MODE != SV_GREEDY;
+  // [0]: the top-k cut exchange, [1]: the nucleus window exchange
+  __shared__ float s_max[2][kWaves];
+  __shared__ int s_key[2][kWaves];
   const int lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int S = P.S, R = P.R;
@@ -585,8 +597,8 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
   const int b = P.b_base + (int)(gw / (uint32_t)(R * S));
   const int rem = (int)(gw % (uint32_t)(R * S));
   const int r = rem / S, c = rem % S;
-  // no early return: the nucleus instance meets at one barrier
-  bool active = b < P.b_end && raw_mode(P, b) == MODE;
+  // no early return: the work-group meets at its barriers
+  bool active = b < P.b_end && (kAny || raw_mode(P, b) == MODE);
   SeqParams sp{};
   if (active) {
     sp = load_params(P, b);
@@ -611,16 +623,17 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
   uint4 buf[kLoads];
   if (active) load_chunk<DT, VEC>(buf, row, c0, c1, lane);
 
-  const bool special = active && (MODE == SV_TOPK || MODE == SV_GREEDY) && sp.mode == MODE;
+  const bool is_topk = kTopk && active && sp.mode == SV_TOPK;  // wave-uniform
+  const bool special = is_topk || (kGreedy && active && sp.mode == SV_GREEDY);
   float kcut = kInf;    // top-k: this chunk's own cut (+inf: none)
   float vmax[kLoads];   // top-k: each vector's largest logit
   if (special) {
     bool bad;
-    const float mx = MODE == SV_TOPK ? vector_maxima<DT>(buf, vmax, &bad) : chunk_max<DT>(buf, &bad);
+    const float mx = is_topk ? vector_maxima<DT>(buf, vmax, &bad) : chunk_max<DT>(buf, &bad);
     rec.m = mx;
     if (bad) {
       rec.flags |= kCfNonFinite;
-    } else if (MODE == SV_GREEDY) {
+    } else if (!is_topk) {  // greedy
       int best = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i)
@@ -634,15 +647,15 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
       if (need <= cap) kcut = choose_cut(vmax, mx, 2.0f, need, min(cap, max(2 * need, 64)));
     }
   }
-  if constexpr (MODE == SV_TOPK) {
+  if constexpr (kTopk) {
     // Each chunk lists against the largest cut among this work-group's
     // chunks of the same row: the chunk that set it holds >= k vectors at
     // or above it, every chunk's list stays complete above it, and no list
     // grows (the shared cut is at least the chunk's own).
-    const bool hascut = special && kcut != kInf;
+    const bool hascut = is_topk && kcut != kInf;
     if (lane == 0) {
-      s_key[wv] = hascut ? (int)(gw / (uint32_t)S) : -1;
-      s_max[wv] = hascut ? kcut : -kInf;
+      s_key[0][wv] = hascut ? (int)(gw / (uint32_t)S) : -1;
+      s_max[0][wv] = hascut ? kcut : -kInf;
     }
     __syncthreads();
     if (hascut) {
@@ -650,7 +663,7 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
       float cut = kcut;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
-        if (s_key[w] == key) cut = fmaxf(cut, s_max[w]);
+        if (s_key[0][w] == key) cut = fmaxf(cut, s_max[0][w]);
       const int cap = P.cap;
       const float c = fmaxf(cut, -kMaxFinite);
       uint32_t mask = 0;
@@ -661,25 +674,25 @@ __global__ __launch_bounds__(kThreads, MODE == SV_TOPK ? 3 : 1) void chunk_kerne
       rec.cut = n <= cap ? cut : kInf;
     }
   }
-  if constexpr (MODE != SV_GREEDY) {
+  if constexpr (kPlain) {
     const bool plain = active && !special;
-    const bool cand = plain && MODE == SV_TOPP && sp.mode == SV_TOPP;
+    const bool cand = plain && kTopp && sp.mode == SV_TOPP;
     PlainStats ps;
     ps.st = 1;
     ps.ma = -1e300;
     if (plain) plain_stats<DT, VEC>(buf, c2, row, c0, c1, lane, ps);
     double g = ps.ma;
-    if constexpr (MODE == SV_TOPP) {
+    if constexpr (kTopp) {
       // the largest chunk maximum among this work-group's chunks of the same row
       if (lane == 0) {
-        s_key[wv] = cand ? (int)(gw / (uint32_t)S) : -1;
-        s_max[wv] = ps.st == 0 ? (float)ps.ma : -kInf;
+        s_key[1][wv] = cand ? (int)(gw / (uint32_t)S) : -1;
+        s_max[1][wv] = ps.st == 0 ? (float)ps.ma : -kInf;
       }
       __syncthreads();
       const int key = cand ? (int)(gw / (uint32_t)S) : -2;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
-        if (s_key[w] == key) g = fmax(g, (double)s_max[w]);
+        if (s_key[1][w] == key) g = fmax(g, (double)s_max[1][w]);
     }
     if (plain) plain_finish<DT>(P, ps, c2, cand, g, slot, c0, lane, rec);
   }
@@ -1914,22 +1927,18 @@ void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream, hip
     case SV_PLAIN: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, start, stop, 0, p); break;
     case SV_TOPK: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, start, stop, 0, p); break;
     case SV_TOPP: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, start, stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_GREEDY: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, kAnyMode>), grid, block, 0, stream, start, stop, 0, p); break;
   }
 }
 
 template <int DT, bool VEC>
 hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
-  // one streaming instance per sampling mode that can occur
-  int modes[4];
-  int nm = 0;
-  for (int mode = SV_PLAIN; mode <= SV_GREEDY; ++mode)
-    if (p.mode || mode == p.dmode) modes[nm++] = mode;
+  // one streaming instance: the default mode's, or the one holding every
+  // path when the call gives a mode per sequence
   const size_t waves = (size_t)nseq * p.R * p.S;
   const dim3 grid((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave)));
-  for (int i = 0; i < nm; ++i)
-    launch_chunk<DT, VEC>(p, modes[i], grid, stream, ev && i == 0 ? ev[0] : nullptr,
-                          ev && i == nm - 1 ? ev[1] : nullptr);
+  launch_chunk<DT, VEC>(p, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipExtLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream,
                         ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, p);
   return hipSuccess;
