@@ -83,6 +83,24 @@ def test_mixed_ragged_parity():
     assert np.all(gpu["accepted"] <= w.k_per_row.numpy())
 
 
+@pytest.mark.parametrize("V,dtype", [(40000, "bf16"), (20000, "f32")])
+def test_every_mode_in_one_call(V, dtype):
+    """A mode per sequence runs one streaming instance holding every path:
+    greedy, top-k, nucleus and plain rows, and rows whose top-k covers the
+    vocabulary or whose top-p is 1 (plain), side by side in one call, with
+    per-row temperatures and ragged K."""
+    B, K = 18, 4
+    w = workloads.iid_normal(B, K, V, sigma_t=3.0, sigma_d=1.0, dtype=dtype, gen_seed=90, seed=15)
+    g = torch.Generator().manual_seed(91)
+    w.mode = torch.tensor([SV_GREEDY, SV_TOPK, SV_TOPP, SV_PLAIN, SV_TOPK, SV_TOPP] * 3, dtype=torch.uint8)
+    w.top_k = torch.tensor([1, 40, 1, 1, V, 1] * 3, dtype=torch.int32)
+    w.top_p = torch.tensor([1.0, 1.0, 0.8, 1.0, 1.0, 1.0] * 3, dtype=torch.float32)
+    w.temperature = (0.5 + torch.rand(B, generator=g)).to(torch.float32)
+    w.k_per_row = torch.randint(0, K + 1, (B,), generator=g).to(torch.int32)
+    _, gpu, _ = check(w, f"every_mode_{dtype}")
+    assert np.all(gpu["accepted"] <= w.k_per_row.numpy())
+
+
 @pytest.mark.parametrize("V,dtype", [(1001, "bf16"), (999, "f32"), (1, "bf16"), (7, "f32")])
 def test_unaligned_vocab_parity(V, dtype):
     # rows that are not a multiple of 16 bytes take the element-wise load path
