@@ -135,3 +135,63 @@ def test_monitor_on_library_outputs(run):
     assert np.all(np.abs(mon.alpha() - A) < 4 * mon.stderr())
     pred = loop_model.expected_tokens(A, 4)
     assert mon.tokens_per_round() == pytest.approx(pred, abs=4 * np.sqrt(loop_model.tokens_variance(A, 4) / 1e6))
+
+
+def test_non_iid_rounds_expected_tokens_and_first_token_law():
+    """100,000 rounds shaped like batch-1 serving (K = 4, V = 32000 bf16,
+    target N(0, 3^2), draft = target + N(0, 1), plain sampling at
+    temperature 1), batched 10,000 rounds per call.  The acceptance rate
+    differs from round to round, so:
+      * given the logits, a round emits n + 1 tokens with
+        E = 1 + sum_k prod_{t<k} a_t, a_t = sum_v min(p_t(v), q_t(v))
+        (roadtointelligence.com "How much faster", per position), and the
+        law of n + 1 gives its variance: sum(n + 1 - E) is tested as a
+        normal z-score;
+      * the first emitted token follows q_0 whatever happens at position 0
+        (the paperlayer.ai summary's Theorem 1): its randomised PIT
+        F(y - 1) + V q(y), V ~ U(0, 1), is uniform (Kolmogorov-Smirnov).
+    The expectations are computed in fp64 from the same bf16 logits."""
+    from speculative_sampling_amd import loop_model
+
+    dev = torch.device("cuda", 0)
+    B, K, V, batches = 10_000, 4, 32000, 10
+    gen_v = torch.Generator(device=dev).manual_seed(2468)
+    dev_sum, var_sum = 0.0, 0.0
+    pits = []
+    for i in range(batches):
+        print(f"[non_iid_rounds] batch {i}", flush=True)
+        w = workloads.iid_normal(B, K, V, sigma_t=3.0, sigma_d=1.0, gen_seed=3000 + i, seed=4000 + i,
+                                 device=dev)
+        sampler = Verifier(B * K, 0, V, torch.bfloat16)
+        toks, st = sampler.sample(w.draft.reshape(-1, V), seed=w.draft_seed)
+        torch.cuda.synchronize()
+        sampler.close()
+        assert int(((st & ST_ERRORS) != 0).sum()) == 0
+        w.draft_tokens = toks.reshape(B, K).to(torch.int32).contiguous()
+        out = run_gpu(w)
+        assert int(((out["row_status"] & ST_ERRORS) != 0).sum()) == 0
+        # per-round acceptance rates in fp64
+        alpha = torch.empty(B, K, dtype=torch.float64, device=dev)
+        for t in range(K):
+            q = torch.softmax(w.target[:, t].double(), dim=-1)
+            p = torch.softmax(w.draft[:, t].double(), dim=-1)
+            alpha[:, t] = torch.minimum(p, q).sum(-1)
+            del p
+            if t == 0:
+                y0 = torch.from_numpy(out["out_tokens"][:, 0]).to(dev).long()
+                qy = q.gather(1, y0[:, None])[:, 0]
+                before = q.cumsum(-1).gather(1, y0[:, None])[:, 0] - qy
+                u = before + torch.rand(B, generator=gen_v, device=dev, dtype=torch.float64) * qy
+                pits.append(u.clamp(0.0, 1.0).cpu().numpy())
+            del q
+        a = alpha.cpu().numpy()
+        n1 = out["accepted"].astype(np.float64) + 1.0
+        exp = np.array([loop_model.expected_tokens(a[b]) for b in range(B)])
+        var = np.array([loop_model.tokens_variance(a[b]) for b in range(B)])
+        dev_sum += float(np.sum(n1 - exp))
+        var_sum += float(np.sum(var))
+    z = dev_sum / np.sqrt(var_sum)
+    assert abs(z) < 4.5, f"z = {z:.2f}"
+    ks = stats.kstest(np.concatenate(pits), "uniform")
+    assert ks.pvalue > 1e-3, f"KS p = {ks.pvalue:.2e}"
+    print(f"[non_iid_rounds] z = {z:.2f}, KS p = {ks.pvalue:.3f}", flush=True)

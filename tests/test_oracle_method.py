@@ -228,6 +228,14 @@ def test_non_iid_expected_tokens_per_round():
     var = (pmf * (ks + 1) ** 2).sum(1) - mean ** 2
     z = ((res["accepted"] + 1) - mean).sum() / np.sqrt(var.sum())
     assert abs(z) < 4
+    # the first emitted token follows q_0 (the paperlayer.ai summary's
+    # Theorem 1): its randomised PIT F(y - 1) + U q(y) is U(0, 1)
+    q0 = q[:, 0].numpy()
+    y0 = res["out_tokens"][:, 0].astype(np.int64)
+    qy = q0[np.arange(B), y0]
+    below = np.cumsum(q0, axis=1)[np.arange(B), y0] - qy
+    pit = np.clip(below + rng.random(B) * qy, 0.0, 1.0)
+    assert stats.kstest(pit, "uniform").pvalue > 1e-3
     # the accept loop saw exactly these probabilities
     np.testing.assert_allclose(res["diag"][:, :, 0],
                                np.take_along_axis(q.numpy(), toks[..., None], -1)[..., 0], rtol=1e-12)
