@@ -3,8 +3,8 @@
 // create  allocates the device workspace once (chunk records, candidate
 //         vector lists, kept lists);
 // run     validates on the host, then enqueues the kernels of the step for
-//         batches of at most kMaxBlocksPerLaunch work-groups on the caller's
-//         stream;
+//         batches of at most kMaxSeqPerLaunch sequences and kMaxWavesPerLaunch
+//         streaming waves on the caller's stream;
 // destroy waits for the last run and frees.
 
 #include <hip/hip_runtime.h>
@@ -38,8 +38,12 @@ struct sv_handle_s {
 namespace {
 
 thread_local std::string g_last_error;
-// Work-groups per launch: keeps the grid's work-item count below 2^32.
-constexpr size_t kMaxBlocksPerLaunch = (size_t)1 << 23;
+// A dispatch counts its work-items in 32 bits.  Per launch: at most 2^23
+// streaming waves (2^29 work-items) and 2^22 sequences (2^22 work-groups of
+// kSeqWaves waves: 3.2e9 work-items).
+constexpr size_t kMaxWavesPerLaunch = (size_t)1 << 23;
+constexpr size_t kMaxSeqPerLaunch = (size_t)1 << 22;
+static_assert(kMaxSeqPerLaunch * sv::kSeqWaves * 64 < ((size_t)1 << 32), "sequence grid");
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
@@ -226,7 +230,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
     return fail(SV_EHIP, "hipSetDevice failed");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t per_seq = (size_t)p.R * p.S;
-  const int seq_per_launch = (int)std::max<size_t>(1, kMaxBlocksPerLaunch / per_seq);
+  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxWavesPerLaunch / per_seq));
   hipError_t e = hipSuccess;
   for (int b0 = 0; b0 < a->B && e == hipSuccess; b0 += seq_per_launch) {
     p.b_base = b0;

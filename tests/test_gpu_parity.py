@@ -222,6 +222,31 @@ def test_gpu_sampler_matches_oracle_sampler():
     assert np.array_equal(g[ok.numpy()], o_toks[ok.numpy()])
 
 
+def test_sampler_over_several_launches():
+    """6,000,000 single-row draws (K = 0, V = 4, fp32): more sequences than
+    one launch of the sequence kernel takes (2^22, so that its grid stays
+    below 2^32 work-items), so the call is split in two.  Rows on both sides
+    of the split and at the ends match the oracle's sampler exactly."""
+    import oracle
+    dev = torch.device("cuda", 0)
+    n, V = 6_000_000, 4
+    g = torch.Generator().manual_seed(404)
+    rows = torch.randn(n, V, generator=g) * 2.0
+    v = Verifier(n, 0, V, torch.float32)
+    print(f"[sampler_split] rows={n} V={V}", flush=True)
+    toks, st = v.sample(rows.to(dev), seed=55)
+    torch.cuda.synchronize()
+    v.close()
+    toks, st = toks.cpu().numpy(), st.cpu().numpy()
+    assert int(((st & ST_ERRORS) != 0).sum()) == 0
+    assert toks.min() >= 0 and toks.max() < V
+    x = rows.numpy()
+    split = 1 << 22
+    for lo, hi in ((0, 300), (split - 300, split + 300), (n - 300, n)):
+        ref = oracle.sample_rows(x[lo:hi], seed=55, row_offset=lo)
+        assert np.array_equal(toks[lo:hi], ref), (lo, hi)
+
+
 def test_headline_shape_sampled_rows():
     # B=64, K=4, V=128256 bf16 nucleus: whole batch on the GPU, the oracle on
     # a sample of sequences (same global row ids via row_offset)
