@@ -111,6 +111,43 @@ def test_unaligned_vocab_parity(V, dtype):
                                seed=11), f"topk_V{V}")
 
 
+@pytest.mark.parametrize("mode", [SV_PLAIN, SV_TOPP, SV_TOPK])
+def test_maximum_draft_length(mode):
+    # K = 64, the largest the library accepts: 129 rows per sequence, several
+    # rows per wave of the sequence kernel, kept sets in global memory
+    check(workloads.iid_normal(3, 64, 3000, sigma_d=0.3, mode=mode, temperature=0.9, top_p=0.8,
+                               top_k=20, gen_seed=40, seed=41), f"k64_{mode}")
+    # identical models accept all 64 drafts and draw the bonus from q_64
+    w, gpu, _ = check(workloads.iid_normal(3, 64, 3000, sigma_d=0.0, mode=mode, temperature=0.9,
+                                           top_p=0.8, top_k=20, gen_seed=46, seed=47), f"k64_same_{mode}")
+    assert np.all(gpu["accepted"] == 64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_vocab(dtype):
+    # V = 2^22, the largest the library accepts: 512 (bf16) or 1024 (fp32)
+    # chunks per row, tile sums beyond the LDS cache in the row draw
+    V = 1 << 22
+    check(workloads.iid_normal(2, 2, V, dtype=dtype, gen_seed=42, seed=43), f"vmax_plain_{dtype}")
+    check(workloads.iid_normal(2, 2, V, dtype=dtype, mode=SV_TOPP, temperature=0.5, top_p=0.9,
+                               gen_seed=42, seed=43), f"vmax_topp_{dtype}")
+    check(workloads.iid_normal(2, 2, V, dtype=dtype, mode=SV_TOPK, temperature=0.7, top_k=50,
+                               gen_seed=42, seed=43), f"vmax_topk_{dtype}")
+
+
+def test_empty_batch():
+    # B = 0 launches nothing and returns success
+    dev = torch.device("cuda", 0)
+    v = Verifier(4, 3, 1000, torch.bfloat16)
+    tgt = torch.zeros(0, 4, 1000, dtype=torch.bfloat16, device=dev)
+    drf = torch.zeros(0, 3, 1000, dtype=torch.bfloat16, device=dev)
+    toks = torch.zeros(0, 3, dtype=torch.int32, device=dev)
+    acc, out, st, _ = v(tgt, drf, toks, seed=1)
+    torch.cuda.synchronize()
+    v.close()
+    assert acc.numel() == 0 and out.shape == (0, 4) and st.numel() == 0
+
+
 def test_k0_is_a_single_draw():
     w = workloads.iid_normal(64, 0, 5000, gen_seed=14, seed=12)
     check(w, "k0")
