@@ -1520,23 +1520,39 @@ __device__ __forceinline__ void load8(const KParams& P, const char* row, int e, 
   }
 }
 
-// Weights of 8 tokens: q, or (q - p)+; bit k of the result is set when
-// token k weighs more than 0.  Tokens past the row end were loaded as -inf
-// and weigh 0, and a walked range never ends inside a group of 8 except at
-// the row end, so no bound test is needed.
+// prob() for a row that keeps every token (threshold -inf): the kept-set
+// test always passes, since a row a draw reads holds no NaN (a NaN makes the
+// sequence an error row before any draw), and -inf still weighs 0.
+__device__ __forceinline__ float prob_all(const RowW& w, float x) {
+  return __builtin_amdgcn_exp2f(fmaf(x, w.c2, -w.oM)) * w.sc;
+}
+
+// Weights of 8 tokens in fp32: q, or (q - p)+; returns their sum, added
+// pairwise in fp32 (both passes of a row draw use this same group sum).
+// Tokens past the row end were loaded as -inf and weigh 0, and a walked
+// range never ends inside a group of 8 except at the row end, so no bound
+// test is needed.  `all` (wave-uniform): every row read keeps every token,
+// so the threshold test is left out.
 template <int DT>
-__device__ __forceinline__ uint32_t weights8(const RowW& wq, bool use_p, const RowW& wp, const uint4 (&rq)[2],
-                                             const uint4 (&rp)[2], double (&w)[8]) {
+__device__ __forceinline__ float weights8(const RowW& wq, bool use_p, const RowW& wp, bool all,
+                                          const uint4 (&rq)[2], const uint4 (&rp)[2], float (&w)[8]) {
   constexpr int VE = Fmt<DT>::VE;
-  uint32_t pos = 0;
+  if (all) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float q = prob(wq, elem<DT>(rq[k / VE], k % VE));
-    if (use_p) q = fmaxf(q - prob(wp, elem<DT>(rp[k / VE], k % VE)), 0.0f);
-    w[k] = (double)q;
-    pos |= q > 0.0f ? (1u << k) : 0u;
+    for (int k = 0; k < 8; ++k) {
+      float q = prob_all(wq, elem<DT>(rq[k / VE], k % VE));
+      if (use_p) q = fmaxf(q - prob_all(wp, elem<DT>(rp[k / VE], k % VE)), 0.0f);
+      w[k] = q;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float q = prob(wq, elem<DT>(rq[k / VE], k % VE));
+      if (use_p) q = fmaxf(q - prob(wp, elem<DT>(rp[k / VE], k % VE)), 0.0f);
+      w[k] = q;
+    }
   }
-  return pos;
+  return ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
 }
 
 // Inverse CDF over logit rows re-read from memory by the whole work-group.
@@ -1555,6 +1571,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   d.y = 0;
   const RowW wq = row_w(rq), wp = row_w(rp);
   bool use_p = resample;
+  const bool all = __builtin_amdgcn_readfirstlane((int)(wq.T == -kInf && (!resample || wp.T == -kInf))) != 0;
   int lo = 0, hi = P.V;
   double base = 0.0;  // weight before lo (chunk-located draws)
   bool located = false, force_last = false;
@@ -1631,13 +1648,14 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         const int vi = t0 + g * kWave + lane;
         double sl = 0.0;
         if (vi < v1) {
-          double w[8];
-          const uint32_t pos = weights8<DT>(wq, use_p, wp, rq[g], rp[g], w);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) sl += w[k];
-          if (pos) {
-            zl = min(zl, lo + 8 * vi + __builtin_ctz(pos));
-            zh = max(zh, lo + 8 * vi + 31 - __builtin_clz(pos));
+          float w[8];
+          const float s8 = weights8<DT>(wq, use_p, wp, all, rq[g], rp[g], w);
+          sl = (double)s8;
+          // the first and last groups of 8 with weight (refined to a token
+          // only where that is needed)
+          if (s8 > 0.0f) {
+            zl = min(zl, lo + 8 * vi);
+            zh = max(zh, lo + 8 * vi + 7);
           }
         }
         sl = wave_sum(sl);
@@ -1713,9 +1731,10 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         ap[0] = ap[1] = make_uint4(ninf, ninf, ninf, ninf);
         load8<DT, VEC>(P, qrow, lo + 8 * vi, aq);
         if (use_p) load8<DT, VEC>(P, prow, lo + 8 * vi, ap);
-        (void)weights8<DT>(wq, use_p, wp, aq, ap, w);
+        float wf[8];
+        sl = (double)weights8<DT>(wq, use_p, wp, all, aq, ap, wf);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sl += w[k];
+        for (int k = 0; k < 8; ++k) w[k] = (double)wf[k];
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) w[k] = 0.0;
@@ -1759,8 +1778,22 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     chi = sm.rx[1];
   }
   __syncthreads();
-  if (y < 0) {  // rounding left no token above the target
-    y = nzhi < 0 ? 0 : nzhi;
+  if (y < 0) {  // rounding left no token above the target: the last token with weight
+    y = 0;
+    if (nzhi >= 0) {
+      const int g0 = nzhi - 7;  // the last group of 8 with weight
+      uint4 aq[2], ap[2];
+      const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+      ap[0] = ap[1] = make_uint4(ninf, ninf, ninf, ninf);
+      load8<DT, VEC>(P, qrow, g0, aq);
+      if (use_p) load8<DT, VEC>(P, prow, g0, ap);
+      float wf[8];
+      (void)weights8<DT>(wq, use_p, wp, all, aq, ap, wf);
+      y = g0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (wf[k] > 0.0f) y = g0 + k;
+    }
     clo = chi = S;
   }
   d.y = y;

@@ -33,7 +33,10 @@ def test_worked_example_parity():
 
 
 def test_plain_bf16_parity():
-    check(workloads.iid_normal(48, 4, 32000, sigma_t=3.0, sigma_d=1.0, gen_seed=5, seed=3), "plain_bf16")
+    _, gpu, _ = check(workloads.iid_normal(48, 4, 32000, sigma_t=3.0, sigma_d=1.0, gen_seed=5, seed=3),
+                      "plain_bf16")
+    # plain draws read the rows again (every token kept: no threshold test)
+    assert np.all(gpu["row_status"] & ST_REREAD)
 
 
 def test_plain_fp32_parity():
@@ -165,7 +168,11 @@ def test_edge_parameters():
                                default_mode=mode, default_temperature=0.9, seed=13, draft_seed=99, **kw)
         # at top_p = 0.999 the tail tokens' masses are far below 1e-6, so the
         # cut always lies within 1e-6 of top_p: every row is flagged
-        check(w, f"edge_{mode}_{kw}", rate_bound=kw.get("default_top_p") != 0.999)
+        _, gpu, _ = check(w, f"edge_{mode}_{kw}", rate_bound=kw.get("default_top_p") != 0.999)
+        if kw.get("default_top_k") == 700:
+            # kept sets beyond the 512-entry list: drawn from the re-read rows
+            # with the kept-set threshold applied per token
+            assert np.any(gpu["row_status"] & ST_REREAD)
     flat = torch.zeros(B, K + 1, V, dtype=torch.bfloat16)
     flat[:, :, ::7] = 1.0   # big tied groups
     w = workloads.Workload("ties", B, K, V, "bf16", flat, flat[:, :K].clone(), default_mode=SV_TOPP,
