@@ -576,6 +576,21 @@ constexpr int kAnyMode = 4;
 // Streaming pass: one wave per chunk.  The instance for MODE handles the
 // sequences whose sampling mode is MODE; those whose effective mode is plain
 // (top-p >= 1, top-k >= V) take the plain path.
+// Work-groups are handed to the 8 XCDs in turn (work-group j to XCD
+// j mod 8), and the sequence kernel's work-group b runs on XCD b mod 8.
+// When every sequence spans a whole number Q of streaming work-groups and
+// the launch holds a multiple of 8 sequences, hardware work-group j takes
+// the logical work-group that keeps all of sequence b's chunks on XCD
+// b mod 8 as well (a permutation of [0, 8 Q n)); otherwise the identity.
+__device__ __forceinline__ uint32_t xcd_logical_wg(uint32_t j, int nseq, int rs) {
+  constexpr uint32_t kXcd = 8;
+  constexpr int wpg = kThreads / kWave;  // waves (chunks) per streaming work-group
+  if (rs % wpg != 0 || nseq % (int)kXcd != 0) return j;
+  const uint32_t Q = (uint32_t)(rs / wpg);
+  const uint32_t x = j % kXcd, k = j / kXcd;
+  return (x + kXcd * (k / Q)) * Q + k % Q;
+}
+
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3 : 1) void chunk_kernel(
     const KParams P) {
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3
   const int lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int S = P.S, R = P.R;
-  const uint32_t gw = blockIdx.x * (uint32_t)kWaves + (uint32_t)wv;
+  const uint32_t gw = xcd_logical_wg(blockIdx.x, P.b_end - P.b_base, R * S) * (uint32_t)kWaves + (uint32_t)wv;
   const int b = P.b_base + (int)(gw / (uint32_t)(R * S));
   const int rem = (int)(gw % (uint32_t)(R * S));
   const int r = rem / S, c = rem % S;
