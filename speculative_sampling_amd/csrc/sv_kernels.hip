@@ -725,7 +725,8 @@ __global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3
 // resampled or bonus token.
 
 constexpr int kSeqThreads = kSeqWaves * kWave;
-constexpr int kRowCache = 768;  // candidate logits of one row held in LDS
+constexpr int kRowCache = 768;
+constexpr int kDrawTiles = 8;  // tiles of a row draw whose loads are in flight together  // candidate logits of one row held in LDS
 constexpr int kVecList = 768;   // candidate vectors of one row that pass the row's cut
 constexpr int kMaxRows = 2 * kMaxK + 1;
 
@@ -1644,11 +1645,11 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     v1 = min(n8, v0 + per);
     double seg = 0.0;
     int zl = 0x7fffffff, zh = -1, nt = 0;
-    for (int t0 = v0; t0 < v1; t0 += 4 * kWave) {
+    for (int t0 = v0; t0 < v1; t0 += kDrawTiles * kWave) {
       // the loads of 4 tiles are in flight together
-      uint4 rq[4][2], rp[4][2];
+      uint4 rq[kDrawTiles][2], rp[kDrawTiles][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kDrawTiles; ++g) {
         const int vi = t0 + g * kWave + lane;
         const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
         rq[g][0] = rq[g][1] = rp[g][0] = rp[g][1] = make_uint4(ninf, ninf, ninf, ninf);
@@ -1658,7 +1659,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         }
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kDrawTiles; ++g) {
         if (t0 + g * kWave >= v1) break;
         const int vi = t0 + g * kWave + lane;
         double sl = 0.0;
