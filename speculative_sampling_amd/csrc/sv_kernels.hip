@@ -1594,8 +1594,9 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   if (!resample && qrec && rq.T == -kInf) {
     // plain bonus draw: the chunk sums give the chunk holding u
     const int S = P.S;
+    // two chunks per thread cover every row: V <= 2^22 is at most 1024 chunks
+    static_assert(2 * kSeqThreads >= kMaxVocab / (64 * kLoads * 4), "chunk sums per thread");
     double wc[2];
-    int cnt = 0;
     for (int j = 0; j < 2; ++j) {
       const int c = 2 * tid + j;
       wc[j] = 0.0;
@@ -1604,7 +1605,6 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         if (r.m > -kInf) wc[j] = r.z * exp2(((double)r.m - (double)rq.M) * (double)wq.c2) / rq.Zs;
       }
     }
-    (void)cnt;
     double tot;
     const double ex = seq_exclusive_scan(wc[0] + wc[1], &tot, sm);
     int cstar = 0x7fffffff, clast = -1;
@@ -1817,7 +1817,6 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   const double plo = located ? base + clo : clo / S, phi = located ? base + chi : chi / S;
   if (nzlo < y && u - plo < kWindow) d.flags |= SV_ST_MARGIN;
   if (nzhi > y && phi - u < kWindow) d.flags |= SV_ST_MARGIN;
-  (void)tid;
   return d;
 }
 
