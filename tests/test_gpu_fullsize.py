@@ -5,7 +5,7 @@ with row_offset set to its index, so its random numbers are those the GPU
 used for that sequence.
 
   * B=256, K=8, V=32000 fp32, top-k 40 at temperature 0.7, draft noise
-    sigma 1.0, and its greedy variant;
+    sigma 0.3, 1.0 and 2.0, and the greedy variant at sigma 1.0;
   * B=512, ragged K_b ~ U{1..8}, V=256000 bf16, Zipf-shaped logits with a
     per-row vocabulary permutation, modes cycling plain / top-k 50 /
     top-p 0.9 at temperature 0.7;
@@ -39,11 +39,15 @@ def check_sampled(w, picks, label):
     return gpu
 
 
-def test_topk_fp32_full():
+@pytest.mark.parametrize("sigma", ["0.3", "1.0", "2.0"])
+def test_topk_fp32_full(sigma):
+    # draft noise sigma 0.3 / 1.0 / 2.0: acceptance from high to low
     dev = torch.device("cuda", 0)
-    w = workloads.config("topk_f32_s1.0", device=dev, gen_seed=31, seed=3)
-    gpu = check_sampled(w, (0, 97, 255), "topk_f32_full")
+    w = workloads.config(f"topk_f32_s{sigma}", device=dev, gen_seed=31, seed=3)
+    gpu = check_sampled(w, (0, 97, 255), f"topk_f32_s{sigma}_full")
     assert np.all(gpu["row_status"] & ST_ERRORS == 0)
+    del w
+    torch.cuda.empty_cache()
 
 
 def test_greedy_fp32_full():
