@@ -153,11 +153,18 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg);
  * spec_verify_validate) and returns a negative code without launching
  * anything if they are invalid.  Data errors found on the device are
  * reported per sequence through row_status.  No allocation, no host
- * synchronisation. */
+ * synchronisation.  The call may be captured into a HIP graph (stream
+ * capture): its kernels become graph nodes that read the argument pointers
+ * given at capture, so each replay uses the data then in those buffers, and
+ * replays must not overlap other runs of the same handle.  Stage profiling
+ * is skipped under capture. */
 int spec_verify_run(sv_handle_t h, const sv_args* args, void* stream);
 
-/* Waits for the last run enqueued through h, then frees its workspace and
- * the handle.  NULL is accepted. */
+/* Waits for the last run enqueued through h (for a handle some run of which
+ * was captured into a graph: for the whole device, since graph launches are
+ * not tracked), then frees its workspace and the handle.  A graph holding a
+ * captured run must not be launched after its handle is destroyed.  NULL is
+ * accepted. */
 int spec_verify_destroy(sv_handle_t h);
 
 /* Host-only check of a (config, args) pair: pointer presence, sizes

@@ -30,6 +30,7 @@ struct sv_handle_s {
   sv::KeptEntry* kept;
   hipEvent_t last;
   bool has_run;
+  bool in_graph;  // some run was captured into a graph: destroy waits for the device
   // stage timing (spec_verify_profile_begin / _end)
   std::vector<hipEvent_t> prof;
   int prof_max, prof_next;
@@ -175,6 +176,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     return fail(SV_EHIP, std::string("workspace initialisation failed: ") + hipGetErrorString(e));
   }
   h->has_run = false;
+  h->in_graph = false;
   h->prof_max = h->prof_next = 0;
   (void)hipSetDevice(prev);
   *out = h;
@@ -229,6 +231,11 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   if (prev != cfg.device && hipSetDevice(cfg.device) != hipSuccess)
     return fail(SV_EHIP, "hipSetDevice failed");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Under stream capture the kernels become graph nodes; stage events and the
+  // completion event are left out (the graph's launches are the caller's).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
+  const bool capturing = cap != hipStreamCaptureStatusNone;
   const size_t per_seq = (size_t)p.R * p.S;
   const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxWavesPerLaunch / per_seq));
   hipError_t e = hipSuccess;
@@ -237,11 +244,12 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
     const int nseq = std::min(seq_per_launch, a->B - b0);
     p.b_end = b0 + nseq;
     hipEvent_t* ev = nullptr;
-    if (b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
+    if (!capturing && b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
     e = sv::launch_verify(p, cfg.dtype, vec, nseq, s, ev);
   }
-  if (e == hipSuccess) e = hipEventRecord(h->last, s);
-  if (e == hipSuccess) h->has_run = true;
+  if (e == hipSuccess && capturing) h->in_graph = true;
+  if (e == hipSuccess && !capturing) e = hipEventRecord(h->last, s);
+  if (e == hipSuccess && !capturing) h->has_run = true;
   if (prev != cfg.device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(SV_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return SV_OK;
@@ -313,7 +321,8 @@ int spec_verify_destroy(sv_handle_t h) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->cfg.device);
   hipError_t e = hipSuccess;
-  if (h->has_run) e = hipEventSynchronize(h->last);
+  if (h->in_graph) e = hipDeviceSynchronize();  // graph launches are not tracked by the handle
+  else if (h->has_run) e = hipEventSynchronize(h->last);
   (void)hipEventDestroy(h->last);
   release_profile(h);
   (void)hipFree(h->ws);
