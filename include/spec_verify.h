@@ -160,11 +160,11 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg);
  * is skipped under capture. */
 int spec_verify_run(sv_handle_t h, const sv_args* args, void* stream);
 
-/* Waits for the last run enqueued through h (for a handle some run of which
- * was captured into a graph: for the whole device, since graph launches are
- * not tracked), then frees its workspace and the handle.  A graph holding a
- * captured run must not be launched after its handle is destroyed.  NULL is
- * accepted. */
+/* If any run was enqueued or captured through h, waits for the device to
+ * finish all queued work (which includes every such run and any launch of a
+ * graph holding one), then frees the workspace and the handle.  A graph
+ * holding a captured run must not be launched after its handle is
+ * destroyed.  NULL is accepted. */
 int spec_verify_destroy(sv_handle_t h);
 
 /* Host-only check of a (config, args) pair: pointer presence, sizes
@@ -178,13 +178,13 @@ uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 
 /* Stage timing, for measurement.  After spec_verify_profile_begin(h, n),
  * the next n calls of spec_verify_run on h record HIP events on their own
- * stream for the two stages of the first launch batch (B <= 2^16 is one
- * batch): stage 0 is the streaming pass over the logits, stage 1 the
- * per-sequence merge, accept walk and draw.  Each stage is timed from the
- * start to the end of its kernels' own dispatches (events attached to the
- * dispatch, so the launch gap before a kernel is not counted).  The events
- * are created here,
- * so run still allocates nothing.  spec_verify_profile_end waits for the
+ * stream for the two stages of the first launch batch (a call is one batch
+ * unless it exceeds 2^23 streaming waves or 2^22 sequences): stage 0 is the
+ * streaming pass over the logits, stage 1 the per-sequence merge, accept
+ * walk and draw.  Each stage is timed from the start to the end of its
+ * kernels' own dispatches (events attached to the dispatch, so the launch
+ * gap before a kernel is not counted).  The events are created here, so run
+ * still allocates nothing; runs under stream capture record none.  spec_verify_profile_end waits for the
  * last recorded event, writes the summed milliseconds of stage i to ms[i]
  * for i < min(n_stages, 2), releases the events and returns the number of
  * calls recorded (negative code on error).  Calling begin again discards an

@@ -5,7 +5,7 @@
 // run     validates on the host, then enqueues the kernels of the step for
 //         batches of at most kMaxSeqPerLaunch sequences and kMaxWavesPerLaunch
 //         streaming waves on the caller's stream;
-// destroy waits for the last run and frees.
+// destroy synchronises the device if the handle has run, then frees.
 
 #include <hip/hip_runtime.h>
 
@@ -28,9 +28,7 @@ struct sv_handle_s {
   sv::ChunkRec* chunks;
   int2* cent;
   sv::KeptEntry* kept;
-  hipEvent_t last;
-  bool has_run;
-  bool in_graph;  // some run was captured into a graph: destroy waits for the device
+  bool has_run;  // some run was enqueued (or captured): destroy waits for the device
   // stage timing (spec_verify_profile_begin / _end)
   std::vector<hipEvent_t> prof;
   int prof_max, prof_next;
@@ -167,8 +165,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
   h->cent = reinterpret_cast<int2*>(base + g.off_cent);
   h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
-  e = hipEventCreateWithFlags(&h->last, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
     delete h;
@@ -176,7 +173,6 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     return fail(SV_EHIP, std::string("workspace initialisation failed: ") + hipGetErrorString(e));
   }
   h->has_run = false;
-  h->in_graph = false;
   h->prof_max = h->prof_next = 0;
   (void)hipSetDevice(prev);
   *out = h;
@@ -231,8 +227,9 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   if (prev != cfg.device && hipSetDevice(cfg.device) != hipSuccess)
     return fail(SV_EHIP, "hipSetDevice failed");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Under stream capture the kernels become graph nodes; stage events and the
-  // completion event are left out (the graph's launches are the caller's).
+  // Under stream capture the kernels become graph nodes; stage events are
+  // left out.  No completion event is recorded per call: destroy and
+  // profile_begin, which must wait for earlier runs, synchronise the device.
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
   const bool capturing = cap != hipStreamCaptureStatusNone;
@@ -247,9 +244,7 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
     if (!capturing && b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
     e = sv::launch_verify(p, cfg.dtype, vec, nseq, s, ev);
   }
-  if (e == hipSuccess && capturing) h->in_graph = true;
-  if (e == hipSuccess && !capturing) e = hipEventRecord(h->last, s);
-  if (e == hipSuccess && !capturing) h->has_run = true;
+  if (e == hipSuccess) h->has_run = true;
   if (prev != cfg.device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(SV_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return SV_OK;
@@ -269,7 +264,7 @@ int spec_verify_profile_begin(sv_handle_t h, int max_calls) {
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
   if (prev != h->cfg.device && hipSetDevice(h->cfg.device) != hipSuccess) return fail(SV_EHIP, "hipSetDevice failed");
-  if (h->has_run) (void)hipEventSynchronize(h->last);
+  if (h->has_run) (void)hipDeviceSynchronize();  // earlier runs may still use the old events
   release_profile(h);
   hipError_t e = hipSuccess;
   for (int i = 0; i < 4 * max_calls && e == hipSuccess; ++i) {
@@ -321,14 +316,12 @@ int spec_verify_destroy(sv_handle_t h) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->cfg.device);
   hipError_t e = hipSuccess;
-  if (h->in_graph) e = hipDeviceSynchronize();  // graph launches are not tracked by the handle
-  else if (h->has_run) e = hipEventSynchronize(h->last);
-  (void)hipEventDestroy(h->last);
+  if (h->has_run) e = hipDeviceSynchronize();
   release_profile(h);
   (void)hipFree(h->ws);
   (void)hipSetDevice(prev);
   delete h;
-  if (e != hipSuccess) return fail(SV_EHIP, std::string("waiting for the last run failed: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("synchronising before the free failed: ") + hipGetErrorString(e));
   return SV_OK;
 }
 
