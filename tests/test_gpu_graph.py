@@ -50,9 +50,12 @@ def test_graph_replays_match_eager():
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     print("[graph] capture", flush=True)
+    binding.spec_verify_profile_begin(v.handle, 4)  # stage events are not recorded under capture
     with torch.cuda.graph(g):
         binding.spec_verify_run(v.handle, args)
     torch.cuda.synchronize()
+    calls, _ = binding.spec_verify_profile_end(v.handle)
+    assert calls == 0
     ref_v = Verifier(B, K, V, torch.bfloat16)
     for rep in range(2):
         for i, w in enumerate(ws):
