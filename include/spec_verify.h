@@ -119,7 +119,12 @@ typedef struct {
  *   row_status    [B] uint32 SV_ST_* bits, or NULL.
  *   diag          [B][K_max][2] float: (q_t(d_t), p_t(d_t)) for t < K_b,
  *                                  NaN elsewhere and on error rows; or NULL.
- * B = 0 is a no-op. */
+ * B = 0 is a no-op.
+ * The library trusts the caller's buffers: target_logits must hold
+ * B * (K_max + 1) * vocab elements and draft_logits B * K_max * vocab
+ * elements of the handle's dtype (vocab is the row stride), and the index
+ * arrays the sizes above.  A shorter buffer is read out of bounds; nothing
+ * on the device can detect it. */
 typedef struct {
   int32_t B;
   int32_t K_max;

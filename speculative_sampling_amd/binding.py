@@ -216,6 +216,8 @@ class Verifier:
     """A handle plus output allocation, for callers that want tensors back."""
 
     def __init__(self, max_batch: int, max_k: int, vocab: int, dtype=torch.bfloat16, device: int = 0):
+        if isinstance(dtype, int):
+            dtype = {SV_BF16: torch.bfloat16, SV_F32: torch.float32}[dtype]
         self.max_batch, self.max_k, self.vocab, self.dtype = max_batch, max_k, vocab, dtype
         self.device = device
         self.handle = spec_verify_create(max_batch, max_k, vocab, dtype, device)
@@ -227,7 +229,22 @@ class Verifier:
                 torch.empty(B, dtype=torch.int32, device=dev),
                 torch.empty(B, K, 2, dtype=torch.float32, device=dev))
 
+    def _check_logits(self, name: str, t: Optional[torch.Tensor]) -> None:
+        """The kernels take V, the dtype and the device from the handle and
+        use V as the row stride, so a tensor that disagrees would be read
+        out of bounds or misread: refuse it before anything is launched."""
+        if t is None:
+            return
+        if t.shape[-1] != self.vocab:
+            raise ValueError(f"{name} has V = {t.shape[-1]}, the handle was created for V = {self.vocab}")
+        if t.dtype != self.dtype:
+            raise TypeError(f"{name} is {t.dtype}, the handle was created for {self.dtype}")
+        if not t.is_cuda or (t.device.index or 0) != self.device:
+            raise ValueError(f"{name} is on {t.device}, the handle is on cuda:{self.device}")
+
     def __call__(self, target, draft, draft_tokens, *, out=None, stream=None, **kw):
+        self._check_logits("target", target)
+        self._check_logits("draft", draft)
         B, K1, _ = target.shape
         acc, toks, st, diag = out if out is not None else self.outputs(B, K1 - 1)
         args = make_args(target, draft, draft_tokens, accepted=acc, out_tokens=toks,
@@ -241,6 +258,7 @@ class Verifier:
         """One draw per logit row from its filtered distribution: the step
         with K = 0 (a bonus draw), row r using counter (row_offset + r, 0,
         BONUS)."""
+        self._check_logits("rows", rows)
         V = rows.shape[-1]
         flat = rows.reshape(-1, 1, V)
         n = flat.shape[0]

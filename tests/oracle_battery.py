@@ -20,6 +20,7 @@ from scipy import stats
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(HERE))
+sys.path.insert(0, HERE)
 import oracle  # noqa: E402
 
 Q = np.array([0.5, 0.25, 0.15, 0.10])
@@ -209,9 +210,40 @@ def check_nonuniform_positions(lib):
     assert abs(z) < 5
 
 
+def check_flags(lib):
+    """Boundary flags at 4e-7 (set) and 2.5e-6 (clear) from each kind of
+    boundary (tests/flag_cases.py)."""
+    import flag_cases as fc
+
+    def ver(t, d, k, **kw):
+        return oracle.verify(t, d, k, seed=fc.SEED, lib=lib, **kw)
+
+    t, d, k, flag, accept, _ = fc.accept_rows(lib)
+    r = ver(t, d, k)
+    assert list((r["flags"] & oracle.FL_ACCEPT) != 0) == list(flag)
+    assert list(r["accepted"] == 1) == list(accept)
+    g, t, d, k = fc.accept_at_one(lib)
+    assert ver(t, d, k, row_offset=g)["flags"][0] & oracle.FL_ACCEPT
+    t, y, flag, _ = fc.bonus_rows(lib)
+    r = ver(t, np.zeros((len(y), 0, 2), np.float32), np.zeros((len(y), 0), np.int32))
+    assert list(r["out_tokens"][:, 0]) == list(y)
+    assert list((r["flags"] & oracle.FL_CDF) != 0) == list(flag)
+    for g, y0 in fc.bonus_at_ends(lib):
+        r = ver(np.zeros((1, 1, 2), np.float32), np.zeros((1, 0, 2), np.float32), np.zeros((1, 0), np.int32),
+                row_offset=g)
+        assert r["out_tokens"][0, 0] == y0 and r["flags"][0] == 0
+    rows, t, d, k, y, flag, _ = fc.resample_rows(lib)
+    for i, g in enumerate(rows):
+        r = ver(t[i:i + 1], d[i:i + 1], k[i:i + 1], row_offset=g)
+        assert r["out_tokens"][0, 0] == y[i] and bool(r["flags"][0] & oracle.FL_CDF) == bool(flag[i])
+    t, d, k, top_p, flag, _ = fc.topp_rows(lib)
+    r = ver(t, d, k, default_mode=oracle.TOPP, top_p=top_p)
+    assert list((r["flags"] & oracle.FL_TOPP) != 0) == list(flag)
+
+
 CHECKS = [check_kat, check_counter_layout, check_plain, check_topk, check_topp, check_greedy,
           check_bonus, check_errors_and_ragged, check_nonuniform_positions,
-          check_worked_example, check_enumeration]
+          check_flags, check_worked_example, check_enumeration]
 
 
 def run(path):

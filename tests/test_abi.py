@@ -153,3 +153,22 @@ def test_stream_probe_rejects_bad_pointers_on_the_host():
     assert lib.spec_verify_stream_probe(ctypes.c_void_p(64), 16384, None, None) == SV_EINVAL
     assert lib.spec_verify_stream_probe(ctypes.c_void_p(8), 16384, ctypes.byref(sink), None) == SV_EINVAL
     assert b"aligned" in lib.spec_verify_last_error()
+
+
+def test_verifier_refuses_logits_that_disagree_with_the_handle():
+    """The kernels take V (the row stride), the dtype and the device from the
+    handle: a tensor that disagrees is refused before anything is launched.
+    Host-only: the handle is never created."""
+    import torch
+    v = binding.Verifier.__new__(binding.Verifier)
+    v.vocab, v.dtype, v.device, v.handle = 1000, torch.bfloat16, 0, 0
+    with pytest.raises(ValueError, match="V = 999"):
+        v._check_logits("target", torch.zeros(2, 3, 999, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="float32"):
+        v._check_logits("draft", torch.zeros(2, 2, 1000, dtype=torch.float32))
+    with pytest.raises(ValueError, match="cpu"):
+        v._check_logits("target", torch.zeros(2, 3, 1000, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="V = 1001"):
+        v(torch.zeros(2, 3, 1001, dtype=torch.bfloat16), None, None)
+    with pytest.raises(ValueError, match="V = 7"):
+        v.sample(torch.zeros(5, 7, dtype=torch.bfloat16), seed=1)

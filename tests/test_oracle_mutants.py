@@ -49,6 +49,25 @@ MUTANTS = {
     "empty_row_undetected": ("if (x[v] != -kInf) any_not_neg_inf = true;", "any_not_neg_inf = true;"),
     "diag_swapped": ("a->diag[((size_t)b * KM + t) * 2 + 0] = q;",
                      "a->diag[((size_t)b * KM + t) * 2 + 0] = p;"),
+    # the boundary flags that excuse a row from exact comparison.  (Dropping
+    # the accept flag's guard q/p < 1 + 1e-6 is not a mutant: u < 1, so
+    # |u - q/p| < 1e-6 already implies it.)
+    "window_times_10": ("const double kWindow = 1e-6;", "const double kWindow = 1e-5;"),
+    "window_over_10": ("const double kWindow = 1e-6;", "const double kWindow = 1e-7;"),
+    "accept_flag_inverted": ("std::fabs(u - ratio) < kWindow", "std::fabs(u - ratio) > kWindow"),
+    "accept_flag_one_sided": ("std::fabs(u - ratio) < kWindow", "u - ratio < kWindow"),
+    "cdf_flag_low_side_dropped": ("if ((ilo && u - lo < kWindow) || (ihi && hi - u < kWindow))",
+                                  "if (ihi && hi - u < kWindow)"),
+    "cdf_flag_high_side_dropped": ("if ((ilo && u - lo < kWindow) || (ihi && hi - u < kWindow))",
+                                   "if (ilo && u - lo < kWindow)"),
+    "cdf_flag_sides_swapped": ("if ((ilo && u - lo < kWindow) || (ihi && hi - u < kWindow))",
+                               "if ((ilo && hi - u < kWindow) || (ihi && u - lo < kWindow))"),
+    "cdf_low_end_counts": ("*interior_lo = any_before;", "*interior_lo = true;"),
+    "cdf_high_end_counts": ("*interior_hi = any_after;", "*interior_hi = true;"),
+    "topp_draft_flag_dropped": ("if (dp[t].topp_margin < kWindow) flags |= ORACLE_FL_TOPP;",
+                                "if (false) flags |= ORACLE_FL_TOPP;"),
+    "topp_margin_signed": ("margin = std::min(margin, std::fabs(before - top_p));",
+                           "margin = std::min(margin, top_p - before);"),
     "accept_position_index": ("double q = tq[t].pi[d[t]], p = dp[t].pi[d[t]];",
                               "double q = tq[t + 1].pi[d[t]], p = dp[t].pi[d[t]];"),
 }
