@@ -289,7 +289,20 @@ def cpu_baseline(w, budget_s, threads=1):
     done = state["done"]
     kind = "single-threaded fp64" if threads == 1 else f"fp64 oracle on disjoint sequences, {threads} threads"
     return {"value": done / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.B} sequences of input set 0 ({el:.1f} s, {kind})"}
+            "sample": f"{done} of {w.B} sequences of input set 0 ({el:.1f} s, {kind})",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

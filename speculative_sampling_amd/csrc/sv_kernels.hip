@@ -725,8 +725,8 @@ __global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3
 // resampled or bonus token.
 
 constexpr int kSeqThreads = kSeqWaves * kWave;
-constexpr int kRowCache = 768;
-constexpr int kDrawTiles = 8;  // tiles of a row draw whose loads are in flight together  // candidate logits of one row held in LDS
+constexpr int kRowCache = 768;   // candidate logits of one row held in LDS
+constexpr int kDrawTiles = 8;   // tiles of a row draw whose loads are in flight together
 constexpr int kVecList = 768;   // candidate vectors of one row that pass the row's cut
 constexpr int kMaxRows = 2 * kMaxK + 1;
 
@@ -1646,7 +1646,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     double seg = 0.0;
     int zl = 0x7fffffff, zh = -1, nt = 0;
     for (int t0 = v0; t0 < v1; t0 += kDrawTiles * kWave) {
-      // the loads of 4 tiles are in flight together
+      // the loads of kDrawTiles tiles are in flight together
       uint4 rq[kDrawTiles][2], rp[kDrawTiles][2];
 #pragma unroll
       for (int g = 0; g < kDrawTiles; ++g) {

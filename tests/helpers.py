@@ -2,12 +2,21 @@
 library and compare them element by element.
 
 Parity rule (both sides take the same seeded inputs):
-  * rows the oracle flags (a decision within 1e-6 of its boundary) are
-    excluded from exact comparison; there may be at most
-    max(1, ceil(1e-4 * B)) of them;
-  * on every other row the accepted count, every emitted token, the error
-    bits and the discrete info bits (zero residual, p(d) = 0) are equal;
-  * diag (q_t(d_t), p_t(d_t)) agrees within DIAG_TOL absolute.
+  * the oracle flags a row when a decision it used lies within 1e-6 of its
+    boundary (an accept ratio, a CDF step, a nucleus cut); only flagged rows
+    may differ;
+  * every row is compared: a row whose accepted count, tokens or discrete
+    status bits (errors, zero residual, p(d) = 0) differ must be flagged,
+    and such differing rows may be at most 1e-4 of the rows compared.  Each
+    comparison adds its rows, flagged rows and differing rows to
+    FLAG_TALLY; the last GPU test module checks the session's totals.  A
+    single comparison may differ on at most max(1, ceil(1e-4 * B)) rows;
+  * diag (q_t(d_t), p_t(d_t)) agrees within DIAG_TOL absolute on every row.
+
+How many rows are flagged depends on the inputs, not on the GPU: plain
+sampling over 32000 near-uniform tokens puts a uniform within 1e-6 of a CDF
+step in about 2.5% of rows, since most tokens' intervals are only a few
+1e-6 wide; a peaked nucleus flags about 1e-5 of rows.
 """
 import math
 
@@ -21,6 +30,9 @@ from speculative_sampling_amd.binding import (ST_ERRORS, ST_PZERO, ST_ZERO_RESID
 # fp32 and bf16 probability tolerances; the fp32-accumulating kernels are
 # expected to be far inside both (the tests report the actual maximum).
 DIAG_TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+# rows compared, rows flagged and rows that differ, over the session
+FLAG_TALLY = {"rows": 0, "flagged": 0, "differ": 0}
 
 
 def oracle_sampler(rows, mode, temperature, top_k, top_p, dmode, dtemp, dtopk, dtopp, seed):
@@ -70,28 +82,31 @@ def run_gpu(w: workloads.Workload, verifier: Verifier = None, row_offset: int = 
     return out
 
 
-def compare(gpu: dict, ref: dict, dtype: str, label: str = "", rate_bound: bool = True):
-    """Asserts parity; returns (n_flagged, max_diag_err).  rate_bound=False
-    drops the flagged-row rate bound for parameters chosen to sit on a
-    boundary (flagged rows are still excluded from exact comparison)."""
+def compare(gpu: dict, ref: dict, dtype: str, label: str = "", diag_only: bool = False):
+    """Asserts parity; returns (n_flagged, max_diag_err).  diag_only=True is
+    for parameters chosen to put every row on a boundary: the rows must all
+    be flagged, only diag is compared, and the comparison stays out of the
+    tally."""
     B = ref["accepted"].shape[0]
     flagged = ref["flags"] != 0
     n_flag = int(flagged.sum())
-    if rate_bound:
-        assert n_flag <= max(1, math.ceil(1e-4 * B)), f"{label}: {n_flag} flagged rows of {B}"
-    ok = ~flagged
-    acc_g, acc_r = gpu["accepted"][ok], ref["accepted"][ok]
-    bad = np.nonzero(acc_g != acc_r)[0]
-    assert bad.size == 0, f"{label}: accepted differs on rows {np.nonzero(ok)[0][bad][:10]}"
-    tg, tr = gpu["out_tokens"][ok], ref["out_tokens"][ok]
-    bad = np.nonzero((tg != tr).any(axis=1))[0]
-    assert bad.size == 0, (f"{label}: tokens differ on rows {np.nonzero(ok)[0][bad][:10]}: "
-                           f"gpu {tg[bad[:3]].tolist()} oracle {tr[bad[:3]].tolist()}")
-    bits = ST_ERRORS | ST_ZERO_RESIDUAL | ST_PZERO
-    sg = gpu["row_status"][ok] & bits
-    sr = ref["row_status"][ok].astype(np.uint32) & bits
-    bad = np.nonzero(sg != sr)[0]
-    assert bad.size == 0, f"{label}: status differs on rows {np.nonzero(ok)[0][bad][:10]}: {sg[bad[:5]]} vs {sr[bad[:5]]}"
+    if diag_only:
+        assert n_flag == B, f"{label}: a diag-only case must flag every row ({n_flag} of {B})"
+    else:
+        bits = ST_ERRORS | ST_ZERO_RESIDUAL | ST_PZERO
+        differ = (gpu["accepted"] != ref["accepted"]) | (gpu["out_tokens"] != ref["out_tokens"]).any(axis=1) | \
+                 ((gpu["row_status"] & bits) != (ref["row_status"].astype(np.uint32) & bits))
+        bad = np.nonzero(differ & ~flagged)[0]
+        assert bad.size == 0, (
+            f"{label}: unflagged rows differ: {bad[:10].tolist()}: accepted gpu "
+            f"{gpu['accepted'][bad[:3]].tolist()} oracle {ref['accepted'][bad[:3]].tolist()}, tokens gpu "
+            f"{gpu['out_tokens'][bad[:3]].tolist()} oracle {ref['out_tokens'][bad[:3]].tolist()}, status gpu "
+            f"{gpu['row_status'][bad[:3]].tolist()} oracle {ref['row_status'][bad[:3]].tolist()}")
+        n_diff = int(differ.sum())
+        assert n_diff <= max(1, math.ceil(1e-4 * B)), f"{label}: {n_diff} flagged rows of {B} differ"
+        FLAG_TALLY["rows"] += B
+        FLAG_TALLY["flagged"] += n_flag
+        FLAG_TALLY["differ"] += n_diff
     dg = gpu["diag"].astype(np.float64)
     dr = ref["diag"]
     both_nan = np.isnan(dg) & np.isnan(dr)

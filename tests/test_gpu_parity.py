@@ -18,12 +18,12 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def check(w, label, rate_bound=True):
+def check(w, label, diag_only=False):
     w = with_oracle_drafts(w)
     ref = run_oracle(w)
     print(f"[{label}] B={w.B} K={w.K_max} V={w.V} {w.dtype}", flush=True)
     gpu = run_gpu(w)
-    n_flag, err = compare(gpu, ref, w.dtype, label, rate_bound)
+    n_flag, err = compare(gpu, ref, w.dtype, label, diag_only)
     print(f"[{label}] flagged={n_flag} max|diag err|={err:.2e}", flush=True)
     return w, gpu, ref
 
@@ -167,8 +167,10 @@ def test_edge_parameters():
         w = workloads.Workload("edge", B, K, V, "bf16", base.target.clone(), base.draft.clone(),
                                default_mode=mode, default_temperature=0.9, seed=13, draft_seed=99, **kw)
         # at top_p = 0.999 the tail tokens' masses are far below 1e-6, so the
-        # cut always lies within 1e-6 of top_p: every row is flagged
-        _, gpu, _ = check(w, f"edge_{mode}_{kw}", rate_bound=kw.get("default_top_p") != 0.999)
+        # cut always lies within 1e-6 of top_p: every row is flagged, and
+        # only the probabilities are compared (test_nucleus_near_one compares
+        # tokens at a top_p this close to 1)
+        _, gpu, _ = check(w, f"edge_{mode}_{kw}", diag_only=kw.get("default_top_p") == 0.999)
         if kw.get("default_top_k") == 700:
             # kept sets beyond the 512-entry list: drawn from the re-read rows
             # with the kept-set threshold applied per token
@@ -179,6 +181,39 @@ def test_edge_parameters():
                            default_top_p=0.5, default_temperature=1.0, seed=14, draft_seed=98)
     _, gpu, _ = check(w, "ties_topp")
     assert np.all(gpu["row_status"] & ST_FULLSELECT)
+
+
+def test_nucleus_near_one():
+    """Nucleus with top_p just below 1, token for token.  Tail tokens have
+    masses far below 1e-6 here, so top_p = 0.999 lands within 1e-6 of a cut
+    on almost every row.  Each sequence instead gets the first top_p of
+    0.990, 0.991, ..., 0.999 (per-row top_p, its draft tokens drawn from the
+    draft filtered at that top_p) at which the oracle flags none of its
+    decisions, so every cut lies more than 1e-6 from its top_p."""
+    import oracle
+    B, K, V = 12, 3, 20000
+    w = workloads.iid_normal(B, K, V, sigma_t=1.5, sigma_d=0.5, mode=SV_TOPP, temperature=0.9,
+                             top_p=0.995, gen_seed=23, seed=21)
+    chosen = np.full(B, np.nan, np.float32)
+    toks = torch.zeros(B, K, dtype=torch.int32)
+    for c in np.round(np.arange(0.990, 0.9995, 0.001), 3).astype(np.float32):
+        w.top_p = torch.full((B,), float(c), dtype=torch.float32)
+        w = with_oracle_drafts(w)
+        ref = run_oracle(w)
+        free = torch.from_numpy(np.isnan(chosen) & (ref["flags"] == 0))
+        chosen[free.numpy()] = c
+        toks[free] = w.draft_tokens[free]
+    assert not np.any(np.isnan(chosen)), "no top_p in [0.990, 0.999] leaves some sequence unflagged"
+    w.top_p = torch.from_numpy(chosen)
+    w.draft_tokens = toks
+    ref = run_oracle(w)
+    assert np.all(ref["flags"] == 0)
+    print(f"[nucleus_near_one] top_p per row {chosen.tolist()}", flush=True)
+    gpu = run_gpu(w)
+    compare(gpu, ref, "bf16", "nucleus_near_one")
+    kept = [oracle.row_probs(workloads.host_array(w.target[b, 0]), oracle.TOPP, 0.9,
+                             top_p=float(chosen[b]))[3] for b in range(B)]
+    assert min(kept) > 2048     # more tokens than a chunk's candidate list holds
 
 
 def test_large_logits_take_the_exact_exponent_path():

@@ -84,13 +84,32 @@ def test_expected_tokens_per_pass(run):
 
 
 def test_emitted_tokens_follow_target(run):
+    """Chi-square over the 10^6 sequences, p > 0.01, for the tokens emitted at
+    each output position and pooled over all of them (each emitted token is
+    distributed as the target: roadtointelligence.com "Speculative
+    Decoding", "Why the output doesn't change")."""
     _, out = run
     toks = out["out_tokens"]
     for i in range(5):
         col = toks[:, i]
         col = col[col >= 0]
         _, pval = stats.chisquare(np.bincount(col, minlength=4), Q * col.size)
-        assert pval > 1e-3, i
+        print(f"[worked_example_gpu] position {i}: chi-square p = {pval:.3f}", flush=True)
+        assert pval > 0.01, i
+    # Pooled over every emitted token.  Tokens of one sequence are dependent
+    # (a long accepted run leans towards min(p, q) / a), so a plain
+    # chi-square over the pooled counts would be miscalibrated.  Sequences
+    # are i.i.d., and each emitted token is q-distributed, so the residual
+    # r_b = c_b - (n_b + 1) q (c_b: sequence b's token counts) has mean 0:
+    # the Wald statistic of sum_b r_b with the empirical covariance is
+    # chi-square with 3 degrees of freedom (the 4 counts sum to n_b + 1).
+    c = np.stack([(toks == v).sum(1) for v in range(4)], 1).astype(np.float64)
+    r = (c - c.sum(1, keepdims=True) * Q[None, :])[:, :3]
+    R = r.sum(0)
+    W = float(R @ np.linalg.solve(np.cov(r, rowvar=False) * r.shape[0], R))
+    pval = stats.chi2.sf(W, 3)
+    print(f"[worked_example_gpu] pooled: Wald chi-square p = {pval:.3f}", flush=True)
+    assert pval > 0.01
 
 
 def test_every_rejection_emits_token_0(run):

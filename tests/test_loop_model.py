@@ -82,9 +82,17 @@ def test_response_time_spread():
         sd2 = lm.response_time(a, 2, n, tt, td)[1]
         sd7 = lm.response_time(a, 7, n, tt, td)[1]
         assert sd7 / sd2 == pytest.approx(sd7_page / sd2_page, rel=0.02)
-    # the reading of the unstated length: about 125 tokens gives both values
-    assert lm.response_time(a, 2, 125, tt, td)[1] == pytest.approx(sd2_page, rel=0.03)
-    assert lm.response_time(a, 7, 125, tt, td)[1] == pytest.approx(sd7_page, rel=0.03)
+    assert sd7_page / sd2_page == pytest.approx(2.21, abs=0.005)
+    # The page does not state the response length behind the two spreads.
+    # Reported, not asserted: the length whose two spreads come closest to
+    # the printed ones (a reading, not a pin).
+    def err(n):
+        s2 = lm.response_time(a, 2, n, tt, td)[1]
+        s7 = lm.response_time(a, 7, n, tt, td)[1]
+        return max(abs(s2 / sd2_page - 1), abs(s7 / sd7_page - 1))
+    best = min(range(60, 301, 5), key=err)
+    print(f"[loop_model] response length closest to the printed spreads: {best} tokens "
+          f"(worst relative error {err(best):.3f})")
 
 
 def test_rounds_moments_by_simulation():
