@@ -209,6 +209,24 @@ int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages);
  * gives the read rate the streaming pass is measured against. */
 int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Runs the
+ * same step as spec_verify_run with the same kernels and results, on
+ * cfg->device and `stream`, with no handle: the workspace is a static
+ * device buffer of SV_STATIC_SCRATCH_BYTES that the library holds on each
+ * device it runs on until the process ends.  cfg gives V, the dtype and the
+ * device; max_batch and max_k only bound B and K_max as in
+ * spec_verify_validate.  A call whose workspace (which grows with B,
+ * K_max and V) exceeds the buffer returns SV_ECAPACITY, launches nothing
+ * and says how many bytes it needed in spec_verify_last_error.  No
+ * allocation, no synchronisation, no events.  Every call on one device
+ * shares that device's buffer: calls that overlap on a device (other
+ * streams, other threads, graph replays) race and give wrong results;
+ * order them on one stream.  The buffer needs no clearing between calls:
+ * each call writes every workspace entry it reads. */
+#define SV_STATIC_SCRATCH_BYTES ((uint64_t)64 << 20)
+int spec_verify_run_static(const sv_config* cfg, const sv_args* args, void* stream);
+
 /* Text of the last error reported on the calling thread ("" if none). */
 const char* spec_verify_last_error(void);
 

@@ -26,7 +26,11 @@ ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 # Every function the header declares.
 EXPORTS = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy",
            "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_profile_begin",
-           "spec_verify_profile_end", "spec_verify_stream_probe", "spec_verify_last_error")
+           "spec_verify_profile_end", "spec_verify_stream_probe", "spec_verify_last_error",
+           "spec_verify_run_static")
+
+# Size of the static device buffer spec_verify_run_static works in.
+SV_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class SvConfig(ctypes.Structure):
@@ -76,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_profile_end.restype = ctypes.c_int
     lib.spec_verify_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.spec_verify_stream_probe.restype = ctypes.c_int
+    lib.spec_verify_run_static.argtypes = [ctypes.POINTER(SvConfig), ctypes.POINTER(SvArgs), ctypes.c_void_p]
+    lib.spec_verify_run_static.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
     lib.spec_verify_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -186,6 +192,20 @@ def spec_verify_run(handle: int, args: SvArgs, stream=None) -> None:
     rc = load_library().spec_verify_run(ctypes.c_void_p(handle), ctypes.byref(args), ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_run")
+
+
+def spec_verify_run_static(vocab: int, dtype, args: SvArgs, device: int = 0, stream=None) -> None:
+    """The step without a handle and without any allocation: the workspace is
+    the library's static device buffer (SV_STATIC_SCRATCH_BYTES per device).
+    Calls that overlap on one device race; order them on one stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    cfg = make_config(max(1, args.B), args.K_max, vocab, dtype, device)
+    rc = load_library().spec_verify_run_static(ctypes.byref(cfg), ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_run_static")
 
 
 def spec_verify_profile_begin(handle: int, max_calls: int) -> None:

@@ -6,6 +6,8 @@
 //         batches of at most kMaxSeqPerLaunch sequences and kMaxWavesPerLaunch
 //         streaming waves on the caller's stream;
 // destroy synchronises the device if the handle has run, then frees.
+// run_static runs the same kernels with the workspace in a static device
+//         array (no allocation at all), for callers that cannot allocate.
 
 #include <hip/hip_runtime.h>
 
@@ -13,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -25,9 +28,6 @@ struct sv_handle_s {
   int S, L, cap, R_max;
   void* ws;
   size_t ws_bytes;
-  sv::ChunkRec* chunks;
-  int2* cent;
-  sv::KeptEntry* kept;
   bool has_run;  // some run was enqueued (or captured): destroy waits for the device
   // stage timing (spec_verify_profile_begin / _end)
   std::vector<hipEvent_t> prof;
@@ -161,10 +161,6 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     (void)hipSetDevice(prev);
     return fail(SV_ENOMEM, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
   }
-  char* base = static_cast<char*>(h->ws);
-  h->chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
-  h->cent = reinterpret_cast<int2*>(base + g.off_cent);
-  h->kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
@@ -179,25 +175,19 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
   return SV_OK;
 }
 
-int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
-  if (!h) return fail(SV_EINVAL, "handle is NULL");
-  int rc = spec_verify_validate(&h->cfg, a);
-  if (rc != SV_OK) return rc;
-  if (a->B == 0) return SV_OK;
-  const sv_config& cfg = h->cfg;
-  const int es = cfg.dtype == SV_BF16 ? 2 : 4;
-  // 16-byte vector loads need every row start on a 16-byte boundary.
-  const bool vec = ((size_t)cfg.vocab * es) % 16 == 0 &&
-                   (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
-                   (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);
+namespace {
+
+// The kernel parameters of one call: the caller's arguments and the
+// workspace laid out by geometry g at ws.
+sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const sv_args* a) {
   sv::KParams p;
   p.B = a->B;
   p.K_max = a->K_max;
   p.V = cfg.vocab;
   p.R = 2 * a->K_max + 1;
-  p.S = h->S;
-  p.L = h->L;
-  p.cap = h->cap;
+  p.S = g.S;
+  p.L = g.L;
+  p.cap = g.cap;
   p.b_base = 0;
   p.b_end = 0;
   p.target = a->target_logits;
@@ -218,9 +208,47 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   p.out_tokens = a->out_tokens;
   p.status = a->row_status;
   p.diag = a->diag;
-  p.chunks = h->chunks;
-  p.cent = h->cent;
-  p.kept = h->kept;
+  char* base = static_cast<char*>(ws);
+  p.chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
+  p.cent = reinterpret_cast<int2*>(base + g.off_cent);
+  p.kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
+  return p;
+}
+
+// 16-byte vector loads need every row start on a 16-byte boundary.
+bool vector_loads(const sv_config& cfg, const sv_args* a) {
+  const int es = cfg.dtype == SV_BF16 ? 2 : 4;
+  return ((size_t)cfg.vocab * es) % 16 == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
+         (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);
+}
+
+// Enqueues the call in launches of at most kMaxSeqPerLaunch sequences and
+// kMaxWavesPerLaunch streaming waves; prof (or NULL) receives the stage
+// events of the first launch.
+hipError_t launch_call(sv::KParams p, int dtype, bool vec, hipStream_t s, hipEvent_t* prof) {
+  const size_t per_seq = (size_t)p.R * p.S;
+  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxWavesPerLaunch / per_seq));
+  hipError_t e = hipSuccess;
+  for (int b0 = 0; b0 < p.B && e == hipSuccess; b0 += seq_per_launch) {
+    p.b_base = b0;
+    const int nseq = std::min(seq_per_launch, p.B - b0);
+    p.b_end = b0 + nseq;
+    e = sv::launch_verify(p, dtype, vec, nseq, s, b0 == 0 ? prof : nullptr);
+  }
+  return e;
+}
+
+}  // namespace
+
+int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
+  if (!h) return fail(SV_EINVAL, "handle is NULL");
+  int rc = spec_verify_validate(&h->cfg, a);
+  if (rc != SV_OK) return rc;
+  if (a->B == 0) return SV_OK;
+  const sv_config& cfg = h->cfg;
+  Geometry g = geometry(&cfg);
+  const sv::KParams p = make_params(cfg, g, h->ws, a);
+  const bool vec = vector_loads(cfg, a);
 
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
@@ -233,17 +261,9 @@ int spec_verify_run(sv_handle_t h, const sv_args* a, void* stream) {
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
   const bool capturing = cap != hipStreamCaptureStatusNone;
-  const size_t per_seq = (size_t)p.R * p.S;
-  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxWavesPerLaunch / per_seq));
-  hipError_t e = hipSuccess;
-  for (int b0 = 0; b0 < a->B && e == hipSuccess; b0 += seq_per_launch) {
-    p.b_base = b0;
-    const int nseq = std::min(seq_per_launch, a->B - b0);
-    p.b_end = b0 + nseq;
-    hipEvent_t* ev = nullptr;
-    if (!capturing && b0 == 0 && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
-    e = sv::launch_verify(p, cfg.dtype, vec, nseq, s, ev);
-  }
+  hipEvent_t* ev = nullptr;
+  if (!capturing && h->prof_next < h->prof_max) ev = &h->prof[4 * (size_t)h->prof_next++];
+  const hipError_t e = launch_call(p, cfg.dtype, vec, s, ev);
   if (e == hipSuccess) h->has_run = true;
   if (prev != cfg.device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(SV_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
@@ -326,3 +346,58 @@ int spec_verify_destroy(sv_handle_t h) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------
+// The entry point that allocates nothing.  Its workspace is `scratch`, a
+// file-scope device array that the runtime places once on every device this
+// library's code runs on and keeps until the process ends.  In host code
+// `scratch` only names the variable: its device address on the current
+// device comes from hipGetSymbolAddress, taken once per device and kept in
+// g_scratch_ptr, and only that address is passed to the kernels.
+static_assert(SV_STATIC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device `dev`.
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int spec_verify_run_static(const sv_config* cfg, const sv_args* a, void* stream) {
+  int rc = spec_verify_validate(cfg, a);
+  if (rc != SV_OK) return rc;
+  if (a->B == 0) return SV_OK;
+  if (cfg->device >= kMaxDevices) return fail(SV_EINVAL, "device ordinal beyond the static scratch table (64)");
+  // the workspace this call needs, laid out for its own B and K_max
+  sv_config need = *cfg;
+  need.max_batch = a->B;
+  need.max_k = a->K_max;
+  const Geometry g = geometry(&need);
+  if (g.total > SV_STATIC_SCRATCH_BYTES)
+    return fail(SV_ECAPACITY, "the call needs " + std::to_string(g.total) +
+                                  " bytes of workspace, more than the static scratch buffer's " +
+                                  std::to_string((unsigned long long)SV_STATIC_SCRATCH_BYTES));
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(SV_EHIP, "hipGetDevice failed");
+  if (prev != cfg->device && hipSetDevice(cfg->device) != hipSuccess) return fail(SV_EHIP, "hipSetDevice failed");
+  void* ws = nullptr;
+  hipError_t e = scratch_address(cfg->device, &ws);
+  if (e == hipSuccess) e = launch_call(make_params(need, g, ws, a), cfg->dtype, vector_loads(*cfg, a),
+                                       static_cast<hipStream_t>(stream), nullptr);
+  if (prev != cfg->device) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("static run failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}

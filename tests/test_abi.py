@@ -172,3 +172,20 @@ def test_verifier_refuses_logits_that_disagree_with_the_handle():
         v(torch.zeros(2, 3, 1001, dtype=torch.bfloat16), None, None)
     with pytest.raises(ValueError, match="V = 7"):
         v.sample(torch.zeros(5, 7, dtype=torch.bfloat16), seed=1)
+
+
+@needs_lib
+def test_static_entry_refuses_calls_beyond_its_buffer_on_the_host():
+    """A call whose workspace exceeds the static buffer is refused before any
+    HIP call: fake device addresses are never touched."""
+    lib = binding.load_library()
+    need = binding.spec_verify_workspace_bytes(4096, 8, 256000, SV_BF16)
+    assert need > binding.SV_STATIC_SCRATCH_BYTES
+    cfg = binding.make_config(4096, 8, 256000, SV_BF16)
+    rc = lib.spec_verify_run_static(ctypes.byref(cfg), ctypes.byref(_args(B=4096, K_max=8)), None)
+    assert rc == SV_ECAPACITY
+    msg = binding.spec_verify_last_error()
+    assert str(need) in msg and "static scratch" in msg
+    # argument errors are reported as by spec_verify_run
+    rc = lib.spec_verify_run_static(ctypes.byref(cfg), ctypes.byref(_args(B=4096, K_max=8, target=None)), None)
+    assert rc == SV_EINVAL
