@@ -1,10 +1,10 @@
 // Host side of libspec_verify: the C ABI declared in include/spec_verify.h.
 //
-// create  allocates the device workspace once (chunk records, candidate
-//         vector lists, kept lists);
+// create  allocates the device workspace once (chunk records, row records,
+//         kept lists);
 // run     validates on the host, then enqueues the kernels of the step for
-//         batches of at most kMaxSeqPerLaunch sequences and kMaxWavesPerLaunch
-//         streaming waves on the caller's stream;
+//         batches of at most kMaxSeqPerLaunch sequences and kMaxRowsPerLaunch
+//         rows on the caller's stream;
 // destroy synchronises the device if the handle has run, then frees.
 // run_static runs the same kernels with the workspace in a static device
 //         array (no allocation at all), for callers that cannot allocate.
@@ -25,7 +25,6 @@
 
 struct sv_handle_s {
   sv_config cfg;
-  int S, L, cap, R_max;
   void* ws;
   size_t ws_bytes;
   bool has_run;  // some run was enqueued (or captured): destroy waits for the device
@@ -38,10 +37,11 @@ namespace {
 
 thread_local std::string g_last_error;
 // A dispatch counts its work-items in 32 bits.  Per launch: at most 2^23
-// streaming waves (2^29 work-items) and 2^22 sequences (2^22 work-groups of
-// kSeqWaves waves: 3.2e9 work-items).
-constexpr size_t kMaxWavesPerLaunch = (size_t)1 << 23;
+// rows (row-kernel work-groups of kThreads: 2^31 work-items) and 2^22
+// sequences (work-groups of kSeqWaves waves: 2^31 work-items).
+constexpr size_t kMaxRowsPerLaunch = (size_t)1 << 23;
 constexpr size_t kMaxSeqPerLaunch = (size_t)1 << 22;
+static_assert(kMaxRowsPerLaunch * sv::kThreads < ((size_t)1 << 32), "row grid");
 static_assert(kMaxSeqPerLaunch * sv::kSeqWaves * 64 < ((size_t)1 << 32), "sequence grid");
 
 int fail(int code, const std::string& msg) {
@@ -50,8 +50,8 @@ int fail(int code, const std::string& msg) {
 }
 
 struct Geometry {
-  int S, L, cap, R_max;
-  size_t off_chunks, off_cent, off_kept, total;
+  int S, L, R_max;
+  size_t off_chunks, off_rows, off_kept, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -69,26 +69,20 @@ int check_config(const sv_config* cfg) {
 Geometry geometry(const sv_config* cfg) {
   Geometry g;
   const int V = cfg->vocab;
-  const int ve = cfg->dtype == SV_BF16 ? 8 : 4;
   const int chunk_cap = sv::chunk_capacity(cfg->dtype);
   // whole chunks of chunk_cap logits, the row's remainder in the last one
   g.S = (V + chunk_cap - 1) / chunk_cap;
   g.L = chunk_cap;
-  // candidate vectors per chunk: fewer per chunk when a row has many, and
-  // never more than a chunk holds
-  const int chunk_vecs = (std::min(g.L, V) + ve - 1) / ve;
-  g.cap = std::min(std::max(32, std::min(sv::kCandVecs, 4096 / g.S)), chunk_vecs);
   g.R_max = 2 * cfg->max_k + 1;
   const size_t rows = (size_t)cfg->max_batch * g.R_max;
+  const size_t target_rows = (size_t)cfg->max_batch * (cfg->max_k + 1);
   size_t off = 0;
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
-  g.off_cent = off;
-  off = align_up(off + rows * g.S * (size_t)g.cap * sizeof(int2), 256);
-  // kept lists go through global memory only for sequences of more rows
-  // than the sequence kernel has waves
+  g.off_rows = off;
+  off = align_up(off + rows * sizeof(sv::RowRec), 256);
   g.off_kept = off;
-  if (g.R_max > sv::kSeqWaves) off = align_up(off + rows * std::min(sv::kListMax, V) * sizeof(sv::KeptEntry), 256);
+  off = align_up(off + target_rows * std::min(sv::kListMax, V) * sizeof(sv::KeptEntry), 256);
   g.total = off;
   return g;
 }
@@ -116,8 +110,11 @@ int spec_verify_validate(const sv_config* cfg, const sv_args* a) {
   if (a->K_max > cfg->max_k) return fail(SV_ECAPACITY, "K_max exceeds max_k");
   if (a->B == 0) return SV_OK;
   if (!a->target_logits) return fail(SV_EINVAL, "target_logits is NULL");
-  if (a->K_max > 0 && (!a->draft_logits || !a->draft_tokens))
-    return fail(SV_EINVAL, "draft_logits and draft_tokens are required when K_max > 0");
+  if (a->K_max > 0 && !a->draft_tokens) return fail(SV_EINVAL, "draft_tokens is required when K_max > 0");
+  // greedy verification needs only the target's argmax: the draft's logits
+  // may be left out when every row is greedy
+  if (a->K_max > 0 && !a->draft_logits && (a->mode || a->default_mode != SV_GREEDY))
+    return fail(SV_EINVAL, "draft_logits is required when K_max > 0 (unless every row is greedy)");
   if (!a->accepted || !a->out_tokens) return fail(SV_EINVAL, "accepted and out_tokens are required");
   // Defaults are checked only where some row can use them.
   if (!a->mode && (a->default_mode < SV_PLAIN || a->default_mode > SV_GREEDY))
@@ -150,10 +147,6 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     return fail(SV_ENOMEM, "host allocation failed");
   }
   h->cfg = *cfg;
-  h->S = g.S;
-  h->L = g.L;
-  h->cap = g.cap;
-  h->R_max = g.R_max;
   h->ws_bytes = g.total;
   hipError_t e = hipMalloc(&h->ws, g.total);
   if (e != hipSuccess) {
@@ -187,11 +180,10 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.R = 2 * a->K_max + 1;
   p.S = g.S;
   p.L = g.L;
-  p.cap = g.cap;
   p.b_base = 0;
   p.b_end = 0;
   p.target = a->target_logits;
-  p.draft = a->draft_logits;
+  p.draft = a->K_max > 0 ? a->draft_logits : nullptr;
   p.tokens = a->draft_tokens;
   p.kpr = a->k_per_row;
   p.mode = a->mode;
@@ -210,7 +202,7 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.diag = a->diag;
   char* base = static_cast<char*>(ws);
   p.chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
-  p.cent = reinterpret_cast<int2*>(base + g.off_cent);
+  p.rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
   p.kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   return p;
 }
@@ -219,15 +211,14 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
 bool vector_loads(const sv_config& cfg, const sv_args* a) {
   const int es = cfg.dtype == SV_BF16 ? 2 : 4;
   return ((size_t)cfg.vocab * es) % 16 == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
-         (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);
+         (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);  // NULL is aligned
 }
 
 // Enqueues the call in launches of at most kMaxSeqPerLaunch sequences and
-// kMaxWavesPerLaunch streaming waves; prof (or NULL) receives the stage
-// events of the first launch.
+// kMaxRowsPerLaunch rows; prof (or NULL) receives the stage events of the
+// first launch.
 hipError_t launch_call(sv::KParams p, int dtype, bool vec, hipStream_t s, hipEvent_t* prof) {
-  const size_t per_seq = (size_t)p.R * p.S;
-  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxWavesPerLaunch / per_seq));
+  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxRowsPerLaunch / p.R));
   hipError_t e = hipSuccess;
   for (int b0 = 0; b0 < p.B && e == hipSuccess; b0 += seq_per_launch) {
     p.b_base = b0;

@@ -9,46 +9,40 @@
 
 namespace sv {
 
-// Work-group shape of every kernel: 4 wave64s.
-constexpr int kThreads = 256;
-// The streaming kernel gives each wave (64 lanes) one chunk of a row; each
-// lane keeps kLoads 16-byte vectors of it in registers (64 VGPRs): 128 bf16
-// or 64 fp32 logits, so a chunk holds at most 8192 bf16 / 4096 fp32 logits.
-constexpr int kLoads = 16;
-// Candidate list capacity per chunk, in 16-byte logit vectors: the vectors
-// that may hold a token near the maximum, kept for the top-k / nucleus
-// threshold search (fewer per chunk when a row has many chunks).
+// Work-group of the row kernel: 4 wave64s stream one logit row.
+constexpr int kRowWaves = 4;
+constexpr int kThreads = 64 * kRowWaves;
+// Each wave streams its share of a row in chunks: every lane keeps kLoads
+// 16-byte vectors of a chunk in registers (64 VGPRs), 128 bf16 or 64 fp32
+// logits, so a chunk holds 8192 bf16 / 4096 fp32 logits.
+constexpr int kLoads = 8;
+// Candidate vectors (the 16-byte logit vectors that may hold a token of a
+// top-k / nucleus kept set) one wave can keep in LDS for its share of a row.
 constexpr int kCandVecs = 256;
-// Largest kept set the final draw takes from the merged kept list without
-// re-reading the logit rows.
+// Largest kept set of a target row that is written out as a list, so that
+// the final draw needs no second read of the logit rows.
 constexpr int kListMax = 512;
-// Waves of the per-sequence kernel (one logit row each); sequences of more
-// rows keep their kept lists in global memory.
-constexpr int kSeqWaves = 12;
+// Waves of the per-sequence kernel (accept walk and final draw).
+constexpr int kSeqWaves = 8;
 constexpr int kMaxK = 64;
 constexpr int kMaxVocab = 1 << 22;
 
 inline int chunk_capacity(int dtype) { return 64 * kLoads * (dtype == SV_BF16 ? 8 : 4); }
 
-// Per-(row, chunk) partial results written by the streaming kernel.
+// Per-(row, chunk) softmax sums of a plain target row: its bonus draw
+// locates the chunk that holds its target from them.
 struct ChunkRec {
-  float m;         // chunk maximum of the raw logits (-inf if none is finite)
-  float cut;       // every token of the chunk with logit >= cut (and > -inf) lies
-                   // in a vector of the chunk's candidate list; +inf when the
-                   // list is incomplete
-  double z;        // sum over the chunk of 2^((x - m) * c2)   (plain, nucleus)
-  int32_t cnt;     // candidate vectors stored
-  int32_t arg;     // lowest index whose logit equals m      (greedy)
-  uint32_t flags;  // kCfNonFinite
-  float o;         // listed vectors' keys are terms 2^(x c2 - o) (nucleus)
+  double z;     // sum over the chunk of 2^(x c2 - o)  (0: no finite logit)
+  float o;      // exponent offset of the chunk's terms
+  int32_t pad;
 };
 constexpr uint32_t kCfNonFinite = 1u;
 
-// Per logit row (one model at one position of one sequence) after merging;
-// held in LDS by the sequence kernel.
+// One logit row (one model at one position of one sequence) after the row
+// kernel: everything the accept walk and the final draw need.
 struct RowRec {
   float M;          // row maximum (raw logit)
-  float T;          // kept set is {x >= T}; -inf for plain
+  float T;          // kept set is {x >= T}; -inf when every token is kept
   double c2;        // log2(e) / temperature
   double Zs;        // kept mass: sum_{x >= T} 2^((x - M) * c2)
   double pid;       // probability of this row's draft token (NaN if none)
@@ -57,20 +51,22 @@ struct RowRec {
   uint32_t flags;   // SV_ST_* error/info bits of the row, plus kRf* below
   int32_t pad;
 };
-// The row's kept set is stored, in vocabulary order with its probabilities,
-// in the row's KeptEntry list.
+// The row's kept set is stored, in vocabulary order, in its KeptEntry list.
 constexpr uint32_t kRfListOk = 1u << 16;
+// The row's chunk records (ChunkRec) were written.
+constexpr uint32_t kRfChunks = 1u << 17;
 
-// One token of a target row's kept set: vocabulary index and probability.
+// One token of a target row's kept set: vocabulary index, the target's logit
+// and, for positions that score a draft token, the draft's logit there.
 struct KeptEntry {
   int32_t idx;
+  float xq;
+  float xp;
   int32_t pad;
-  double q;
 };
 
 struct KParams {
   int32_t B, K_max, V, R, S, L;
-  int32_t cap;  // candidate vectors per chunk
   int32_t b_base, b_end;  // sequences [b_base, b_end) of this launch
   const void* target;
   const void* draft;
@@ -90,18 +86,18 @@ struct KParams {
   int32_t* out_tokens;
   uint32_t* status;
   float* diag;
-  ChunkRec* chunks;
-  int2* cent;      // [row][chunk][cap] candidate vectors: first logit index and key
-  KeptEntry* kept;  // [rows][kListMax]
+  ChunkRec* chunks;  // [B][R][S]  (plain target rows)
+  RowRec* rows;      // [B][R]
+  KeptEntry* kept;   // [B][K_max + 1][min(kListMax, V)]  (target rows)
 };
 
 // Enqueues the kernels of one call for sequences
-// [p.b_base, p.b_base + nseq): the streaming chunk pass (the default mode's
-// instance, or the one holding every mode's path when the call gives a mode
-// per sequence), then the per-sequence merge, accept walk and draw.
-// When ev is not NULL, ev[0] / ev[1] mark the start and end of the streaming
-// kernel, ev[2] / ev[3] those of the sequence kernel, each recorded on the
-// kernel's own dispatch.
+// [p.b_base, p.b_base + nseq): the row kernel (the default mode's instance,
+// or the one holding every mode's path when the call gives a mode per
+// sequence), then the per-sequence accept walk and draw.  When ev is not
+// NULL, ev[0] / ev[1] mark the start and end of the row kernel, ev[2] /
+// ev[3] those of the sequence kernel, each recorded on the kernel's own
+// dispatch.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream,
                          hipEvent_t* ev = nullptr);
 // Reads the first bytes / 16384 whole 16 KB blocks of data once (see spec_verify_stream_probe).

@@ -1,23 +1,22 @@
 // gfx950 kernels of the verify-and-resample step of speculative sampling.
 //
-// A call runs two stages on the caller's stream; the kernel boundary orders
+// A call runs two kernels on the caller's stream; the kernel boundary orders
 // them, so no work-group ever waits for another:
 //
-//   chunk_kernel    one wave per chunk of a logit row.  Every used row
-//                   (target positions 0..K_b, draft positions 0..K_b-1) is
-//                   split into chunks of 8192 bf16 / 4096 fp32 logits; each
-//                   wave streams its chunk from HBM into registers exactly
-//                   once and reduces it: the sum of the terms 2^((x - m) c2)
-//                   and the maximum, the candidate vectors of the nucleus /
-//                   top-k threshold search, the greedy argmax.  One instance
-//                   per sampling mode keeps each mode's registers minimal.
-//   seq_kernel      one work-group per sequence.  Each wave merges one row:
-//                   log-sum-exp over the chunks, radix selection of the
-//                   threshold over the candidates cached in LDS, kept mass,
-//                   the probability of the row's draft token and, for target
-//                   rows, the kept set in vocabulary order.  Then the accept
-//                   walk, the first rejection, the resample from
-//                   normalize((q - p)+) or the bonus draw, and the outputs.
+//   row_kernel   one work-group of 4 waves per logit row (target positions
+//                0..K_b and draft positions 0..K_b-1 of every sequence).
+//                The waves stream the row from HBM once, 16 KB per wave at a
+//                time into registers, and reduce it: the sum of the terms
+//                2^((x - m) c2) and the maximum of every chunk, the greedy
+//                argmax, and the candidate vectors of a top-k / nucleus kept
+//                set, which stay in LDS.  Then one wave finishes the row:
+//                log-sum-exp over the chunks, the threshold by radix
+//                selection over the candidates, the kept mass, the
+//                probability of the row's draft token and, for target rows,
+//                the kept set in vocabulary order.
+//   seq_kernel   one work-group per sequence: the accept walk, the first
+//                rejection, the resample from normalize((q - p)+) or the
+//                bonus draw, and the outputs.
 //
 // The step follows the pages' rule (FDE Interviews breakdown of Chen et al.,
 // section 01 and its figure; paperlayer.ai summary of arXiv 2302.01318,
@@ -225,8 +224,31 @@ __device__ __forceinline__ int wave_min_i(int v) {
 __device__ __forceinline__ int wave_max_i(int v) {
   return lane63(wave_scan(v, (int)0x80000000, [](int a, int b) { return max(a, b); }));
 }
+// Maximum of values >= 0 (or +inf) over the wave, taken on their bit
+// patterns, which such floats order as the values (no NaN handling needed).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  return __int_as_float(wave_max_i(__float_as_int(v)));
+}
 __device__ __forceinline__ uint32_t wave_or_u(uint32_t v) {
   return lane63(wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
+}
+// How many of the lanes below this one have their bit set in the wave-uniform
+// mask bal (v_mbcnt from the scalar mask; no per-lane mask register).
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// A wave-uniform value moved to scalar registers.
+__device__ __forceinline__ double uniform_d(double v) {
+  return lane_at(v, 0);
+}
+
+// The lane id, opaque to the compiler: expressions of it are recomputed
+// where they are used instead of being hoisted out of a loop and held in
+// registers (or spilled) across it.
+__device__ __forceinline__ int fresh_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
 }
 
 // ---------------------------------------------------- per-sequence params --
@@ -275,11 +297,10 @@ __device__ __forceinline__ bool decode_row(const KParams& P, const SeqParams& sp
   return *tgt ? (*t <= sp.Kb) : (*t < sp.Kb);
 }
 
-// ======================================================= chunk kernel ====
+// ================================================== chunk reductions ====
 //
-// Each wave owns one chunk of a logit row (64 lanes x kLoads vectors) and
-// reduces it on its own, with wave ballots and shuffles only: no barrier and
-// no LDS, so the waves of a work-group never wait for one another.
+// A wave holds one chunk of a logit row in registers (64 lanes x kLoads
+// vectors) and reduces it with wave ballots and DPP moves only.
 
 // Loads this lane's part of chunk [c0, c1) into registers: vector i holds
 // logits c0 + (i * 64 + lane) * VE + [0, VE).  Every load is issued
@@ -334,6 +355,74 @@ __device__ __forceinline__ void load_chunk(uint4 (&buf)[kLoads], const char* row
       }
       buf[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+  }
+}
+
+// Makes the compiler forget what it knows of buf's values (the asm emits
+// nothing): a later pass unpacks the logits again instead of keeping the
+// first pass's 128 unpacked values live in registers.
+__device__ __forceinline__ void unpack_barrier(uint4 (&buf)[kLoads]) {
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) asm volatile("" : "+v"(buf[i].x), "+v"(buf[i].y), "+v"(buf[i].z), "+v"(buf[i].w));
+}
+
+// load_chunk for a whole chunk (c1 = c0 + 64 * kLoads * VE).
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_whole_chunk(uint4 (&buf)[kLoads], const char* row, int c0, int lane) {
+  constexpr int VE = Fmt<DT>::VE, ES = Fmt<DT>::ES;
+  if constexpr (VEC) {
+    // one base address and constant offsets
+    const uint4* base = reinterpret_cast<const uint4*>(row + (size_t)c0 * ES);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) buf[i] = load_stream(&base[i * kWave + lane]);
+  } else {
+    load_chunk<DT, VEC>(buf, row, c0, c0 + kWave * kLoads * VE, lane);
+  }
+}
+
+// A buffer resource over one logit row of `bytes` bytes: buffer loads past
+// its end return 0 instead of reading memory.  The row is the same for the
+// whole wave; its address goes through readfirstlane so that the resource
+// lives in scalar registers (a resource the compiler cannot prove uniform
+// turns every load into a loop over the lanes' distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_resource(const char* row, int bytes) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(row);
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32) |
+                     (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uintptr_t)u), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Issues the loads of the chunk at byte offset `off` of a row of whole
+// 16-byte vectors, through the row's buffer resource (non-temporal: every
+// logit is read once).  The offset goes into the per-lane offset, which the
+// hardware checks against the row's size: vectors past the row's end read
+// as 0 without touching memory, and off = the row's size issues loads that
+// all read 0 (so that a wave always has the same number of loads in flight).
+// mask_chunk makes every vector past the chunk's end -inf once the data is
+// needed, so that issuing the loads does not wait for them.
+template <int DT>
+__device__ __forceinline__ void issue_chunk(uint4 (&buf)[kLoads], __amdgpu_buffer_rsrc_t rs, int off, int lane) {
+  const int v0 = off + lane * 16;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, v0 + i * kWave * 16, 0, 2);
+    buf[i] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void mask_chunk(uint4 (&buf)[kLoads], int c0, int c1, int lane) {
+  constexpr int VE = Fmt<DT>::VE;
+  const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+  const int nvec = (c1 - c0) / VE;
+  if (nvec >= kWave * kLoads) return;  // a whole chunk (wave-uniform)
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const bool ok = i * kWave + lane < nvec;
+    buf[i].x = ok ? buf[i].x : ninf;
+    buf[i].y = ok ? buf[i].y : ninf;
+    buf[i].z = ok ? buf[i].z : ninf;
+    buf[i].w = ok ? buf[i].w : ninf;
   }
 }
 
@@ -422,16 +511,16 @@ __device__ __forceinline__ float choose_cut(const float (&vmax)[kLoads], float m
   return kInf;
 }
 
-// One exp per logit: returns the lane's sum of the terms 2^(x c2 - o) and
-// the largest term of each of its vectors (emax[i]).  With o = r c2 rounded
-// to fp32 each term is 2^((x - r) c2 + delta), delta = r c2 - o being common
-// to all of them; the exponent x c2 - o is rounded once (fma).  The logits
-// are only used through the terms, so each vector is unpacked right where
-// it is consumed.
+// One exp per logit: returns the lane's sum of the chunk's terms
+// 2^(x c2 - o), the largest term of each of its vectors (emax[i]) and its
+// largest term (*em).  The exponent x c2 - o is rounded once (fma).  The
+// logits are only used through the terms, so each vector is unpacked right
+// where it is consumed.
 template <int DT>
-__device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, float o, float (&emax)[kLoads]) {
+__device__ __forceinline__ float exp_terms(const uint4 (&buf)[kLoads], float c2, float o, float (&emax)[kLoads],
+                                           float* em) {
   constexpr int VE = Fmt<DT>::VE;
-  float acc = 0.0f;
+  float acc = 0.0f, mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     float e[VE];
@@ -447,288 +536,99 @@ __device__ __forceinline__ float exp_pass(const uint4 (&buf)[kLoads], float c2, 
       mi = fmaxf(fmaxf(fmaxf(e[0], e[1]), e[2]), e[3]);
     }
     emax[i] = mi;
+    mx = fmaxf(mx, mi);
     acc += si;
   }
+  *em = mx;
   return acc;
 }
 
-// Lists each vector flagged in `mask` as (index of its first logit, key),
-// in (vector, lane) order, i.e. increasing vocabulary index; returns how
-// many there are (entries beyond cap are dropped).  key[i] is the vector's
-// largest term 2^(x c2 - o) (nucleus) or its largest logit (top-k).
-__device__ __forceinline__ int list_vectors(int2* de, uint32_t mask, const float* key, int c0, int ve, int cap,
-                                            int lane) {
-  const uint64_t below = (1ull << lane) - 1ull;
-  const int e0 = c0 + lane * ve;  // first index of the lane's vector in slot 0
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const bool h = (mask >> i) & 1u;
-    const uint64_t bal = __ballot(h);
-    if (bal) {  // slots with no listed vector cost one ballot
-      if (h) {
-        const int pos = n + __popcll(bal & below);
-        if (pos < cap) de[pos] = make_int2(e0 + i * kWave * ve, __float_as_int(key[i]));
-      }
-      n += __popcll(bal);
-    }
-  }
-  return n;
-}
-
-// Softmax statistics of a plain / nucleus chunk from one exp per logit.
-struct PlainStats {
-  float o;        // exponent offset: terms are 2^(x c2 - o)
-  double zw;      // sum of the chunk's terms
-  double ma;      // the chunk maximum, from its largest term
-  int st;         // 0 = statistics valid, 1 = no finite logit, 2 = NaN or +inf
-  float emax[kLoads];  // largest term of each of the lane's vectors
+// Lane-local softmax sums of the streaming pass (plain and nucleus rows).
+// Every lane adds the terms 2^(x c2 - o) of its own logits, over all the
+// chunks of its wave, into an fp64 sum, so a chunk costs no wave-wide sum.
+// The offset o is wave-uniform, an integer, and only grows: raising it
+// rescales the sums by a power of two, which is exact.
+struct SoftAcc {
+  double z;   // the lane's sum of 2^(x c2 - o)
+  float o;    // the exponent offset (-inf until the wave has seen a finite logit)
+  float lt;   // the largest x c2 of the wave's logits so far, from its largest term (-inf: none)
 };
 
-// The exponent reference r is the largest logit of the lanes' first
-// vectors.  A chunk whose terms overflow (a logit far above r) or hold a NaN
-// is re-read once and redone from its exact maximum.
+// Raises the offset to floor(xc2) if that is larger (and finite).
+__device__ __forceinline__ void raise_offset(SoftAcc& sa, float xc2) {
+  const float on = floorf(xc2);
+  if (on > sa.o && on < kInf) {
+    if (sa.o > -kInf) sa.z = ldexp(sa.z, (int)fmaxf(sa.o - on, -2000.0f));
+    sa.o = on;
+  }
+}
+
+struct SoftChunk {
+  float zt;  // the lane's sum of the chunk's terms 2^(x c2 - o)
+  float o;   // the offset o of those terms
+  float em;  // the chunk's largest term (wave-uniform; 0 if none)
+  bool ok;   // false: the chunk holds a NaN or +inf, or a logit whose x c2 overflows fp32
+};
+
+// Adds one chunk (held in buf, -inf past the row's end) to the lane sums.
+// A term is rounded in its exponent x c2 - o, so it is accurate to about
+// |x c2 - o| 2^-24 relative, and the largest terms, which dominate the sum,
+// need o close to the maximum.  The offset is the floor of the largest
+// x c2 of the wave's earlier chunks (for its first chunk, of the largest
+// logit of the lanes' first vectors); a chunk whose lane sums exceed 2^8 (a
+// logit well above that), or hold a NaN or inf, is re-read and redone from
+// its exact maximum.  The re-read keeps the first pass's registers free as
+// soon as each vector's terms are taken.
 template <int DT, bool VEC>
-__device__ __forceinline__ void plain_stats(uint4 (&buf)[kLoads], float c2, const char* row, int c0, int c1,
-                                            int lane, PlainStats& ps) {
+__device__ __forceinline__ SoftChunk soft_chunk(uint4 (&buf)[kLoads], float c2, const char* row, int c0, int c1,
+                                                int lane, bool first, SoftAcc& sa, float (&emax)[kLoads]) {
   constexpr int VE = Fmt<DT>::VE;
-  float r = -kInf;
+  SoftChunk out;
+  out.ok = true;
+  if (first) {
+    float r = -kInf;
 #pragma unroll
-  for (int k = 0; k < VE; ++k) r = fmaxf(r, elem<DT>(buf[0], k));
-  r = wave_max(r);
-  float o = r * c2;
-  float zt = 0.0f;
-  const bool ok = r > -kInf && r < kInf;  // false on NaN
-  if (ok) zt = exp_pass<DT>(buf, c2, o, ps.emax);
-  ps.st = 0;
-  if (!ok || __ballot(!(zt < kInf))) {
+    for (int k = 0; k < VE; ++k) r = fmaxf(r, elem<DT>(buf[0], k));
+    r = wave_max(r);
+    if (r > -kInf) raise_offset(sa, r * c2);
+  }
+  float em;
+  out.zt = exp_terms<DT>(buf, c2, sa.o, emax, &em);
+  if (__ballot(!(out.zt <= 256.0f)) != 0) {
     // rare: re-read the chunk
     load_chunk<DT, VEC>(buf, row, c0, c1, lane);
-    bool bad;
-    const float mx = chunk_max<DT>(buf, &bad);
-    ps.st = bad ? 2 : (mx == -kInf ? 1 : 0);
-    o = mx * c2;
-    zt = 0.0f;
-    if (ps.st == 0) zt = exp_pass<DT>(buf, c2, o, ps.emax);  // every term <= 2^delta now
-    else {
+    bool nf;
+    const float mx = chunk_max<DT>(buf, &nf);
+    out.zt = 0.0f;
+    em = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) ps.emax[i] = 0.0f;
+    for (int i = 0; i < kLoads; ++i) emax[i] = 0.0f;
+    if (nf) {
+      out.ok = false;
+      return out;
     }
-  }
-  float em = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) em = fmaxf(em, ps.emax[i]);
-  em = wave_max(em);
-  ps.o = o;
-  ps.zw = wave_sum((double)zt);
-  // the largest term 2^a belongs to the chunk maximum x = (a + o) / c2
-  ps.ma = ps.st == 0 ? ((double)log2f(em) + (double)o) * (1.0 / (double)c2) : -1e300;
-}
-
-// Finishes a plain / nucleus chunk.  A nucleus chunk lists every logit
-// x >= g - 10/c2, where g >= the chunk maximum is the largest maximum among
-// the chunks of the same row in this work-group (lists that overflow are
-// retried with 8 and 6); its vectors are flagged from their largest terms
-// with a 2^-8 margin in the exponent, a superset of those holding one.
-template <int DT>
-__device__ __forceinline__ void plain_finish(const KParams& P, const PlainStats& ps, float c2, bool cand,
-                                             double g, size_t slot, int c0, int lane, ChunkRec& rec) {
-  if (ps.st == 2) {
-    rec.flags |= kCfNonFinite;
-    return;
-  }
-  if (ps.st == 1) {
-    rec.m = -kInf;
-    rec.cut = -kInf;  // nothing finite: the (empty) candidate list is complete
-    return;
-  }
-  const float m = (float)ps.ma;
-  rec.m = m;
-  rec.o = ps.o;
-  // refer the sum to m: 2^(x c2 - o) = 2^((x - m) c2) 2^(m c2 - o)
-  // (the exponent is -log2 of the largest term, within [-2^7, 0]: fp32
-  // exp2 keeps the ~1e-7 relative error of the terms themselves)
-  rec.z = ps.zw * (double)exp2f((float)((double)ps.o - (double)m * (double)c2));
-  if (cand) {
-    int2* de = P.cent + slot * (size_t)P.cap;
-    int n = 0;
-    float cut = kInf;
-    const double ic2 = 1.0 / (double)c2;
-    for (int attempt = 0; attempt < 3; ++attempt) {
-      cut = (float)(g - (attempt == 0 ? kCandLog2 : attempt == 1 ? 8.0 : 6.0) * ic2);
-      // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
-      const float thr = exp2f((float)((double)cut * (double)c2 - (double)ps.o) - 0.00390625f);
-      uint32_t mask = 0;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) mask |= ps.emax[i] >= thr ? (1u << i) : 0u;
-      n = list_vectors(de, mask, ps.emax, c0, Fmt<DT>::VE, P.cap, lane);
-      if (n <= P.cap) break;
-    }
-    rec.cnt = n <= P.cap ? n : 0;
-    rec.cut = n <= P.cap ? cut : kInf;  // +inf: incomplete, the merge falls back to the full row
-  }
-}
-
-// Template mode of the streaming instance for calls with a per-sequence
-// mode array: every wave takes its own row's path, in one launch.
-constexpr int kAnyMode = 4;
-
-// Streaming pass: one wave per chunk.  The instance for MODE handles the
-// sequences whose sampling mode is MODE; those whose effective mode is plain
-// (top-p >= 1, top-k >= V) take the plain path.
-// Work-groups are handed to the 8 XCDs in turn (work-group j to XCD
-// j mod 8), and the sequence kernel's work-group b runs on XCD b mod 8.
-// When every sequence spans a whole number Q of streaming work-groups and
-// the launch holds a multiple of 8 sequences, hardware work-group j takes
-// the logical work-group that keeps all of sequence b's chunks on XCD
-// b mod 8 as well (a permutation of [0, 8 Q n)); otherwise the identity.
-__device__ __forceinline__ uint32_t xcd_logical_wg(uint32_t j, int nseq, int rs) {
-  constexpr uint32_t kXcd = 8;
-  constexpr int wpg = kThreads / kWave;  // waves (chunks) per streaming work-group
-  if (rs % wpg != 0 || nseq % (int)kXcd != 0) return j;
-  const uint32_t Q = (uint32_t)(rs / wpg);
-  const uint32_t x = j % kXcd, k = j / kXcd;
-  return (x + kXcd * (k / Q)) * Q + k % Q;
-}
-
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads, (MODE == SV_TOPK || MODE == kAnyMode) ? 3 : 1) void chunk_kernel(
-    const KParams P) {
-  constexpr int VE = Fmt<DT>::VE;
-  constexpr int kWaves = kThreads / kWave;
-  // which paths this instance holds
-  constexpr bool kAny = MODE == kAnyMode;
-  constexpr bool kTopk = MODE == SV_TOPK || kAny;
-  constexpr bool kGreedy = MODE == SV_GREEDY || kAny;
-  constexpr bool kTopp = MODE == SV_TOPP || kAny;
-  constexpr bool kPlain = MODE != SV_GREEDY;
-  // [0]: the top-k cut exchange, [1]: the nucleus window exchange
-  __shared__ float s_max[2][kWaves];
-  __shared__ int s_key[2][kWaves];
-  const int lane = (int)__lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  const int S = P.S, R = P.R;
-  const uint32_t gw = xcd_logical_wg(blockIdx.x, P.b_end - P.b_base, R * S) * (uint32_t)kWaves + (uint32_t)wv;
-  const int b = P.b_base + (int)(gw / (uint32_t)(R * S));
-  const int rem = (int)(gw % (uint32_t)(R * S));
-  const int r = rem / S, c = rem % S;
-  // no early return: the work-group meets at its barriers
-  bool active = b < P.b_end && (kAny || raw_mode(P, b) == MODE);
-  SeqParams sp{};
-  if (active) {
-    sp = load_params(P, b);
-    active = sp.valid;
-  }
-  bool tgt = false;
-  int t = 0;
-  if (active) active = decode_row(P, sp, r, &tgt, &t);  // padding rows are never read
-  const char* row = active ? static_cast<const char*>(row_ptr<DT>(P, b, tgt, t)) : nullptr;
-  const size_t slot = ((size_t)b * R + r) * S + c;
-  const int c0 = c * P.L;
-  const int c1 = min(P.V, c0 + P.L);
-  const float c2 = (float)sp.c2;
-  ChunkRec rec;
-  rec.m = -kInf;
-  rec.cut = kInf;
-  rec.z = 0.0;
-  rec.cnt = 0;
-  rec.arg = -1;
-  rec.flags = 0;
-  rec.o = 0.0f;
-  uint4 buf[kLoads];
-  if (active) load_chunk<DT, VEC>(buf, row, c0, c1, lane);
-
-  const bool is_topk = kTopk && active && sp.mode == SV_TOPK;  // wave-uniform
-  const bool special = is_topk || (kGreedy && active && sp.mode == SV_GREEDY);
-  float kcut = kInf;    // top-k: this chunk's own cut (+inf: none)
-  float vmax[kLoads];   // top-k: each vector's largest logit
-  if (special) {
-    bool bad;
-    const float mx = is_topk ? vector_maxima<DT>(buf, vmax, &bad) : chunk_max<DT>(buf, &bad);
-    rec.m = mx;
-    if (bad) {
-      rec.flags |= kCfNonFinite;
-    } else if (!is_topk) {  // greedy
-      int best = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i)
-#pragma unroll
-        for (int k = 0; k < VE; ++k)
-          if (elem<DT>(buf[i], k) == mx) best = min(best, c0 + (i * kWave + lane) * VE + k);
-      rec.arg = wave_min_i(best);
-    } else {
-      const int need = sp.topk, cap = P.cap;
-      // at most about 2k candidate vectors per chunk keep the row's list short
-      if (need <= cap) kcut = choose_cut(vmax, mx, 2.0f, need, min(cap, max(2 * need, 64)));
-    }
-  }
-  if constexpr (kTopk) {
-    // Each chunk lists against the largest cut among this work-group's
-    // chunks of the same row: the chunk that set it holds >= k vectors at
-    // or above it, every chunk's list stays complete above it, and no list
-    // grows (the shared cut is at least the chunk's own).
-    const bool hascut = is_topk && kcut != kInf;
-    if (lane == 0) {
-      s_key[0][wv] = hascut ? (int)(gw / (uint32_t)S) : -1;
-      s_max[0][wv] = hascut ? kcut : -kInf;
-    }
-    __syncthreads();
-    if (hascut) {
-      const int key = (int)(gw / (uint32_t)S);
-      float cut = kcut;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (s_key[0][w] == key) cut = fmaxf(cut, s_max[0][w]);
-      const int cap = P.cap;
-      const float c = fmaxf(cut, -kMaxFinite);
-      uint32_t mask = 0;
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= c ? (1u << i) : 0u;
-      const int n = list_vectors(P.cent + slot * (size_t)cap, mask, vmax, c0, VE, cap, lane);
-      rec.cnt = min(n, cap);
-      rec.cut = n <= cap ? cut : kInf;
-    }
-  }
-  if constexpr (kPlain) {
-    const bool plain = active && !special;
-    const bool cand = plain && kTopp && sp.mode == SV_TOPP;
-    PlainStats ps;
-    ps.st = 1;
-    ps.ma = -1e300;
-    if (plain) plain_stats<DT, VEC>(buf, c2, row, c0, c1, lane, ps);
-    double g = ps.ma;
-    if constexpr (kTopp) {
-      // the largest chunk maximum among this work-group's chunks of the same row
-      if (lane == 0) {
-        s_key[1][wv] = cand ? (int)(gw / (uint32_t)S) : -1;
-        s_max[1][wv] = ps.st == 0 ? (float)ps.ma : -kInf;
+    if (mx > -kInf) {
+      raise_offset(sa, mx * c2);
+      out.zt = exp_terms<DT>(buf, c2, sa.o, emax, &em);
+      if (__ballot(!(out.zt < kInf)) != 0) {
+        out.ok = false;
+        return out;
       }
-      __syncthreads();
-      const int key = cand ? (int)(gw / (uint32_t)S) : -2;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (s_key[1][w] == key) g = fmax(g, (double)s_max[1][w]);
     }
-    if (plain) plain_finish<DT>(P, ps, c2, cand, g, slot, c0, lane, rec);
   }
-  if (active && lane == 0) P.chunks[slot] = rec;
+  sa.z += (double)out.zt;
+  out.o = sa.o;
+  out.em = wave_max_nonneg(em);
+  if (out.em > 0.0f) {
+    // the chunk maximum x c2, from its largest term; the next chunk's offset
+    const float xc2 = __builtin_amdgcn_logf(out.em) + sa.o;
+    sa.lt = fmaxf(sa.lt, xc2);
+    raise_offset(sa, xc2);
+  }
+  return out;
 }
 
-// ===================================================== sequence kernel ====
-//
-// One work-group per sequence.  Wave w merges rows w, w + kSeqWaves, ... of
-// the sequence with wave-level operations only: log-sum-exp over the chunk
-// records, the top-k / nucleus threshold by radix selection over the
-// candidates cached in LDS, the probability of the row's draft token and,
-// for target rows, the kept set in vocabulary order.  After one barrier the
-// work-group runs the accept walk, finds the first rejection and draws the
-// resampled or bonus token.
-
-constexpr int kSeqThreads = kSeqWaves * kWave;
-constexpr int kRowCache = 768;   // candidate logits of one row held in LDS
-constexpr int kDrawTiles = 8;   // tiles of a row draw whose loads are in flight together
-constexpr int kVecList = 768;   // candidate vectors of one row that pass the row's cut
-constexpr int kMaxRows = 2 * kMaxK + 1;
+// ========================================================= selection ====
 
 // Orders the wave's LDS accesses (and keeps the compiler from moving them).
 __device__ __forceinline__ void wave_sync() {
@@ -747,26 +647,9 @@ __device__ __forceinline__ int wave_incl_scan_i(int v, int) {
   return wave_scan(v, 0, [](int a, int b) { return a + b; });
 }
 
-struct WaveSmem {
-  float cx[kRowCache];  // cached candidates: logit and vocabulary index;
-  int ci[kRowCache];    //   afterwards the kept set in vocabulary order
-  int vi[kVecList];     // first index of each candidate vector; afterwards
-                        //   the draft's logits at the kept set (float bits)
-  uint32_t hc[256];     // radix histogram: counts and fixed-point masses
+struct Hist {  // selection histogram: counts and fixed-point masses per digit
+  uint32_t hc[256];
   unsigned long long hm[256];
-  int pre[kWave];       // list start of each chunk of the current batch
-  float thr[kWave];     // key threshold of each chunk of the current batch
-};
-
-struct SmemSeq {
-  WaveSmem w[kSeqWaves];
-  RowRec rows[kMaxRows];
-  double rd[kSeqWaves];
-  int ri[kSeqWaves];
-  uint32_t misc[4];
-  double rx[2];
-  double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
-  double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
 };
 
 struct SelOut {
@@ -782,7 +665,7 @@ struct SelOut {
 // mass (nucleus) reaches `target`; without one (not reached), the lowest
 // non-empty digit.  Adds the exclusive sums at the digit to above_*, and
 // returns the digit with its own count and mass in last_*.
-__device__ __forceinline__ int pick_digit(const WaveSmem& ws, bool by_mass, unsigned long long target,
+__device__ __forceinline__ int pick_digit(const Hist& ws, bool by_mass, unsigned long long target,
                                           unsigned long long& above_c, unsigned long long& above_m,
                                           unsigned long long& last_c, unsigned long long& last_m, bool& reached,
                                           int lane) {
@@ -839,7 +722,7 @@ __device__ __forceinline__ int pick_digit(const WaveSmem& ws, bool by_mass, unsi
   return dg;
 }
 
-__device__ __forceinline__ void clear_histogram(WaveSmem& ws, int lane) {
+__device__ __forceinline__ void clear_histogram(Hist& ws, int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     ws.hc[lane + kWave * j] = 0;
@@ -854,7 +737,7 @@ __device__ __forceinline__ void clear_histogram(WaveSmem& ws, int lane) {
 // the result independent of the order of the atomic additions.  each(f)
 // calls f(x, mass) for this lane's share of the elements.
 template <int DT, class Each>
-__device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigned long long target, WaveSmem& ws,
+__device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigned long long target, Hist& ws,
                                               int lane) {
   const int levels = DT == SV_BF16 ? 2 : 4;
   uint32_t pkey = 0, pmask = 0;
@@ -894,20 +777,43 @@ __device__ __forceinline__ bool narrow_range(float lo, float hi) {
   return lo <= hi && (fkey(hi) >> 16) - (fkey(lo) >> 16) < 256u;
 }
 
+// Fixed-point mass of a logit, in units of the row's largest term:
+// 2^((x - M) c2) = 2^(x c2 - oM) 2^(oM - M c2), with oM = M c2 in fp32 and
+// the second factor (fM) exact in fp64.
+__device__ __forceinline__ unsigned long long mass_of(float x, float c2, float oM, double fM) {
+  return (unsigned long long)((double)__builtin_amdgcn_exp2f(fmaf(x, c2, -oM)) * fM * kFix + 0.5);
+}
+
+// The bf16 value whose 16-bit order key (fkey(x) >> 16) is k16.
+__device__ __forceinline__ float bf16_of_key(uint32_t k16) {
+  return key_value((k16 << 16) | ((k16 & 0x8000u) ? 0u : 0xFFFFu));
+}
+
 // The same selection as wave_select in one level, for bf16 elements in
-// [lo, hi] with narrow_range(lo, hi): digit 255 - (key(hi) - key).
+// [lo, hi] with narrow_range(lo, hi): digit 255 - (key(hi) - key).  Every
+// digit is one bf16 value, so the histogram counts elements only and each
+// digit's mass is its count times the value's mass (mass_of with c2, oM,
+// fM): the same integers as adding the elements' masses one by one.
 template <class Each>
-__device__ __forceinline__ SelOut select_narrow(Each&& each, bool by_mass, unsigned long long target, WaveSmem& ws,
-                                                int lane, float hi) {
+__device__ __forceinline__ SelOut select_narrow(Each&& each, bool by_mass, unsigned long long target, Hist& ws,
+                                                int lane, float hi, float c2, float oM, double fM) {
   const uint32_t kb = (fkey(hi) >> 16) - 255u;  // the key of digit 0
   unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
   bool reached = true;
-  clear_histogram(ws, lane);
-  each([&](float x, unsigned long long m) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ws.hc[lane + kWave * j] = 0;
+  wave_sync();
+  each([&](float x, unsigned long long) {
     const uint32_t dg = min(255u, (fkey(x) >> 16) - kb);  // the bound only guards the index
     atomicAdd(&ws.hc[dg], 1u);
-    atomicAdd(&ws.hm[dg], m);
   });
+  wave_sync();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int dg = lane + kWave * j;
+    const uint32_t c = ws.hc[dg];
+    ws.hm[dg] = c ? (unsigned long long)c * mass_of(bf16_of_key(kb + (uint32_t)dg), c2, oM, fM) : 0ull;
+  }
   wave_sync();
   const int dg = pick_digit(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
   wave_sync();
@@ -925,128 +831,12 @@ __device__ __forceinline__ SelOut select_narrow(Each&& each, bool by_mass, unsig
 // Selection over elements known to lie in [lo, hi].
 template <int DT, class Each>
 __device__ __forceinline__ SelOut select_bounded(Each&& each, bool by_mass, unsigned long long target,
-                                                 WaveSmem& ws, int lane, float lo, float hi) {
+                                                 Hist& ws, int lane, float lo, float hi, float c2, float oM,
+                                                 double fM) {
   if constexpr (DT == SV_BF16) {
-    if (narrow_range(lo, hi)) return select_narrow(each, by_mass, target, ws, lane, hi);
+    if (narrow_range(lo, hi)) return select_narrow(each, by_mass, target, ws, lane, hi, c2, oM, fM);
   }
   return wave_select<DT>(each, by_mass, target, ws, lane);
-}
-
-// Fixed-point mass of a logit, in units of the row's largest term:
-// 2^((x - M) c2) = 2^(x c2 - oM) 2^(oM - M c2), with oM = M c2 in fp32 and
-// the second factor (fM) exact in fp64.
-__device__ __forceinline__ unsigned long long mass_of(float x, float c2, float oM, double fM) {
-  return (unsigned long long)((double)__builtin_amdgcn_exp2f(fmaf(x, c2, -oM)) * fM * kFix + 0.5);
-}
-
-// Collects, in list order (chunk, vector, lane: increasing vocabulary
-// index), the first index of every listed candidate vector of the row whose
-// key reaches the threshold of its chunk for the cut Cu, into ws.vi;
-// returns how many there are (entries beyond kVecList are counted only).
-// keep_keys also stores each kept entry's key in ws.cx.  The key of a
-// nucleus vector is its largest term 2^(x c2 - o_chunk) (the
-// threshold 2^(Cu c2 - o_chunk - 2^-8) keeps every vector holding x >= Cu);
-// that of a top-k vector its largest logit (threshold Cu).
-template <class RecAt>
-__device__ __forceinline__ int filter_listed(const KParams& P, size_t slot0, RecAt&& rec_at, float Cu, float c2,
-                                             bool terms, int lane, WaveSmem& ws, bool keep_keys = false) {
-  constexpr int kBatch = 16;
-  const int S = P.S;
-  const uint64_t below = (1ull << lane) - 1ull;
-  int nv = 0;
-  for (int s0 = 0; s0 < S; s0 += kWave) {
-    const int s = s0 + lane;
-    int cnt = 0;
-    float th = -kInf;
-    if (s < S) {
-      const ChunkRec c = rec_at(s);
-      cnt = c.cnt;
-      th = terms ? exp2f((float)((double)Cu * (double)c2 - (double)c.o) - 0.00390625f) : Cu;
-    }
-    const int inc = wave_incl_scan_i(cnt, lane);
-    const int tot = lane63(inc);
-    const int pre = inc - cnt;  // list start of chunk s0 + lane
-    wave_sync();
-    ws.pre[lane] = pre;
-    ws.thr[lane] = th;
-    wave_sync();
-    const int nb = min(kWave, S - s0);
-    // The chunk of list position fi is the last non-empty chunk whose list
-    // starts at or before fi.  Non-empty chunks start at distinct positions,
-    // so with a bitmap of those starts the chunk's rank among the non-empty
-    // ones is a popcount, and a table maps the rank to the chunk.  The
-    // bitmap (ws.hm) and the table (ws.hc) borrow the histogram arrays,
-    // which every selection clears before use.
-    const bool nonempty = lane < nb && cnt > 0;
-    const uint64_t neb = __ballot(nonempty);
-    const int nne = __popcll(neb);
-    if (nonempty) ws.hc[__popcll(neb & below)] = (uint32_t)lane;
-    for (int f0 = 0; f0 < tot; f0 += kBatch * kWave) {
-      int2 ent[kBatch];
-      int ch[kBatch];
-      if (lane < kBatch) ws.hm[lane] = 0ull;
-      wave_sync();
-      const int rel = pre - f0;
-      if (nonempty && rel >= 0 && rel < kBatch * kWave) atomicOr(&ws.hm[rel >> 6], 1ull << (rel & 63));
-      wave_sync();
-      int base = __popcll(__ballot(nonempty && pre < f0)) - 1;  // rank of the chunk holding f0 - 1
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const unsigned long long wq = ws.hm[q];
-        // (readfirstlane returns int: go through uint32_t, or the low word
-        // would be sign-extended)
-        const uint64_t word = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(wq >> 32)) << 32) |
-                              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wq);
-        // set bits of the word at positions <= lane: those below it (mbcnt
-        // counts a scalar mask's bits below the lane) plus the lane's own
-        const int below_n = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
-        const int r = base + below_n + (int)((word >> lane) & 1ull);
-        ch[q] = (int)ws.hc[max(0, min(r, nne - 1))];
-        base += __popcll(word);
-      }
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const int fi = f0 + q * kWave + lane;
-        ent[q] = make_int2(0, 0);
-        if (fi < tot) ent[q] = P.cent[(slot0 + s0 + ch[q]) * (size_t)P.cap + min(fi - ws.pre[ch[q]], P.cap - 1)];
-      }
-      float th[kBatch];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) th[q] = ws.thr[ch[q]];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const bool pass = f0 + q * kWave + lane < tot && __int_as_float(ent[q].y) >= th[q];
-        const uint64_t bal = __ballot(pass);
-        if (pass) {
-          const int pos = nv + __popcll(bal & below);
-          if (pos < kVecList) {
-            ws.vi[pos] = ent[q].x;
-            if (keep_keys) ws.cx[pos] = __int_as_float(ent[q].y);  // kRowCache >= kVecList
-          }
-        }
-        nv += __popcll(bal);
-      }
-    }
-    wave_sync();
-  }
-  return nv;
-}
-
-// Loads candidate vectors ws.vi[j0 + q * 64 + lane] (< nv) into registers.
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_candidates(const KParams& P, const char* row, int j0, int nv, int lane,
-                                                const WaveSmem& ws, uint4 (&v)[4], int (&e0)[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = j0 + q * kWave + lane;
-    e0[q] = j < nv ? ws.vi[j] : 0;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    v[q] = make_uint4(0, 0, 0, 0);
-    if (j0 + q * kWave + lane < nv) v[q] = load_vec<DT, VEC>(row, e0[q], P.V);
-  }
 }
 
 // Appends the logits >= c of one vector per lane to (dx, di) at *n, in
@@ -1055,14 +845,13 @@ template <int DT>
 __device__ __forceinline__ void append_ge(bool have, const uint4& v, int e0, float c, int lane, float* dx, int* di,
                                           int cap, int* n) {
   constexpr int VE = Fmt<DT>::VE;
-  const uint64_t below = (1ull << lane) - 1ull;
   bool pass[VE];
   int before = 0, total = 0;
 #pragma unroll
   for (int k = 0; k < VE; ++k) {
     pass[k] = have && elem<DT>(v, k) >= c;
     const uint64_t bal = __ballot(pass[k]);
-    before += __popcll(bal & below);  // passing logits of the lower lanes
+    before += lanes_below(bal);  // passing logits of the lower lanes
     total += __popcll(bal);
   }
   int pos = *n + before;
@@ -1079,102 +868,584 @@ __device__ __forceinline__ void append_ge(bool have, const uint4& v, int e0, flo
   *n += total;
 }
 
-// Merges logit row r of sequence b into sm.rows[r] (one wave).
+// ========================================================== row kernel ====
+//
+// One work-group of kRowWaves waves per logit row.  Wave w streams the w-th
+// quarter of the row's chunks, one chunk at a time into registers; the
+// candidate vectors of a top-k / nucleus kept set go to the wave's part of
+// an LDS buffer, so the buffer holds them in vocabulary order.  The waves
+// share their running maxima (nucleus) or cuts (top-k) through LDS without
+// waiting for each other: a value read early is only lower, which lists
+// more, never fewer, candidates.  After one barrier, wave 0 finishes the
+// row.
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// Template mode of the row kernel for calls with a per-sequence mode array:
+// every work-group takes its own row's path, in one launch.
+constexpr int kAnyMode = 4;
+// What one wave of the row kernel found over its part of the row.
+struct WaveRec {
+  double z;        // plain / nucleus: the sum of 2^(x c2 - o) over the wave's logits
+  float m;         // the largest logit (-inf if none is finite)
+  float o;         // the exponent offset of z
+  int arg;         // greedy: the lowest index holding m
+  uint32_t flags;  // kCfNonFinite
+};
+
+struct RowSmem {
+  uint4 cv[kRowWaves][kCandVecs];  // candidate vectors of each wave, in vocabulary order
+  int ci[kRowWaves][kCandVecs];    // the vocabulary index of each one's first logit
+  float ck[kRowWaves][kCandVecs];  // while listing: the largest logit of each vector (within 2^-8 / c2)
+  WaveRec wrec[kRowWaves];         // each wave's record
+  Hist h;
+  float kx[kListMax];              // the kept set in vocabulary order: logits
+  int ki[kListMax];                //   and vocabulary indices
+  float pub[kRowWaves];            // each wave's running maximum (nucleus) or cut (top-k)
+  float ucut[kRowWaves];           // the largest listing cut each wave used
+  int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
+  SelOut sel;                      // the finish: a selection's result, for every wave
+  int seldg;                       //   a selection level's digit
+  int wsum[kRowWaves];             //   each wave's part of a work-group sum
+};
+
+__device__ __forceinline__ float lds_load_relaxed(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store_relaxed(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// The largest value the row's waves have published so far.
+__device__ __forceinline__ float published_max(const RowSmem& sm) {
+  float g = -kInf;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) g = fmaxf(g, lds_load_relaxed(&sm.pub[w]));
+  return g;
+}
+
+// Lists the lane's vectors flagged in `mask` (slot i holds logits
+// c0 + (i * 64 + lane) * VE + [0, VE)) in the wave's LDS list from position
+// n, as (first vocabulary index, key), in (slot, lane) order, which is
+// increasing vocabulary index.  Returns the new count; entries beyond
+// kCandVecs are counted, not stored.
+__device__ __forceinline__ int list_vectors(RowSmem& sm, int wv, int n, uint32_t mask, const float (&key)[kLoads],
+                                            int c0, int ve, int lane) {
+  const int e0 = c0 + lane * ve;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const bool h = (mask >> i) & 1u;
+    const uint64_t bal = __ballot(h);
+    if (bal) {  // slots with no flagged vector cost one ballot
+      if (h) {
+        const int pos = n + lanes_below(bal);
+        if (pos < kCandVecs) {
+          sm.ci[wv][pos] = e0 + i * kWave * ve;
+          sm.ck[wv][pos] = key[i];
+        }
+      }
+      n += __popcll(bal);
+    }
+  }
+  return n;
+}
+
+// Keeps the first n listed vectors of the wave whose key reaches `cut`, in
+// order (in place: positions only move down); returns how many.
+__device__ __forceinline__ int compact_listed(RowSmem& sm, int wv, int n, float cut, int lane) {
+  int m = 0;
+  for (int j0 = 0; j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool keep = j < n && sm.ck[wv][j] >= cut;
+    const int idx = j < n ? sm.ci[wv][j] : 0;
+    const float key = j < n ? sm.ck[wv][j] : 0.0f;
+    const uint64_t bal = __ballot(keep);
+    wave_sync();
+    if (keep) {
+      sm.ci[wv][m + lanes_below(bal)] = idx;
+      sm.ck[wv][m + lanes_below(bal)] = key;
+    }
+    m += __popcll(bal);
+    wave_sync();
+  }
+  return m;
+}
+
+// Number of the wave's first n listed vectors whose key reaches t.
+__device__ __forceinline__ int count_listed(const RowSmem& sm, int wv, int n, float t, int lane) {
+  int m = 0;
+  for (int j0 = 0; j0 < n; j0 += kWave) m += __popcll(__ballot(j0 + lane < n && sm.ck[wv][j0 + lane] >= t));
+  return m;
+}
+
+// Top-k: a cut t >= cut such that at least `need` of the wave's first n
+// listed vectors have a key (their largest logit) >= t, and as few more as
+// the search finds: k vectors each holding a logit >= t make t a lower
+// bound of the row's k-th largest logit.  Bisection between cut and the
+// largest key; returns cut when no higher value keeps `need` of them.
+__device__ __forceinline__ float raise_cut(const RowSmem& sm, int wv, int n, float cut, int need, int lane) {
+  float top = -kInf;
+  for (int j = lane; j < n; j += kWave) top = fmaxf(top, sm.ck[wv][j]);
+  top = wave_max(top);
+  float lo = cut, hi = top;  // count(lo) >= need is not known: lo is kept only if it is the best found
+  float best = cut;
+  if (!(hi > lo)) return cut;
+  if (count_listed(sm, wv, n, hi, lane) >= need) return hi;
+  for (int it = 0; it < 30; ++it) {
+    const float mid = 0.5f * (lo + hi);
+    if (!(mid > lo && mid < hi)) break;
+    const int m = count_listed(sm, wv, n, mid, lane);
+    if (m >= need) {
+      best = mid;
+      lo = mid;
+      if (m <= 2 * need) break;
+    } else {
+      hi = mid;
+    }
+  }
+  return best;
+}
+
+// After a wave's last chunk: keeps its listed vectors whose key reaches
+// `cut`, in order, and loads them from the row into the wave's part of the
+// LDS buffer (all loads of a lane in flight together).  Returns how many.
 template <int DT, bool VEC>
-__device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp, int b, int r, int lane,
-                                          WaveSmem& ws, RowRec& out) {
-  const int S = P.S;
+__device__ __forceinline__ int gather_listed(RowSmem& sm, int wv, int n, float cut, const char* row, int V, int lane) {
+  constexpr int Q = kCandVecs / kWave;
+  const int m = compact_listed(sm, wv, n, cut, lane);
+  uint4 v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = q * kWave + lane;
+    v[q] = make_uint4(0, 0, 0, 0);
+    if (j < m) v[q] = load_vec<DT, VEC>(row, sm.ci[wv][j], V);
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = q * kWave + lane;
+    if (j < m) sm.cv[wv][j] = v[q];
+  }
+  return m;
+}
+
+template <int DT>
+__device__ __forceinline__ float vector_max(const uint4& v) {
+  float m = -kInf;
+#pragma unroll
+  for (int k = 0; k < Fmt<DT>::VE; ++k) m = fmaxf(m, elem<DT>(v, k));
+  return m;
+}
+
+// ---- the finish's selection, over the whole work-group ----
+//
+// The same selections as select_bounded, with the histogram filled by all
+// kThreads threads (one bin per thread to clear) and each digit picked by
+// wave 0 and passed to the others through LDS.  each(f, with_mass) calls
+// f(x, mass) for this thread's share of the elements (mass only when
+// with_mass is set).
+template <int DT, class Each>
+__device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned long long target, RowSmem& sm,
+                                            int tid, int wv, int lane, float lo, float hi, float c2, float oM,
+                                            double fM) {
+  static_assert(kThreads == 256, "one histogram bin per thread");
+  unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
+  bool reached = true;
+  if (DT == SV_BF16 && narrow_range(lo, hi)) {
+    // one level: every digit is one bf16 value (see select_narrow)
+    const uint32_t kb = (fkey(hi) >> 16) - 255u;
+    sm.h.hc[tid] = 0;
+    __syncthreads();
+    each([&](float x, unsigned long long) { atomicAdd(&sm.h.hc[min(255u, (fkey(x) >> 16) - kb)], 1u); }, false);
+    __syncthreads();
+    const uint32_t c = sm.h.hc[tid];
+    sm.h.hm[tid] = c ? (unsigned long long)c * mass_of(bf16_of_key(kb + (uint32_t)tid), c2, oM, fM) : 0ull;
+    __syncthreads();
+    if (wv == 0) {
+      const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+      if (lane == 0) {
+        uint32_t pkey = (kb + (uint32_t)dg) << 16;
+        pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
+        sm.sel.T = key_value(pkey);
+        sm.sel.reached = reached;
+        sm.sel.n_keep = (uint32_t)(above_c + last_c);
+        sm.sel.m_keep = above_m + last_m;
+        sm.sel.m_above = above_m;
+      }
+    }
+    __syncthreads();
+    return sm.sel;
+  }
+  // MSB-first 8-bit digits over the 32-bit keys (bf16: the top 16 bits)
+  const int levels = DT == SV_BF16 ? 2 : 4;
+  uint32_t pkey = 0, pmask = 0;
+  for (int lv = 0; lv < levels; ++lv) {
+    const int shift = 24 - 8 * lv;
+    sm.h.hc[tid] = 0;
+    sm.h.hm[tid] = 0;
+    __syncthreads();
+    each(
+        [&](float x, unsigned long long m) {
+          const uint32_t key = fkey(x);
+          if ((key & pmask) == pkey) {
+            const uint32_t dg = (key >> shift) & 255u;
+            atomicAdd(&sm.h.hc[dg], 1u);
+            atomicAdd(&sm.h.hm[dg], m);
+          }
+        },
+        true);
+    __syncthreads();
+    if (wv == 0) {
+      const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+      if (lane == 0) sm.seldg = dg;
+    }
+    __syncthreads();
+    pkey |= (uint32_t)sm.seldg << shift;
+    pmask |= 255u << shift;
+  }
+  if (DT == SV_BF16) pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
+  if (wv == 0 && lane == 0) {
+    sm.sel.T = key_value(pkey);
+    sm.sel.reached = reached;
+    sm.sel.n_keep = (uint32_t)(above_c + last_c);
+    sm.sel.m_keep = above_m + last_m;
+    sm.sel.m_above = above_m;
+  }
+  __syncthreads();
+  return sm.sel;
+}
+
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
+  constexpr int VE = Fmt<DT>::VE;
+  constexpr bool kAny = MODE == kAnyMode;
+  __shared__ RowSmem sm;
+  const int lane = (int)__lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int R = P.R, S = P.S;
+  const int b = P.b_base + (int)(blockIdx.x / (uint32_t)R);
+  const int r = (int)(blockIdx.x % (uint32_t)R);
+  // Whole work-groups return here, before any barrier.
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid) return;  // the sequence kernel reports the parameter error
   bool tgt;
   int t;
-  const bool used = decode_row(P, sp, r, &tgt, &t);
+  if (!decode_row(P, sp, r, &tgt, &t)) return;  // padding rows are never read
+  if (!tgt && P.draft == nullptr) return;        // greedy calls without draft logits
+  // the row's filter (work-group uniform)
+  // (a greedy instance only ever sees greedy rows: the mode is never remapped)
+  const bool is_greedy = MODE == SV_GREEDY || (kAny && sp.mode == SV_GREEDY);
+  const bool is_topk = (MODE == SV_TOPK || kAny) && sp.mode == SV_TOPK;
+  const bool is_topp = (MODE == SV_TOPP || kAny) && sp.mode == SV_TOPP;
+  const bool is_plain = !is_greedy && !is_topk && !is_topp;
+  const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
+  const size_t rid = (size_t)b * R + r;
+  const size_t slot0 = rid * S;
+  const float c2 = (float)sp.c2;
+  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
+  const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
+  // the draft token's logit, for the finish (loaded now, while the row streams)
+  const float xtok = (tok_ok && threadIdx.x == 0) ? load_logit<DT>(row, tok) : 0.0f;
+  if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
+  __syncthreads();
+
+  // ---- streaming: wave wv takes chunks [cb, ce) ----
+  // Each lane accumulates over all of the wave's chunks on its own (softmax
+  // sums, maxima, the greedy candidate); the wave reduces once, after its
+  // last chunk.  Only the top-k and nucleus candidate lists, and the chunk
+  // sums of plain target rows, are built chunk by chunk.
+  const int per = (S + kRowWaves - 1) / kRowWaves;
+  const int cb = min(S, wv * per), ce = min(S, cb + per);
+  int nc = 0;            // candidate vectors listed by this wave
+  bool over = false;     // the wave's candidate buffer overflowed
+  float run = -kInf;     // this wave's running maximum (nucleus) or cut (top-k)
+  float ucut = -kInf;    // the largest listing cut this wave used
+  const double ic2 = uniform_d(1.0 / (double)c2);
+  const float ic2f = (float)ic2;
+  const bool chunk_sums = is_plain && tgt;  // the bonus draw of a plain row locates its chunk
+  bool bad = false;      // wave-uniform: a NaN or +inf was seen
+  SoftAcc sa;            // plain / nucleus
+  sa.z = 0.0;
+  sa.o = -kInf;
+  sa.lt = -kInf;
+  float lmax = -kInf;    // greedy: the lane's largest logit; top-k: the wave's
+  int lvec = -1;         // greedy: first index of the lane's first vector holding lmax
+  // Reduces chunk c, held in buf (its tail masked first when the row ends
+  // inside it and `mask` is set).
+  auto do_chunk = [&](const int c, uint4 (&buf)[kLoads], bool mask) {
+    const int c0 = c * P.L, c1 = min(P.V, c0 + P.L);
+    const int ln = fresh_lane(lane);
+    if (mask && c1 - c0 < P.L) mask_chunk<DT>(buf, c0, c1, ln);
+    if (bad) return;
+    if (is_greedy) {
+      int nf = 0;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        float m = -kInf;
+#pragma unroll
+        for (int k = 0; k < VE; ++k) {
+          const float x = elem<DT>(buf[i], k);
+          m = fmaxf(m, x);
+          nf |= !(x < kInf);
+        }
+        // strictly larger: the lane's earlier vector (lower index) keeps ties
+        if (m > lmax) {
+          lmax = m;
+          lvec = c0 + (i * kWave + ln) * VE;
+        }
+      }
+      bad = __ballot(nf) != 0;
+    } else if (is_topk) {
+      float vmax[kLoads];
+      bool nf;
+      const float mx = vector_maxima<DT>(buf, vmax, &nf);
+      if (nf) {
+        bad = true;
+        return;
+      }
+      lmax = fmaxf(lmax, mx);
+      if (over) return;
+      // Every cut published so far is a lower bound of the row's k-th
+      // largest logit (some chunk holds k vectors at or above it); this
+      // chunk may raise it with its own.
+      float cut = fmaxf(run, published_max(sm));
+      const int need = sp.topk;
+      const int capk = min(kCandVecs, max(2 * need, 64));
+      // a chunk with many vectors above the cut raises it with its own
+      if (mx > cut && need <= kCandVecs && count_vectors_ge(vmax, cut) > capk) {
+        const float kc = choose_cut(vmax, mx, 2.0f, need, capk);
+        if (kc < kInf) cut = fmaxf(cut, kc);
+      }
+      run = cut;
+      if (lane == 0) lds_store_relaxed(&sm.pub[wv], run);
+      const float cf = fmaxf(cut, -kMaxFinite);  // -inf logits are never candidates
+      uint32_t mask = 0;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= cf ? (1u << i) : 0u;
+      int n = list_vectors(sm, wv, nc, mask, vmax, c0, VE, ln);
+      if (n > kCandVecs) {
+        // Raise the cut to the need-th largest listed key (or near it),
+        // drop the entries below it, and list the chunk again.
+        wave_sync();
+        cut = raise_cut(sm, wv, nc, cut, need, ln);
+        nc = compact_listed(sm, wv, nc, cut, ln);
+        run = cut;
+        if (lane == 0) lds_store_relaxed(&sm.pub[wv], run);
+        const float cf2 = fmaxf(cut, -kMaxFinite);
+        mask = 0;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= cf2 ? (1u << i) : 0u;
+        n = list_vectors(sm, wv, nc, mask, vmax, c0, VE, ln);
+      }
+      if (n > kCandVecs) over = true;
+      else nc = n;
+      ucut = fmaxf(ucut, cut);
+    } else {
+      float emax[kLoads];
+      const SoftChunk ch = soft_chunk<DT, VEC>(buf, c2, row, c0, c1, ln, c == cb, sa, emax);
+      if (!ch.ok) {
+        bad = true;
+        return;
+      }
+      if (chunk_sums) {
+        const double zc = wave_sum((double)ch.zt);
+        if (lane == 0) {
+          ChunkRec cr;
+          cr.z = zc;
+          cr.o = ch.o;
+          cr.pad = 0;
+          P.chunks[slot0 + c] = cr;
+        }
+      }
+      if (is_topp && !over) {
+        // the chunk maximum, from its largest term
+        const double ma = ch.em > 0.0f ? ((double)__builtin_amdgcn_logf(ch.em) + (double)ch.o) * ic2 : -1e300;
+        // list every vector holding a logit >= g - 10/c2, g the largest
+        // chunk maximum known; a list that would overflow the buffer is
+        // first compacted against g, then retried with 8 and 6
+        const double g = fmax(fmax((double)run, ma), (double)published_max(sm));
+        bool done = false;
+        float cut = kInf;
+        for (int attempt = 0; attempt < 4 && !done; ++attempt) {
+          if (attempt == 1) {
+            // drop the entries the raised maximum has left behind (keys
+            // are within 2^-8 / c2 of their vectors' maxima)
+            nc = compact_listed(sm, wv, nc, (float)(g - kCandLog2 * ic2 - 0.00390625 * ic2), ln);
+          }
+          cut = (float)(g - (attempt <= 1 ? kCandLog2 : attempt == 2 ? 8.0 : 6.0) * ic2);
+          // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
+          // (the exponent is >= -10.01: o never exceeds g c2)
+          const float thr = __builtin_amdgcn_exp2f((float)((double)cut * (double)c2 - (double)ch.o) - 0.00390625f);
+          uint32_t mask = 0;
+          float key[kLoads];  // the vector's largest logit, from its largest term (fp32 suffices)
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) {
+            mask |= emax[i] >= thr ? (1u << i) : 0u;
+            key[i] = (__builtin_amdgcn_logf(emax[i]) + ch.o) * ic2f;  // only read where emax[i] >= thr
+          }
+          const int n = list_vectors(sm, wv, nc, mask, key, c0, VE, ln);
+          if (n <= kCandVecs) {
+            nc = n;
+            done = true;
+          }
+        }
+        if (!done) over = true;
+        ucut = fmaxf(ucut, cut);
+        run = fmaxf(run, (float)ma);
+        if (lane == 0) lds_store_relaxed(&sm.pub[wv], run);
+      }
+    }
+  };
+  if constexpr (VEC) {
+    // Two chunk buffers: the loads of chunk c + 1 are in flight while chunk
+    // c is reduced, so that every wave keeps memory busy.
+    // The next chunk's loads are issued whether or not it exists (then at
+    // the row's end, where they read nothing), so that the number of loads
+    // in flight is always the same and each wait is for one chunk only.
+    constexpr int ES = Fmt<DT>::ES;
+    const int row_bytes = P.V * ES;
+    const __amdgpu_buffer_rsrc_t rs = row_resource(row, row_bytes);
+    auto off = [&](int cc) { return cc < ce ? cc * P.L * ES : row_bytes; };
+    uint4 A[kLoads], B[kLoads];
+    int c = cb;
+    issue_chunk<DT>(A, rs, off(c), lane);
+    while (c < ce) {
+      issue_chunk<DT>(B, rs, off(c + 1), lane);
+      do_chunk(c, A, true);
+      if (++c >= ce) break;
+      issue_chunk<DT>(A, rs, off(c + 1), lane);
+      do_chunk(c, B, true);
+      ++c;
+    }
+  } else {
+    for (int c = cb; c < ce; ++c) {
+      uint4 buf[kLoads];
+      load_chunk<DT, VEC>(buf, row, c * P.L, min(P.V, c * P.L + P.L), lane);
+      do_chunk(c, buf, false);
+    }
+  }
+  if ((is_topk || is_topp) && !over && nc > 0) {
+    // Keep the listed vectors that can still hold a kept token and load
+    // them: for top-k those at or above the largest cut published, for a
+    // nucleus those within 10 log2 units of the largest chunk maximum
+    // known (keys are within 2^-8 / c2 of the vectors' maxima).
+    const float g = fmaxf(run, published_max(sm));
+    const float fcut = is_topk ? g : (float)((double)g - kCandLog2 * ic2);
+    nc = gather_listed<DT, VEC>(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), row, P.V,
+                                lane);
+    ucut = fmaxf(ucut, fcut);
+  }
+  {
+    // the wave's record
+    WaveRec wr;
+    wr.z = 0.0;
+    wr.m = -kInf;
+    wr.o = 0.0f;
+    wr.arg = 0x7fffffff;
+    wr.flags = bad ? kCfNonFinite : 0u;
+    if (!bad) {
+      if (is_greedy) {
+        // the lowest index of the lane's maximum, in its first vector holding it
+        int idx = 0x7fffffff;
+        if (lvec >= 0) {
+          const uint4 v = load_vec<DT, VEC>(row, lvec, P.V);
+#pragma unroll
+          for (int k = VE - 1; k >= 0; --k)
+            if (elem<DT>(v, k) == lmax) idx = lvec + k;
+        }
+        wr.m = wave_max(lmax);
+        wr.arg = wave_min_i(lmax == wr.m ? idx : 0x7fffffff);
+      } else if (is_topk) {
+        wr.m = lmax;
+      } else {
+        wr.m = sa.lt > -kInf ? (float)((double)sa.lt * ic2) : -kInf;
+        wr.z = wave_sum(sa.z);
+        wr.o = sa.o;
+      }
+    }
+    if (lane == 0) {
+      sm.wrec[wv] = wr;
+      sm.ncand[wv] = over ? -1 : nc;
+      sm.ucut[wv] = ucut;
+    }
+  }
+  __syncthreads();
+
+  // ---- finish ----
+  // Every wave derives the row's statistics from the wave records; the
+  // selection and the kept list of a top-k / nucleus row use the whole
+  // work-group, other rows only wave 0.
+  const int tid = (int)threadIdx.x;
   RowRec rr;
   rr.M = -kInf;
   rr.T = -kInf;
-  rr.c2 = (double)(float)sp.c2;
+  rr.c2 = (double)c2;
   rr.Zs = 1.0;
   rr.pid = __builtin_nan("");
   rr.g = -1;
   rr.n_keep = -1;
   rr.flags = 0;
   rr.pad = 0;
-  if (!used) {
-    if (lane == 0) out = rr;
-    return;
-  }
-  const void* row = row_ptr<DT>(P, b, tgt, t);
-  const size_t rowid = (size_t)b * P.R + r;
-  const size_t slot0 = rowid * S;
-  const int mode = sp.mode;
-  const float c2 = (float)sp.c2;
-  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
-  const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
-  const float xtok = tok_ok ? load_logit<DT>(row, tok) : 0.0f;  // issued early
-
-  // chunk records: held in registers when the row has at most 64 chunks
-  const ChunkRec* crec = P.chunks + slot0;
-  const bool small = S <= kWave;
-  ChunkRec mine;
-  mine.m = -kInf;
-  mine.cut = -kInf;
-  mine.z = 0.0;
-  mine.cnt = 0;
-  mine.arg = 0x7fffffff;
-  mine.flags = 0;
-  mine.o = 0.0f;
-  if (small && lane < S) mine = crec[lane];
-  auto recs = [&](auto&& f) {
-    if (small) {
-      if (lane < S) f(mine);
-    } else {
-      for (int s = lane; s < S; s += kWave) f(crec[s]);
-    }
-  };
   float mx = -kInf;
   uint32_t fl = 0;
-  recs([&](const ChunkRec& c) {
-    mx = fmaxf(mx, c.m);
-    fl |= c.flags;
-  });
-  const float M = wave_max(mx);
-  fl = wave_or_u(fl);
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    mx = fmaxf(mx, sm.wrec[w].m);
+    fl |= sm.wrec[w].flags;
+  }
+  const float M = mx;
   rr.M = M;
   if ((fl & kCfNonFinite) || !(M < kInf) || isnan(M)) rr.flags |= SV_ST_NONFINITE;
   else if (M == -kInf) rr.flags |= SV_ST_EMPTY;
 
   double Z = 0.0;
-  if (!(rr.flags & kErrBits) && (mode == SV_PLAIN || mode == SV_TOPP)) {
-    double term = 0.0;
-    recs([&](const ChunkRec& c) {
-      if (c.m > -kInf) term += c.z * exp2(((double)c.m - (double)M) * (double)c2);
-    });
-    Z = wave_sum(term);
+  if (!(rr.flags & kErrBits) && (is_plain || is_topp)) {
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const WaveRec& c = sm.wrec[w];
+      if (c.m > -kInf) Z += c.z * exp2((double)c.o - (double)M * (double)c2);
+    }
     if (!(Z > 0.0) || !(Z < 1e300)) rr.flags |= SV_ST_NONFINITE;
+    else if (chunk_sums) rr.flags |= kRfChunks;
   }
+  const bool selecting = !(rr.flags & kErrBits) && (is_topk || is_topp);  // work-group uniform
+  if (!selecting && wv != 0) return;
 
   const float oM = M * c2;
   const double fM = exp2_small((double)oM - (double)M * (double)c2);
   bool list_ok = false;
-  int src = 0;  // where the candidates >= the final cut lie: 1 registers, 2 LDS cache
-  int n = 0, nv = 0;
-  uint4 rv[4];  // candidate vectors held in registers (src 1)
-  int re[4];
+  // the candidate vectors: the waves' buffers one after another
+  int pre[kRowWaves + 1];
+  float C = -kInf;  // every token >= C lies in a listed vector (+inf: incomplete)
+  pre[0] = 0;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    const int n = sm.ncand[w];
+    if (n < 0) C = kInf;
+    else if (C < kInf) C = fmaxf(C, sm.ucut[w]);
+    pre[w + 1] = pre[w] + max(n, 0);
+  }
+  const int N = pre[kRowWaves];
+  auto vec_at = [&](int j, uint4& v, int& e0) {
+    const int w = (j >= pre[1]) + (j >= pre[2]) + (j >= pre[3]);
+    const int pos = j - (w == 0 ? 0 : w == 1 ? pre[1] : w == 2 ? pre[2] : pre[3]);
+    v = sm.cv[w][pos];
+    e0 = sm.ci[w][pos];
+  };
   if (!(rr.flags & kErrBits)) {
-    if (mode == SV_PLAIN) {
+    if (is_plain) {
       rr.Zs = Z;
-    } else if (mode == SV_GREEDY) {
+    } else if (is_greedy) {
       int best = 0x7fffffff;
-      recs([&](const ChunkRec& c) {
-        if (c.m == M) best = min(best, c.arg);
-      });
-      rr.g = wave_min_i(best);
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w)
+        if (sm.wrec[w].m == M) best = min(best, sm.wrec[w].arg);
+      rr.g = best;
       rr.T = M;
       rr.n_keep = 1;
     } else {
-      // every logit >= C of the row lies in a listed candidate vector
-      float cm = -kInf;
-      recs([&](const ChunkRec& c) { cm = fmaxf(cm, c.cut); });
-      const float C = wave_max(cm);
-      const bool by_mass = mode == SV_TOPP;
+      const bool by_mass = is_topp;
       unsigned long long target;
       if (by_mass) {
         const double tt = (double)sp.topp * Z * kFix;
@@ -1182,81 +1453,56 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
       } else {
         target = (unsigned long long)sp.topk;
       }
-      const char* rowc = static_cast<const char*>(row);
-      auto rec_at = [&](int s) { return small ? mine : crec[s]; };  // s = lane when small
-      // A nucleus first tries the cut 8 log2 units below the row maximum
-      // (its lists reach 10), then C.  The candidates >= the cut are held
-      // in registers (up to 256 vectors) or cached in LDS; the full row is
-      // re-read when they do not fit or the threshold falls below C.
-      SelOut so;
-      bool ok = false;
       // an upper bound of every logit of the row: M comes from the chunks'
       // largest terms, within a few ulps of the largest logit
       const float Mhi = M + (fabsf(M) + 1.0f) * 0.001953125f;
-      float C1 = by_mass ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
-      if (!by_mass && C < kInf) {
-        // top-k: the k-th largest logit is at least the k-th largest vector
-        // maximum (every vector holds its maximum), so that key bounds it
-        const int nk0 = min(filter_listed(P, slot0, rec_at, C, c2, false, lane, ws, true), kVecList);
-        const SelOut sk = select_bounded<DT>(
-            [&](auto&& f) {
-              for (int j = lane; j < nk0; j += kWave) f(ws.cx[j], 0ull);
+      // Candidates spanning fewer than 256 bf16 values take one histogram
+      // pass over all of them.  Otherwise a nucleus first tries the cut 8
+      // log2 units below the row maximum (the lists reach 10), then C, and
+      // top-k first selects the k-th largest vector key over the
+      // candidates: every vector holds its own maximum, so the k-th largest
+      // logit is at least that key.
+      const bool narrow = DT == SV_BF16 && C < kInf && narrow_range(fmaxf(C, -kMaxFinite), Mhi);
+      float C1 = (by_mass && !narrow) ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
+      if (!by_mass && !narrow && C < kInf) {
+        const SelOut sk = wg_select<DT>(
+            [&](auto&& f, bool) {
+              for (int j = tid; j < N; j += kThreads) {
+                uint4 v;
+                int e0;
+                vec_at(j, v, e0);
+                const float vm = vector_max<DT>(v);
+                if (vm >= C) f(vm, 0ull);
+              }
             },
-            false, target, ws, lane, C, Mhi);
+            false, target, sm, tid, wv, lane, C, Mhi, c2, oM, fM);
         if (sk.reached) C1 = fmaxf(C, sk.T);
       }
+      SelOut so;
+      bool ok = false;
       for (int pass = 0; pass < 2 && !ok && C < kInf; ++pass) {
         const float Cu = pass == 0 ? C1 : C;
         if (pass == 1 && !(C1 > C)) break;
         const float Cuf = fmaxf(Cu, -kMaxFinite);  // -inf padding never passes
-        nv = filter_listed(P, slot0, rec_at, Cu, c2, by_mass, lane, ws);
-        src = 0;
-        if (nv <= 4 * kWave) {
-          load_candidates<DT, VEC>(P, rowc, 0, nv, lane, ws, rv, re);
-          so = select_bounded<DT>(
-              [&](auto&& f) {
+        so = wg_select<DT>(
+            [&](auto&& f, bool with_mass) {
+              for (int j = tid; j < N; j += kThreads) {
+                uint4 v;
+                int e0;
+                vec_at(j, v, e0);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  const bool have = q * kWave + lane < nv;
-                  if (__ballot(have)) {
-#pragma unroll
-                    for (int k = 0; k < Fmt<DT>::VE; ++k) {
-                      const float x = elem<DT>(rv[q], k);
-                      if (have && x >= Cuf) f(x, mass_of(x, c2, oM, fM));
-                    }
-                  }
+                for (int k = 0; k < VE; ++k) {
+                  const float x = elem<DT>(v, k);
+                  if (x >= Cuf) f(x, with_mass ? mass_of(x, c2, oM, fM) : 0ull);
                 }
-              },
-              by_mass, target, ws, lane, Cuf, Mhi);
-          src = 1;
-        } else if (nv <= kVecList) {
-          n = 0;
-          for (int j0 = 0; j0 < nv; j0 += 4 * kWave) {
-            load_candidates<DT, VEC>(P, rowc, j0, nv, lane, ws, rv, re);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bool have = j0 + q * kWave + lane < nv;
-              if (__ballot(have)) append_ge<DT>(have, rv[q], re[q], Cuf, lane, ws.cx, ws.ci, kRowCache, &n);
-            }
-          }
-          if (n <= kRowCache) {
-            wave_sync();
-            so = select_bounded<DT>(
-                [&](auto&& f) {
-                  for (int j = lane; j < n; j += kWave) {
-                    const float x = ws.cx[j];
-                    f(x, mass_of(x, c2, oM, fM));
-                  }
-                },
-                by_mass, target, ws, lane, Cuf, Mhi);
-            src = 2;
-          }
-        }
-        ok = src != 0 && so.reached && so.T >= Cu;
+              }
+            },
+            by_mass, target, sm, tid, wv, lane, Cuf, Mhi, c2, oM, fM);
+        ok = so.reached && so.T >= Cu;
       }
       if (!ok) {
-        // full-row selection: re-read the row
-        src = 0;
+        // full-row selection by wave 0: re-read the row
+        if (wv != 0) return;
         so = wave_select<DT>(
             [&](auto&& f) {
               for (int e = lane; e < P.V; e += kWave) {
@@ -1264,7 +1510,7 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
                 f(x, mass_of(x, c2, oM, fM));
               }
             },
-            by_mass, target, ws, lane);
+            by_mass, target, sm.h, lane);
         rr.flags |= SV_ST_FULLSELECT;
       }
       rr.T = so.T;
@@ -1272,74 +1518,116 @@ __device__ __forceinline__ void merge_row(const KParams& P, const SeqParams& sp,
       rr.Zs = (double)so.m_keep / kFix;
       if (by_mass) {
         const double lo = (double)so.m_above / kFix / Z, hi = (double)so.m_keep / kFix / Z;
-        if (fabs(lo - (double)sp.topp) < kWindow || fabs(hi - (double)sp.topp) < kWindow)
-          rr.flags |= SV_ST_MARGIN;
+        if (fabs(lo - (double)sp.topp) < kWindow || fabs(hi - (double)sp.topp) < kWindow) rr.flags |= SV_ST_MARGIN;
       }
       if (!(rr.Zs > 0.0)) rr.flags |= SV_ST_EMPTY;
-      list_ok = ok && tgt && so.n_keep <= (uint32_t)kListMax;
+      list_ok = ok && tgt && so.n_keep <= (uint32_t)kListMax && !(rr.flags & kErrBits);
     }
   }
 
-  if (tok != INT32_MIN) {  // this row scores a draft token
-    if (!tok_ok) {
-      rr.flags |= SV_ST_TOKEN;
-    } else if (!(rr.flags & kErrBits)) {
-      if (mode == SV_GREEDY) rr.pid = tok == rr.g ? 1.0 : 0.0;
-      else rr.pid = xtok >= rr.T ? exp2(((double)xtok - (double)M) * (double)c2) / rr.Zs : 0.0;
-    }
-  }
-
-  if (list_ok && !(rr.flags & kErrBits)) {
+  if (list_ok) {
     // the kept set, in vocabulary order: the candidates >= T, compacted in
-    // list order
+    // buffer order by the work-group, then written out with the draft's
+    // logits at the same tokens (for a resample at this position)
     rr.flags |= kRfListOk;
     int nk = 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-    wave_sync();
-    if (src == 1) {
+    for (int j0 = 0; j0 < N; j0 += kThreads) {
+      const int j = j0 + tid;
+      const bool have = j < N;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      int e0 = 0;
+      if (have) vec_at(j, v, e0);
+      bool pass[VE];
+      int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool have = q * kWave + lane < nv;
-        if (__ballot(have)) append_ge<DT>(have, rv[q], re[q], rr.T, lane, ws.cx, ws.ci, kListMax, &nk);
+      for (int k = 0; k < VE; ++k) {
+        pass[k] = have && elem<DT>(v, k) >= rr.T;
+        cnt += pass[k] ? 1 : 0;
       }
-    } else {
-      for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + lane;
-        const float x = j < n ? ws.cx[j] : -kInf;
-        const int ix = j < n ? ws.ci[j] : 0;
-        const bool keep = j < n && x >= rr.T;
-        const uint64_t bal = __ballot(keep);
-        wave_sync();
-        if (keep) {
-          const int pos = nk + __popcll(bal & below);  // pos <= j: no entry is overwritten unread
-          ws.cx[pos] = x;
-          ws.ci[pos] = ix;
+      const int incl = wave_incl_scan_i(cnt, lane);
+      if (lane == kWave - 1) sm.wsum[wv] = incl;
+      __syncthreads();
+      int off = nk + incl - cnt, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) {
+        const int sw = sm.wsum[w];
+        off += w < wv ? sw : 0;
+        tot += sw;
+      }
+#pragma unroll
+      for (int k = 0; k < VE; ++k) {
+        if (pass[k]) {
+          if (off < kListMax) {
+            sm.kx[off] = elem<DT>(v, k);
+            sm.ki[off] = e0 + k;
+          }
+          ++off;
         }
-        nk += __popcll(bal);
-        wave_sync();
       }
+      nk += tot;
+      __syncthreads();
     }
-    wave_sync();
-    if (P.R <= kSeqWaves) {
-      // the set stays in this wave's LDS for the draw, with the draft's
-      // logits at its tokens (for a resample at this position)
-      if (t < sp.Kb) {
-        const void* drow = row_ptr<DT>(P, b, false, t);
-        for (int j = lane; j < nk; j += kWave) ws.vi[j] = __float_as_int(load_logit<DT>(drow, ws.ci[j]));
-      }
-    } else {
-      KeptEntry* kl = P.kept + rowid * (size_t)min(kListMax, P.V);  // n_keep <= min(kListMax, V)
-      for (int j = lane; j < nk; j += kWave) {
+    nk = min(nk, kListMax);
+    KeptEntry* kl = P.kept + ((size_t)b * (P.K_max + 1) + t) * (size_t)min(kListMax, P.V);
+    const void* drow = (t < sp.Kb && P.draft) ? row_ptr<DT>(P, b, false, t) : nullptr;
+    // the draft's logits first, all loads of a thread in flight together
+    constexpr int Q = kListMax / kThreads;
+    float xp[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int j = q * kThreads + tid;
+      xp[q] = (drow && j < nk) ? load_logit<DT>(drow, sm.ki[j]) : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int j = q * kThreads + tid;
+      if (j < nk) {
         KeptEntry ke;
-        ke.idx = ws.ci[j];
+        ke.idx = sm.ki[j];
+        ke.xq = sm.kx[j];
+        ke.xp = xp[q];
         ke.pad = 0;
-        ke.q = (double)mass_of(ws.cx[j], c2, oM, fM) / kFix / rr.Zs;
         kl[j] = ke;
       }
     }
   }
-  if (lane == 0) out = rr;
+
+  if (tid == 0) {
+    if (tok != INT32_MIN) {  // this row scores a draft token
+      if (!tok_ok) {
+        rr.flags |= SV_ST_TOKEN;
+      } else if (!(rr.flags & kErrBits)) {
+        if (is_greedy) rr.pid = tok == rr.g ? 1.0 : 0.0;
+        else rr.pid = xtok >= rr.T ? exp2(((double)xtok - (double)M) * (double)c2) / rr.Zs : 0.0;
+      }
+    }
+    P.rows[rid] = rr;
+  }
 }
+
+// ===================================================== sequence kernel ====
+//
+// One work-group per sequence.  The row records of its 2 K_b + 1 rows come
+// from the row kernel; wave 0 runs the accept walk, finds the first
+// rejection and draws the resampled or bonus token from the target's kept
+// set; a draw that needs the full rows (plain rows, large kept sets) is
+// done by the whole work-group.
+
+constexpr int kSeqThreads = kSeqWaves * kWave;
+constexpr int kDrawTiles = 4;   // tiles of a row draw whose loads are in flight together
+constexpr int kTileCap = 384;   // tile sums per wave of a row draw held in LDS
+constexpr int kMaxRows = 2 * kMaxK + 1;
+
+struct SmemSeq {
+  RowRec rows[kMaxRows];
+  double rd[kSeqWaves];
+  int ri[kSeqWaves];
+  uint32_t misc[4];
+  double rx[2];
+  double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
+  double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
+  double tsum[kSeqWaves][kTileCap];
+};
 
 // ------------------------------------------------------------- draws ----
 
@@ -1407,12 +1695,11 @@ __device__ __forceinline__ float prob(const RowW& w, float x) {
 // Inverse CDF over the target's kept set in vocabulary order (one wave):
 // w = (q - p)+ when resampling, else w = q.  Entry i sits in slot i / 64 of
 // lane i % 64, so a set of up to 64 tokens costs one wave step per stage.
-// The set is read from the LDS of the wave that merged the row (ls), or
-// from global memory.  The draft's weights are fp32 terms as in prob().
+// The set and the draft's logits at its tokens come from the row kernel's
+// kept list kl.  The draft's weights are fp32 terms as in prob().
 template <int DT>
-__device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
-                                               size_t rowq, const void* drow, double u, int lane,
-                                               const WaveSmem* ls) {
+__device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, const RowRec& rp,
+                                               const KeptEntry* kl, double u, int lane) {
   constexpr int E = kListMax / kWave;
   const int N = rq.n_keep;  // <= kListMax
   const int ns = (N + kWave - 1) / kWave;
@@ -1420,41 +1707,29 @@ __device__ __forceinline__ Draw draw_from_list(const KParams& P, const RowRec& r
   double qv[E];
   float pv[E];
   int iv[E];
-  if (ls) {
-    const float c2q = (float)rq.c2;
-    const float oM = rq.M * c2q;
-    const double fM = exp2_small((double)oM - (double)rq.M * (double)c2q);
-    const double inv = 1.0 / (rq.Zs * kFix);
+  const float c2q = (float)rq.c2;
+  const float oM = rq.M * c2q;
+  const double fM = exp2_small((double)oM - (double)rq.M * (double)c2q);
+  const double inv = 1.0 / (rq.Zs * kFix);
+  KeptEntry ke[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = j * kWave + lane;
-      qv[j] = 0.0;
-      pv[j] = 0.0f;
-      iv[j] = 0;
-      if (j < ns && i < N) {
-        iv[j] = ls->ci[i];
-        qv[j] = (double)mass_of(ls->cx[i], c2q, oM, fM) * inv;
-        if (resample) pv[j] = prob(wp, __int_as_float(ls->vi[i]));
-      }
-    }
-  } else {
-    const KeptEntry* kl = P.kept + rowq * (size_t)min(kListMax, P.V);
+  for (int j = 0; j < E; ++j) {
+    const int i = j * kWave + lane;
+    ke[j].idx = 0;
+    ke[j].xq = -kInf;
+    ke[j].xp = -kInf;
+    if (j < ns && i < N) ke[j] = kl[i];
+  }
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = j * kWave + lane;
-      qv[j] = 0.0;
-      pv[j] = 0.0f;
-      iv[j] = 0;
-      if (j < ns && i < N) {
-        const KeptEntry ke = kl[i];
-        qv[j] = ke.q;
-        iv[j] = ke.idx;
-      }
-    }
-    if (resample) {
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (j < ns && j * kWave + lane < N) pv[j] = prob(wp, load_logit<DT>(drow, iv[j]));
+  for (int j = 0; j < E; ++j) {
+    const int i = j * kWave + lane;
+    qv[j] = 0.0;
+    pv[j] = 0.0f;
+    iv[j] = 0;
+    if (j < ns && i < N) {
+      iv[j] = ke[j].idx;
+      qv[j] = (double)mass_of(ke[j].xq, c2q, oM, fM) * inv;
+      if (resample) pv[j] = prob(wp, ke[j].xp);
     }
   }
   Draw d;
@@ -1580,7 +1855,6 @@ template <int DT, bool VEC>
 __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
                                                const char* qrow, const char* prow, double u, SmemSeq& sm, int lane,
                                                int wv, const ChunkRec* qrec) {
-  constexpr int kTileCap = (int)(kRowCache * sizeof(float) / sizeof(double));
   const int tid = threadIdx.x;
   Draw d;
   d.flags = SV_ST_REREAD;
@@ -1591,27 +1865,31 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   int lo = 0, hi = P.V;
   double base = 0.0;  // weight before lo (chunk-located draws)
   bool located = false, force_last = false;
-  if (!resample && qrec && rq.T == -kInf) {
+  if (!resample && qrec && (rq.flags & kRfChunks)) {
     // plain bonus draw: the chunk sums give the chunk holding u
     const int S = P.S;
-    // two chunks per thread cover every row: V <= 2^22 is at most 1024 chunks
-    static_assert(2 * kSeqThreads >= kMaxVocab / (64 * kLoads * 4), "chunk sums per thread");
-    double wc[2];
-    for (int j = 0; j < 2; ++j) {
-      const int c = 2 * tid + j;
+    // kCpt consecutive chunks per thread cover every row (V <= 2^22)
+    constexpr int kCpt = (kMaxVocab / (kWave * kLoads * 4) + kSeqThreads - 1) / kSeqThreads;
+    double wc[kCpt];
+    double wsum = 0.0;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const int c = kCpt * tid + j;
       wc[j] = 0.0;
       if (c < S) {
         const ChunkRec r = qrec[c];
-        if (r.m > -kInf) wc[j] = r.z * exp2(((double)r.m - (double)rq.M) * (double)wq.c2) / rq.Zs;
+        if (r.z > 0.0) wc[j] = r.z * exp2((double)r.o - (double)rq.M * (double)wq.c2) / rq.Zs;
       }
+      wsum += wc[j];
     }
     double tot;
-    const double ex = seq_exclusive_scan(wc[0] + wc[1], &tot, sm);
+    const double ex = seq_exclusive_scan(wsum, &tot, sm);
     int cstar = 0x7fffffff, clast = -1;
     double cb = 0.0;
-    for (int j = 0; j < 2; ++j) {
-      const int c = 2 * tid + j;
-      const double before = ex + (j ? wc[0] : 0.0);
+    double before = ex;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const int c = kCpt * tid + j;
       if (c < S && wc[j] > 0.0) {
         if (before + wc[j] > u && cstar == 0x7fffffff) {
           cstar = c;
@@ -1619,6 +1897,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
         }
         clast = c;
       }
+      before += wc[j];
     }
     const int cs = seq_min_i(cstar, sm);
     const int cl = seq_max_i(clast, sm);
@@ -1635,7 +1914,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
       force_last = cs == 0x7fffffff;  // u beyond the rounded total: the last token of the last chunk
     }
   }
-  double* tsum = reinterpret_cast<double*>(sm.w[wv].cx);  // this wave's tile sums
+  double* tsum = sm.tsum[wv];  // this wave's tile sums
   double S = 0.0;
   int nzlo = 0x7fffffff, nzhi = -1, per = 0, v0 = 0, v1 = 0;
   for (int pass = 0; pass < 2; ++pass) {
@@ -1849,6 +2128,7 @@ __device__ __forceinline__ void write_tokens(const KParams& P, int b, int n, int
   }
 }
 
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   __shared__ SmemSeq sm;
@@ -1862,12 +2142,18 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
   const uint64_t g = P.row_offset + (uint64_t)b;
-  // With fewer rows than waves the last wave is free during the merge: it
-  // draws the walk's uniforms (they depend only on seed, sequence, position
-  // and purpose), which takes them off the path after the barrier.
-  const bool pre_u = R < kSeqWaves;
-  for (int r = wv; r < R; r += kSeqWaves) merge_row<DT, VEC>(P, sp, b, r, lane, sm.w[wv], sm.rows[r]);
-  if (pre_u && wv == kSeqWaves - 1) {
+  const bool greedy = sp.mode == SV_GREEDY;
+  // greedy calls may come without draft logits: the rule then needs only
+  // the target's argmax (the draft rows' records are not made)
+  const bool have_draft = P.draft != nullptr;
+  for (int r = tid; r < R; r += kSeqThreads) {
+    const bool used = r <= KM ? r <= Kb : (r - KM - 1 < Kb && have_draft);
+    if (used) sm.rows[r] = P.rows[(size_t)b * R + r];
+  }
+  // The walk's uniforms depend only on seed, sequence, position and
+  // purpose: the last wave draws those of positions 0..63 while the records
+  // load.  Greedy rows use none (u p < q with p, q in {0, 1} holds iff q = 1).
+  if (!greedy && wv == kSeqWaves - 1) {
     const int t = lane;
     if (t < Kb) sm.ua[t] = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
     if (t <= Kb) sm.ud[t] = uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
@@ -1875,12 +2161,13 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   __syncthreads();
 
   // Wave 0: the rows' flags, the accept walk, and the draw when it needs no
-  // more than the kept set in LDS.  The work-group joins only for a draw
-  // from the rows.
+  // more than the kept list.  The work-group joins only for a draw from the
+  // rows.
   if (wv == 0) {
     uint32_t st = 0;
     for (int t = lane; t <= Kb; t += kWave) st |= sm.rows[t].flags;
-    for (int t = lane; t < Kb; t += kWave) st |= sm.rows[KM + 1 + t].flags;
+    if (have_draft)
+      for (int t = lane; t < Kb; t += kWave) st |= sm.rows[KM + 1 + t].flags;
     st = wave_or_u(st) & ~kRfListOk;
     int job = 0;  // 0 done, 1 draw from the rows
     if (st & kErrBits) {
@@ -1891,7 +2178,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
           float q = __builtin_nanf(""), p = __builtin_nanf("");
           if (t < Kb) {
             q = (float)sm.rows[t].pid;
-            p = (float)sm.rows[KM + 1 + t].pid;
+            if (have_draft) p = (float)sm.rows[KM + 1 + t].pid;
           }
           P.diag[((size_t)b * KM + t) * 2 + 0] = q;
           P.diag[((size_t)b * KM + t) * 2 + 1] = p;
@@ -1907,16 +2194,21 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
         bool rej = false;
         uint32_t s2 = 0;
         double ud = 0.0;
-        const bool have_u = pre_u && t0 == 0;  // drawn during the merge (t < 64)
+        const bool have_u = t0 == 0;  // drawn by the last wave (t < 64)
         if (t < Kb) {
-          const double q = sm.rows[t].pid, p = sm.rows[KM + 1 + t].pid;
-          const double ua = have_u ? sm.ua[t] : uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
-          rej = !(ua * p < q);
+          const double q = sm.rows[t].pid;
+          const double p = have_draft ? sm.rows[KM + 1 + t].pid : __builtin_nan("");
           if (p == 0.0) s2 |= SV_ST_PZERO;
-          // q / p < 1 + w and |u - q / p| < w, multiplied through by p > 0
-          if (p > 0.0 && q < p * (1.0 + kWindow) && fabs(ua * p - q) < kWindow * p) s2 |= SV_ST_MARGIN;
+          if (greedy) {
+            rej = !(q > 0.0);
+          } else {
+            const double ua = have_u ? sm.ua[t] : uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
+            rej = !(ua * p < q);
+            // q / p < 1 + w and |u - q / p| < w, multiplied through by p > 0
+            if (p > 0.0 && q < p * (1.0 + kWindow) && fabs(ua * p - q) < kWindow * p) s2 |= SV_ST_MARGIN;
+          }
         }
-        if (t <= Kb)
+        if (!greedy && t <= Kb)
           ud = have_u ? sm.ud[t] : uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
         const uint64_t rb = __ballot(rej);
         const int end = rb ? t0 + __ffsll((long long)rb) - 1 : Kb;  // the walk stops here if < t0 + 64
@@ -1930,15 +2222,14 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
       }
       const bool resample = n < Kb;
       const RowRec& rq = sm.rows[n];
-      const RowRec& rp = resample ? sm.rows[KM + 1 + n] : sm.rows[n];
-      if (sp.mode == SV_GREEDY) {
+      const RowRec& rp = resample && have_draft ? sm.rows[KM + 1 + n] : sm.rows[n];
+      if (greedy) {
         const int y = rq.g;
-        if (resample && rp.g == rq.g) st |= SV_ST_ZERO_RESIDUAL;
+        if (resample && have_draft && rp.g == rq.g) st |= SV_ST_ZERO_RESIDUAL;
         write_tokens(P, b, n, y, st, lane, kWave);
       } else if (rq.flags & kRfListOk) {
-        const Draw d = draw_from_list<DT>(P, rq, resample, rp, (size_t)b * R + n,
-                                          resample ? row_ptr<DT>(P, b, false, n) : nullptr, u, lane,
-                                          R <= kSeqWaves ? &sm.w[n] : nullptr);
+        const KeptEntry* kl = P.kept + ((size_t)b * (KM + 1) + n) * (size_t)min(kListMax, P.V);
+        const Draw d = draw_from_list<DT>(rq, resample, rp, kl, u, lane);
         write_tokens(P, b, n, d.y, st | d.flags, lane, kWave);
       } else {
         job = 1;
@@ -1953,7 +2244,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   }
   __syncthreads();
   if (sm.misc[2] == 0u) return;
-  // draw from the rows (plain mode, or a kept set not held as a list)
+  // draw from the rows (plain rows, or a kept set not held as a list)
   const int n = (int)sm.misc[0];
   uint32_t st = sm.misc[1];
   const double u = sm.rx[0];
@@ -1969,30 +2260,30 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
 
 // start / stop: events recorded on the kernel's own dispatch (NULL: none).
 template <int DT, bool VEC>
-void launch_chunk(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+void launch_rows(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 block(kThreads);
   switch (mode) {
-    case SV_PLAIN: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_TOPK: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_TOPP: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_GREEDY: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((chunk_kernel<DT, VEC, kAnyMode>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_PLAIN: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPK: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPP: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_GREEDY: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
+    default: hipExtLaunchKernelGGL((row_kernel<DT, VEC, kAnyMode>), grid, block, 0, stream, start, stop, 0, p); break;
   }
 }
 
 template <int DT, bool VEC>
 hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
-  // one streaming instance: the default mode's, or the one holding every
+  // one row-kernel instance: the default mode's, or the one holding every
   // path when the call gives a mode per sequence
-  const size_t waves = (size_t)nseq * p.R * p.S;
-  const dim3 grid((unsigned)((waves + kThreads / kWave - 1) / (kThreads / kWave)));
-  launch_chunk<DT, VEC>(p, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+  const dim3 grid((unsigned)((size_t)nseq * p.R));
+  launch_rows<DT, VEC>(p, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipExtLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream,
                         ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, p);
   return hipSuccess;
 }
 
 }  // namespace
+
 
 namespace {
 
