@@ -263,13 +263,21 @@ __device__ __forceinline__ int raw_mode(const KParams& P, int b) {
   return P.mode ? (int)P.mode[b] : P.dmode;
 }
 
-__device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
+// The sequence's parameters as stored (the loads only) ...
+__device__ __forceinline__ SeqParams raw_params(const KParams& P, int b) {
   SeqParams s;
   s.Kb = P.kpr ? P.kpr[b] : P.K_max;
   s.mode = raw_mode(P, b);
   s.tau = P.temp ? P.temp[b] : P.dtemp;
   s.topk = P.topk ? P.topk[b] : P.dtopk;
   s.topp = P.topp ? P.topp[b] : P.dtopp;
+  s.c2 = 0.0;
+  s.valid = false;
+  return s;
+}
+
+// ... and checked: valid, and the effective mode with c2 = log2(e) / tau.
+__device__ __forceinline__ SeqParams check_params(const KParams& P, SeqParams s) {
   bool ok = s.Kb >= 0 && s.Kb <= P.K_max && s.mode >= 0 && s.mode <= 3;
   if (ok && s.mode != SV_GREEDY) ok = isfinite(s.tau) && s.tau > 0.0f;
   if (ok && s.mode == SV_TOPK) ok = s.topk >= 1 && s.topk <= P.V;
@@ -283,6 +291,10 @@ __device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
   return s;
 }
 
+__device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
+  return check_params(P, raw_params(P, b));
+}
+
 template <int DT>
 __device__ __forceinline__ const void* row_ptr(const KParams& P, int b, bool tgt, int t) {
   constexpr int ES = Fmt<DT>::ES;
@@ -290,12 +302,6 @@ __device__ __forceinline__ const void* row_ptr(const KParams& P, int b, bool tgt
   return static_cast<const char*>(tgt ? P.target : P.draft) + r * (size_t)P.V * ES;
 }
 
-// Row r of a sequence: target positions 0..K_max, then draft positions.
-__device__ __forceinline__ bool decode_row(const KParams& P, const SeqParams& sp, int r, bool* tgt, int* t) {
-  *tgt = r <= P.K_max;
-  *t = *tgt ? r : r - P.K_max - 1;
-  return *tgt ? (*t <= sp.Kb) : (*t < sp.Kb);
-}
 
 // ================================================== chunk reductions ====
 //
@@ -637,6 +643,16 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A work-group barrier that orders LDS accesses only.  __syncthreads also
+// waits for every global load the wave has in flight (its release fence
+// covers global memory); the row kernel's waves exchange data through LDS
+// alone, and keep their loads in flight across its barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int) {
   return wave_scan(v, 0ull, [](unsigned long long a, unsigned long long b) { return a + b; });
 }
@@ -904,6 +920,7 @@ struct RowSmem {
   Hist h;
   float kx[kListMax];              // the kept set in vocabulary order: logits
   int ki[kListMax];                //   and vocabulary indices
+  float kp[kListMax];              //   and the draft's logits there (resample positions)
   float pub[kRowWaves];            // each wave's running maximum (nucleus) or cut (top-k)
   float ucut[kRowWaves];           // the largest listing cut each wave used
   int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
@@ -1056,12 +1073,12 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
     // one level: every digit is one bf16 value (see select_narrow)
     const uint32_t kb = (fkey(hi) >> 16) - 255u;
     sm.h.hc[tid] = 0;
-    __syncthreads();
+    lds_barrier();
     each([&](float x, unsigned long long) { atomicAdd(&sm.h.hc[min(255u, (fkey(x) >> 16) - kb)], 1u); }, false);
-    __syncthreads();
+    lds_barrier();
     const uint32_t c = sm.h.hc[tid];
     sm.h.hm[tid] = c ? (unsigned long long)c * mass_of(bf16_of_key(kb + (uint32_t)tid), c2, oM, fM) : 0ull;
-    __syncthreads();
+    lds_barrier();
     if (wv == 0) {
       const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
       if (lane == 0) {
@@ -1074,7 +1091,7 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
         sm.sel.m_above = above_m;
       }
     }
-    __syncthreads();
+    lds_barrier();
     return sm.sel;
   }
   // MSB-first 8-bit digits over the 32-bit keys (bf16: the top 16 bits)
@@ -1084,7 +1101,7 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
     const int shift = 24 - 8 * lv;
     sm.h.hc[tid] = 0;
     sm.h.hm[tid] = 0;
-    __syncthreads();
+    lds_barrier();
     each(
         [&](float x, unsigned long long m) {
           const uint32_t key = fkey(x);
@@ -1095,12 +1112,12 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
           }
         },
         true);
-    __syncthreads();
+    lds_barrier();
     if (wv == 0) {
       const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
       if (lane == 0) sm.seldg = dg;
     }
-    __syncthreads();
+    lds_barrier();
     pkey |= (uint32_t)sm.seldg << shift;
     pmask |= 255u << shift;
   }
@@ -1112,7 +1129,7 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
     sm.sel.m_keep = above_m + last_m;
     sm.sel.m_above = above_m;
   }
-  __syncthreads();
+  lds_barrier();
   return sm.sel;
 }
 
@@ -1126,37 +1143,54 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const int R = P.R, S = P.S;
   const int b = P.b_base + (int)(blockIdx.x / (uint32_t)R);
   const int r = (int)(blockIdx.x % (uint32_t)R);
+  // Row r of the padded layout: target positions 0..K_max, then draft
+  // positions; whether the sequence uses it depends on its K_b.
   // Whole work-groups return here, before any barrier.
-  const SeqParams sp = load_params(P, b);
+  const bool tgt = r <= P.K_max;
+  const int t = tgt ? r : r - P.K_max - 1;
+  if (!tgt && P.draft == nullptr) return;  // greedy calls without draft logits
+  const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
+  // wave wv streams chunks [cb, ce) of the row
+  const int per = (S + kRowWaves - 1) / kRowWaves;
+  const int cb = min(S, wv * per), ce = min(S, cb + per);
+  constexpr int ES = Fmt<DT>::ES;
+  const int row_bytes = P.V * ES;
+  // The first chunk's loads go out before the sequence's parameters have
+  // arrived (under a full stream their loads can take microseconds): its
+  // parameter loads are issued first, then the chunk's, and only K_b, when
+  // the call has a k_per_row array, is waited for (padding rows are never
+  // read: theirs read nothing, past the row's end).
+  const SeqParams raw = raw_params(P, b);
+  const bool used = tgt ? t <= raw.Kb : t < raw.Kb;
+  uint4 A[kLoads], B[kLoads];
+  const __amdgpu_buffer_rsrc_t rs = row_resource(row, row_bytes);
+  auto off = [&](int cc) { return cc < ce ? cc * P.L * ES : row_bytes; };
+  if constexpr (VEC) issue_chunk<DT>(A, rs, used ? off(cb) : row_bytes, lane);
+  const SeqParams sp = check_params(P, raw);
   if (!sp.valid) return;  // the sequence kernel reports the parameter error
-  bool tgt;
-  int t;
-  if (!decode_row(P, sp, r, &tgt, &t)) return;  // padding rows are never read
-  if (!tgt && P.draft == nullptr) return;        // greedy calls without draft logits
+  if (!used) return;      // a padding row
   // the row's filter (work-group uniform)
   // (a greedy instance only ever sees greedy rows: the mode is never remapped)
   const bool is_greedy = MODE == SV_GREEDY || (kAny && sp.mode == SV_GREEDY);
   const bool is_topk = (MODE == SV_TOPK || kAny) && sp.mode == SV_TOPK;
   const bool is_topp = (MODE == SV_TOPP || kAny) && sp.mode == SV_TOPP;
   const bool is_plain = !is_greedy && !is_topk && !is_topp;
-  const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
   const size_t rid = (size_t)b * R + r;
   const size_t slot0 = rid * S;
   const float c2 = (float)sp.c2;
   const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
   const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
-  // the draft token's logit, for the finish (loaded now, while the row streams)
+  // the draft token's logit, used by the finish: loaded behind the first
+  // chunk, so that it arrives while the row streams
   const float xtok = (tok_ok && threadIdx.x == 0) ? load_logit<DT>(row, tok) : 0.0f;
   if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
-  __syncthreads();
+  lds_barrier();
 
   // ---- streaming: wave wv takes chunks [cb, ce) ----
   // Each lane accumulates over all of the wave's chunks on its own (softmax
   // sums, maxima, the greedy candidate); the wave reduces once, after its
   // last chunk.  Only the top-k and nucleus candidate lists, and the chunk
   // sums of plain target rows, are built chunk by chunk.
-  const int per = (S + kRowWaves - 1) / kRowWaves;
-  const int cb = min(S, wv * per), ce = min(S, cb + per);
   int nc = 0;            // candidate vectors listed by this wave
   bool over = false;     // the wave's candidate buffer overflowed
   float run = -kInf;     // this wave's running maximum (nucleus) or cut (top-k)
@@ -1176,6 +1210,10 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   auto do_chunk = [&](const int c, uint4 (&buf)[kLoads], bool mask) {
     const int c0 = c * P.L, c1 = min(P.V, c0 + P.L);
     const int ln = fresh_lane(lane);
+    // Every path waits for this chunk's loads here, and only for them: a
+    // path that left them in flight (a wave that stops early) would make
+    // the loop's next iteration wait for all loads, the next chunk's too.
+    unpack_barrier(buf);
     if (mask && c1 - c0 < P.L) mask_chunk<DT>(buf, c0, c1, ln);
     if (bad) return;
     if (is_greedy) {
@@ -1261,19 +1299,20 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       if (is_topp && !over) {
         // the chunk maximum, from its largest term
         const double ma = ch.em > 0.0f ? ((double)__builtin_amdgcn_logf(ch.em) + (double)ch.o) * ic2 : -1e300;
-        // list every vector holding a logit >= g - 10/c2, g the largest
-        // chunk maximum known; a list that would overflow the buffer is
-        // first compacted against g, then retried with 8 and 6
+        // List every vector holding a logit >= g - w/c2, g the largest chunk
+        // maximum known, with the window w = 10 log2 units first.  A list
+        // that would overflow the buffer is first compacted against the
+        // window about to be tried, then the chunk is listed again with it,
+        // narrowing to 8, 6, 5, 4, 3, 2: everything at or above the
+        // narrowest cut used stays listed.
         const double g = fmax(fmax((double)run, ma), (double)published_max(sm));
         bool done = false;
         float cut = kInf;
-        for (int attempt = 0; attempt < 4 && !done; ++attempt) {
-          if (attempt == 1) {
-            // drop the entries the raised maximum has left behind (keys
-            // are within 2^-8 / c2 of their vectors' maxima)
-            nc = compact_listed(sm, wv, nc, (float)(g - kCandLog2 * ic2 - 0.00390625 * ic2), ln);
-          }
-          cut = (float)(g - (attempt <= 1 ? kCandLog2 : attempt == 2 ? 8.0 : 6.0) * ic2);
+        for (int attempt = 0; attempt < 8 && !done; ++attempt) {
+          const double w = attempt <= 1 ? kCandLog2 : attempt == 2 ? 8.0 : (double)(9 - attempt);
+          // (keys are within 2^-8 / c2 of their vectors' maxima)
+          if (attempt >= 1) nc = compact_listed(sm, wv, nc, (float)(g - w * ic2 - 0.00390625 * ic2), ln);
+          cut = (float)(g - w * ic2);
           // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
           // (the exponent is >= -10.01: o never exceeds g c2)
           const float thr = __builtin_amdgcn_exp2f((float)((double)cut * (double)c2 - (double)ch.o) - 0.00390625f);
@@ -1303,21 +1342,19 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     // The next chunk's loads are issued whether or not it exists (then at
     // the row's end, where they read nothing), so that the number of loads
     // in flight is always the same and each wait is for one chunk only.
-    constexpr int ES = Fmt<DT>::ES;
-    const int row_bytes = P.V * ES;
-    const __amdgpu_buffer_rsrc_t rs = row_resource(row, row_bytes);
-    auto off = [&](int cc) { return cc < ce ? cc * P.L * ES : row_bytes; };
-    uint4 A[kLoads], B[kLoads];
+    // Pairs of chunks: every iteration enters with A(c) in flight and
+    // leaves with A(c + 2) in flight, so the loop has no exit in its middle
+    // and every path into its head holds the same loads.
+    const int n = ce - cb;
     int c = cb;
-    issue_chunk<DT>(A, rs, off(c), lane);
-    while (c < ce) {
+    for (int k = 0; k + 1 < n; k += 2, c += 2) {
       issue_chunk<DT>(B, rs, off(c + 1), lane);
       do_chunk(c, A, true);
-      if (++c >= ce) break;
-      issue_chunk<DT>(A, rs, off(c + 1), lane);
-      do_chunk(c, B, true);
-      ++c;
+      issue_chunk<DT>(A, rs, off(c + 2), lane);
+      do_chunk(c + 1, B, true);
     }
+    if (n & 1) do_chunk(c, A, true);  // the last chunk
+    else unpack_barrier(A);           // loads past the row's end
   } else {
     for (int c = cb; c < ce; ++c) {
       uint4 buf[kLoads];
@@ -1370,7 +1407,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       sm.ucut[wv] = ucut;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- finish ----
   // Every wave derives the row's statistics from the wave records; the
@@ -1433,6 +1470,24 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     v = sm.cv[w][pos];
     e0 = sm.ci[w][pos];
   };
+  // The draft's logits at the candidates of a target row whose position
+  // may be resampled: loaded now, while the selection runs, for the kept
+  // list (candidate j is thread j mod kThreads's, in round j / kThreads).
+  constexpr int kRounds = kRowWaves * kCandVecs / kThreads;
+  const bool want_p = selecting && tgt && t < sp.Kb && P.draft != nullptr;
+  const char* drow = want_p ? static_cast<const char*>(row_ptr<DT>(P, b, false, t)) : nullptr;
+  uint4 dv[kRounds];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int j = q * kThreads + tid;
+    dv[q] = make_uint4(0, 0, 0, 0);
+    if (want_p && j < N) {
+      uint4 v;
+      int e0;
+      vec_at(j, v, e0);
+      dv[q] = load_vec<DT, VEC>(drow, e0, P.V);
+    }
+  }
   if (!(rr.flags & kErrBits)) {
     if (is_plain) {
       rr.Zs = Z;
@@ -1531,7 +1586,10 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     // logits at the same tokens (for a resample at this position)
     rr.flags |= kRfListOk;
     int nk = 0;
-    for (int j0 = 0; j0 < N; j0 += kThreads) {
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+      const int j0 = q * kThreads;
+      if (j0 >= N) break;  // work-group uniform
       const int j = j0 + tid;
       const bool have = j < N;
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -1546,7 +1604,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       }
       const int incl = wave_incl_scan_i(cnt, lane);
       if (lane == kWave - 1) sm.wsum[wv] = incl;
-      __syncthreads();
+      lds_barrier();
       int off = nk + incl - cnt, tot = 0;
 #pragma unroll
       for (int w = 0; w < kRowWaves; ++w) {
@@ -1560,35 +1618,23 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
           if (off < kListMax) {
             sm.kx[off] = elem<DT>(v, k);
             sm.ki[off] = e0 + k;
+            sm.kp[off] = want_p ? elem<DT>(dv[q], k) : __builtin_nanf("");
           }
           ++off;
         }
       }
       nk += tot;
-      __syncthreads();
+      lds_barrier();
     }
     nk = min(nk, kListMax);
     KeptEntry* kl = P.kept + ((size_t)b * (P.K_max + 1) + t) * (size_t)min(kListMax, P.V);
-    const void* drow = (t < sp.Kb && P.draft) ? row_ptr<DT>(P, b, false, t) : nullptr;
-    // the draft's logits first, all loads of a thread in flight together
-    constexpr int Q = kListMax / kThreads;
-    float xp[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int j = q * kThreads + tid;
-      xp[q] = (drow && j < nk) ? load_logit<DT>(drow, sm.ki[j]) : __builtin_nanf("");
-    }
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int j = q * kThreads + tid;
-      if (j < nk) {
-        KeptEntry ke;
-        ke.idx = sm.ki[j];
-        ke.xq = sm.kx[j];
-        ke.xp = xp[q];
-        ke.pad = 0;
-        kl[j] = ke;
-      }
+    for (int j = tid; j < nk; j += kThreads) {
+      KeptEntry ke;
+      ke.idx = sm.ki[j];
+      ke.xq = sm.kx[j];
+      ke.xp = sm.kp[j];
+      ke.pad = 0;
+      kl[j] = ke;
     }
   }
 
