@@ -104,7 +104,14 @@ typedef struct {
  *                                  bonus position.  Rows t > K_b are never
  *                                  read (padding may hold anything).
  *   draft_logits  [B][K_max][V]    rows t >= K_b are never read.  May be NULL
- *                                  when K_max = 0.
+ *                                  when K_max = 0, or when every sequence is
+ *                                  greedy (mode NULL, default_mode
+ *                                  SV_GREEDY): greedy verification needs only
+ *                                  the target's argmax, so then only the
+ *                                  K_b + 1 target rows are read; diag's p
+ *                                  column is NaN and SV_ST_ZERO_RESIDUAL /
+ *                                  SV_ST_PZERO, which need the draft's
+ *                                  argmax, are never set.
  *   draft_tokens  [B][K_max] int32 may be NULL when K_max = 0.
  *   k_per_row     [B] int32 in [0, K_max], or NULL (every row uses K_max).
  *   mode          [B] uint8 sv_mode, or NULL (default_mode).

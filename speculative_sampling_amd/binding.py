@@ -154,7 +154,12 @@ def make_args(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens:
     B, K1, V = target.shape
     K = K1 - 1
     if K > 0:
-        if draft is None or tuple(draft.shape) != (B, K, V) or draft.dtype != target.dtype:
+        # greedy verification needs only the target's argmax: the draft's
+        # logits may be left out when every sequence is greedy
+        greedy_only = mode is None and default_mode == SV_GREEDY
+        if draft is None and not greedy_only:
+            raise ValueError("draft is required unless every sequence is greedy")
+        if draft is not None and (tuple(draft.shape) != (B, K, V) or draft.dtype != target.dtype):
             raise ValueError("draft must be [B][K_max][V] with the target's dtype")
         if draft_tokens is None or tuple(draft_tokens.shape) != (B, K):
             raise ValueError("draft_tokens must be [B][K_max]")
@@ -163,7 +168,7 @@ def make_args(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens:
     return SvArgs(
         B, K,
         _ptr(target, name="target"),
-        _ptr(draft, name="draft") if K > 0 else None,
+        _ptr(draft, name="draft") if K > 0 and draft is not None else None,
         _ptr(draft_tokens, torch.int32, B * K, "draft_tokens") if K > 0 else None,
         _ptr(k_per_row, torch.int32, B, "k_per_row"),
         _ptr(mode, torch.uint8, B, "mode"),

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from speculative_sampling_amd import binding
 from speculative_sampling_amd.binding import (SV_BF16, SV_ECAPACITY, SV_EDTYPE, SV_EINVAL, SV_F32,
@@ -64,6 +65,24 @@ def test_validate_accepts_good_arguments():
     assert validate(_args()) == SV_OK
     assert validate(_args(B=0, target=None, accepted=None)) == SV_OK
     assert validate(_args(K_max=0, draft=None, tokens=None)) == SV_OK
+
+
+@needs_lib
+def test_greedy_calls_may_leave_out_the_draft_logits():
+    # the greedy rule needs only the target's argmax: without a mode array
+    # and with greedy as the default, draft_logits may be NULL
+    assert validate(_args(draft=None, default_mode=SV_GREEDY)) == SV_OK
+    # any other default, or a mode array (which may name other modes), needs them
+    assert validate(_args(draft=None, default_mode=SV_TOPK)) == SV_EINVAL
+    assert validate(_args(draft=None, default_mode=SV_GREEDY, mode=0x60000)) == SV_EINVAL
+    # the binding refuses the same calls before anything is launched
+    t = torch.zeros(2, 3, 100)
+    toks = torch.zeros(2, 2, dtype=torch.int32)
+    out = dict(accepted=torch.zeros(2, dtype=torch.int32), out_tokens=torch.zeros(2, 3, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        binding.make_args(t, None, toks, default_mode=SV_TOPP, **out)
+    with pytest.raises(ValueError):
+        binding.make_args(t, None, toks, default_mode=SV_GREEDY, mode=torch.zeros(2, dtype=torch.uint8), **out)
 
 
 @needs_lib
