@@ -174,7 +174,11 @@ int spec_verify_run(sv_handle_t h, const sv_args* args, void* stream);
 
 /* If any run was enqueued or captured through h, waits for the device to
  * finish all queued work (which includes every such run and any launch of a
- * graph holding one), then frees the workspace and the handle.  A graph
+ * graph holding one), then frees the workspace and the handle.  The wait is
+ * device-wide by design: a run records no event and allocates nothing, so
+ * the handle does not know which streams its runs used, and a device
+ * synchronisation is the one wait that covers them all; it also waits for
+ * work of other handles and other libraries on the device.  A graph
  * holding a captured run must not be launched after its handle is
  * destroyed.  NULL is accepted. */
 int spec_verify_destroy(sv_handle_t h);
@@ -191,9 +195,9 @@ uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 /* Stage timing, for measurement.  After spec_verify_profile_begin(h, n),
  * the next n calls of spec_verify_run on h record HIP events on their own
  * stream for the two stages of the first launch batch (a call is one batch
- * unless it exceeds 2^23 streaming waves or 2^22 sequences): stage 0 is the
- * streaming pass over the logits, stage 1 the per-sequence merge, accept
- * walk and draw.  Each stage is timed from the start to the end of its
+ * unless it exceeds 2^23 logit rows or 2^22 sequences): stage 0 is the
+ * streaming pass over the logit rows with each row's finish (statistics,
+ * threshold, kept list), stage 1 the per-sequence accept walk and draw.  Each stage is timed from the start to the end of its
  * kernels' own dispatches (events attached to the dispatch, so the launch
  * gap before a kernel is not counted).  The events are created here, so run
  * still allocates nothing; runs under stream capture record none.  spec_verify_profile_end waits for the

@@ -223,6 +223,30 @@ def test_large_logits_take_the_exact_exponent_path():
     check(w, "large_logits")
 
 
+@pytest.mark.parametrize("dtype,mode", [("bf16", SV_PLAIN), ("f32", SV_PLAIN), ("bf16", SV_TOPP)])
+def test_one_dominant_token_at_low_temperature(dtype, mode):
+    """One token per row sits 40 logits above the rest, at tau = 0.5: the
+    row's terms span about 2^-115 .. 1, and the dominant token lies far above
+    the largest logit of most lanes' first vectors, so the sums are taken
+    with an exponent offset that the row's own maximum must raise (the chunk
+    holding the token is redone from its exact maximum).  q(d) near 1 and
+    the tail's tiny masses must both match the oracle."""
+    B, K, V = 16, 4, 40000
+    w = workloads.iid_normal(B, K, V, sigma_t=1.0, sigma_d=0.5, dtype=dtype, mode=mode, temperature=0.5,
+                             top_p=0.9, gen_seed=61, seed=60)
+    g = torch.Generator().manual_seed(62)
+    tgt, drf = w.target.float(), w.draft.float()
+    for b in range(B):
+        for t in range(K + 1):
+            i = int(torch.randint(0, V, (1,), generator=g))
+            tgt[b, t, i] += 40.0
+            if t < K:
+                drf[b, t, i] += 40.0 if b % 2 == 0 else 0.0   # odd sequences: the draft misses it
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    w.target, w.draft = tgt.to(dt).contiguous(), drf.to(dt).contiguous()
+    check(w, f"dominant_{dtype}_{mode}")
+
+
 def test_error_rows():
     B, K, V = 10, 3, 4096
     w = workloads.iid_normal(B, K, V, gen_seed=17, seed=16)
