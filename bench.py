@@ -12,9 +12,9 @@ so the 256 MB Infinity Cache cannot serve repeated reads.  Draft tokens are
 drawn by the library itself (the step with K = 0 on the draft rows).
 
 Prints one JSON line: value = rows/s; roofline = algorithmic logit bytes per
-call / average time of the streaming kernel (HIP events the library attaches
-to that kernel's own dispatches on the launch stream) against the 8 TB/s HBM
-peak;
+call / average time of the row kernel (the streaming pass over the logit
+rows with each row's finish; HIP events the library attaches to that
+kernel's own dispatches on the launch stream) against the 8 TB/s HBM peak;
 streaming_ceiling = the read rate of the library's read-only probe over the
 same rotating logits; per_call_us = p10 / median / p90 of single calls;
 cpu_baseline = the fp64 oracle on a bounded sample, on one thread and on
@@ -45,7 +45,7 @@ def kernel_source_hash():
 def stored_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"row_kernel_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -71,6 +71,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run --steps plain device copies of BYTES bytes (HBM counter calibration)")
+    ap.add_argument("--workload", default=None,
+                    help="another named workload (speculative_sampling_amd.workloads.config); "
+                         "default: the headline, B=64 K=4 V=128256 bf16 nucleus")
+    ap.add_argument("--batch", type=int, default=None, help="B of the named workload")
+    ap.add_argument("--no-draft", action="store_true",
+                    help="greedy workloads: call without the draft's logits (only target rows are read)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -87,29 +93,49 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    name = workloads.HEADLINE
+    name = args.workload or workloads.HEADLINE
+    kw = {} if args.batch is None else {"B": args.batch}
+    if args.batch is not None and name not in ("latency_b1", "worked_example"):
+        kw = {}
+        print("--batch applies to latency_b1 and worked_example only", file=sys.stderr)
     sets = []
     for r in range(args.sets):
-        w = workloads.config(name, device=dev, gen_seed=1000 + r, seed=r)
+        w = workloads.config(name, device=dev, gen_seed=1000 + r, seed=r, **kw)
         sets.append(w)
-    v = binding.Verifier(64, 4, 128256, torch.bfloat16, 0)
-    sampler = binding.Verifier(64 * 4, 0, 128256, torch.bfloat16, 0)
-    for w in sets:
-        toks, st = sampler.sample(w.draft, seed=w.draft_seed, default_mode=w.default_mode,
-                                  default_temperature=w.default_temperature,
-                                  default_top_p=w.default_top_p)
-        w.draft_tokens = toks.to(torch.int32).contiguous()
-    torch.cuda.synchronize()
-    sampler.close()
     w0 = sets[0]
     B, K, V = w0.B, w0.K_max, w0.V
+    no_draft = args.no_draft
+    if no_draft and (w0.mode is not None or w0.default_mode != workloads.GREEDY):
+        print("--no-draft needs a greedy workload", file=sys.stderr)
+        sys.exit(2)
+    v = binding.Verifier(B, K, V, w0.target.dtype, 0)
+    # draft tokens: one draw per draft row by the library itself (the step
+    # with K = 0), from each row's own filtered distribution
+    sampler = binding.Verifier(B * K, 0, V, w0.target.dtype, 0)
+    for w in sets:
+        md, tmp, tk, tp = w.row_params()
+        toks, st = sampler.sample(w.draft, seed=w.draft_seed, mode=md, temperature=tmp, top_k=tk, top_p=tp,
+                                  default_mode=w.default_mode, default_temperature=w.default_temperature,
+                                  default_top_k=w.default_top_k, default_top_p=w.default_top_p)
+        toks = toks.to(torch.int32)
+        if w.k_per_row is not None:   # padding slots hold token 0
+            pad = torch.arange(K, device=dev).unsqueeze(0) >= w.k_per_row.to(dev).unsqueeze(1)
+            toks = torch.where(pad, torch.zeros_like(toks), toks)
+        w.draft_tokens = toks.contiguous()
+    torch.cuda.synchronize()
+    sampler.close()
     alg_bytes = w0.algorithmic_bytes()
+    if no_draft:   # only the target rows t <= K_b
+        es = w0.target.element_size()
+        kb = B * K if w0.k_per_row is None else int(w0.k_per_row.to(torch.int64).sum().item())
+        alg_bytes = (kb + B) * V * es
     outs = [v.outputs(B, K) for _ in sets]
     stream = torch.cuda.current_stream(dev)
-    argss = [binding.make_args(w.target, w.draft, w.draft_tokens, accepted=o[0], out_tokens=o[1],
-                               row_status=o[2], diag=o[3], default_mode=w.default_mode,
-                               default_temperature=w.default_temperature,
-                               default_top_p=w.default_top_p, seed=w.seed)
+    argss = [binding.make_args(w.target, None if no_draft else w.draft, w.draft_tokens, accepted=o[0],
+                               out_tokens=o[1], row_status=o[2], diag=o[3], k_per_row=w.k_per_row, mode=w.mode,
+                               temperature=w.temperature, top_k=w.top_k, top_p=w.top_p,
+                               default_mode=w.default_mode, default_temperature=w.default_temperature,
+                               default_top_k=w.default_top_k, default_top_p=w.default_top_p, seed=w.seed)
              for w, o in zip(sets, outs)]
 
     def step(i):
@@ -139,8 +165,8 @@ def main():
     for i in range(args.steps):
         step(i)
     runs, (stage0_ms, stage1_ms) = binding.spec_verify_profile_end(v.handle)
-    stream_ms = stage0_ms / runs        # the streaming pass (chunk kernel)
-    seq_ms = stage1_ms / runs           # per-sequence merge, accept walk, draw
+    stream_ms = stage0_ms / runs        # the row kernel: streaming pass and each row's finish
+    seq_ms = stage1_ms / runs           # per-sequence accept walk and draw
     achieved = alg_bytes / (stream_ms * 1e-3) / 1e9
 
     # per-call spread: each call bracketed by its own pair of events
@@ -158,12 +184,12 @@ def main():
     # streaming ceiling: the library's read-only probe over the same rotating
     # logits (same access pattern as the streaming pass, no arithmetic)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    probe_bytes = sum(w.target.numel() * w.target.element_size() + w.draft.numel() * w.draft.element_size()
-                      for w in sets) / len(sets)
+    probe_tensors = lambda w: (w.target,) if no_draft else (w.target, w.draft)
+    probe_bytes = sum(x.numel() * x.element_size() for w in sets for x in probe_tensors(w)) / len(sets)
 
     def probe(i):
         w = sets[i % len(sets)]
-        for x in (w.target, w.draft):
+        for x in probe_tensors(w):
             binding.spec_verify_stream_probe(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(),
                                              stream.cuda_stream)
 
@@ -213,9 +239,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",  # bf16 logits decoded exactly to fp32; fp32 terms, fp64 sums
         "data": "synthetic",
-        "config": {"workload": name, "B": B, "K": K, "V": V, "dtype": "bf16", "mode": "top-p",
-                   "top_p": w0.default_top_p, "temperature": w0.default_temperature,
-                   "input_sets": len(sets), "parallelism": "single-gpu"},
+        "config": workload_config(w0, name, len(sets), no_draft),
         "logits_GBps": gbs_step,
         "pct_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS,
         "stage_ms": {"stream": stream_ms, "sequence": seq_ms},
@@ -223,11 +247,11 @@ def main():
                         "note": "each call bracketed by its own events"},
         "streaming_ceiling": {"GBps": ceiling, "kernel": "stream_probe_kernel",
                               "pct_hbm_peak": 100.0 * ceiling / HBM_PEAK_GBS,
-                              "chunk_kernel_frac_of_ceiling": achieved / ceiling,
+                              "row_kernel_frac_of_ceiling": achieved / ceiling,
                               "value_frac_of_ceiling": gbs_step / ceiling},
         "mean_accepted": alpha_tokens,
         "loop_model": loop,
-        "roofline": {"bound": "hbm", "kernel": "chunk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "row_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
@@ -235,6 +259,24 @@ def main():
     }
     v.close()
     print(json.dumps(line), flush=True)
+
+
+def workload_config(w, name, nsets, no_draft):
+    modes = {0: "plain", 1: "top-k", 2: "top-p", 3: "greedy"}
+    c = {"workload": name, "B": w.B, "K": w.K_max, "V": w.V, "dtype": w.dtype,
+         "mode": "per-sequence" if w.mode is not None else modes[w.default_mode]}
+    if w.mode is None and w.default_mode == 2:
+        c["top_p"] = w.default_top_p
+    if w.mode is None and w.default_mode == 1:
+        c["top_k"] = w.default_top_k
+    if w.mode is not None or w.default_mode != 3:
+        c["temperature"] = w.default_temperature
+    if w.k_per_row is not None:
+        c["k_per_row"] = "ragged"
+    if no_draft:
+        c["draft_logits"] = "none"
+    c.update({"input_sets": nsets, "parallelism": "single-gpu"})
+    return c
 
 
 def calibrate_copy(torch, nbytes, steps):

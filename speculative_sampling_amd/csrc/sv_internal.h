@@ -56,13 +56,11 @@ constexpr uint32_t kRfListOk = 1u << 16;
 // The row's chunk records (ChunkRec) were written.
 constexpr uint32_t kRfChunks = 1u << 17;
 
-// One token of a target row's kept set: vocabulary index, the target's logit
-// and, for positions that score a draft token, the draft's logit there.
+// One token of a target row's kept set: vocabulary index and the target's
+// logit.
 struct KeptEntry {
   int32_t idx;
   float xq;
-  float xp;
-  int32_t pad;
 };
 
 struct KParams {

@@ -580,10 +580,10 @@ struct SoftChunk {
 // A term is rounded in its exponent x c2 - o, so it is accurate to about
 // |x c2 - o| 2^-24 relative, and the largest terms, which dominate the sum,
 // need o close to the maximum.  The offset is the floor of the largest
-// x c2 of the wave's earlier chunks (for its first chunk, of the largest
-// logit of the lanes' first vectors); a chunk whose lane sums exceed 2^8 (a
-// logit well above that), or hold a NaN or inf, is re-read and redone from
-// its exact maximum.  The re-read keeps the first pass's registers free as
+// x c2 of the wave's earlier chunks (for its first chunk, of that chunk's
+// own maximum); a chunk whose lane sums exceed 2^8 (a logit well above
+// that), or hold a NaN or inf, is re-read and redone from its exact
+// maximum.  The re-read keeps the first pass's registers free as
 // soon as each vector's terms are taken.
 template <int DT, bool VEC>
 __device__ __forceinline__ SoftChunk soft_chunk(uint4 (&buf)[kLoads], float c2, const char* row, int c0, int c1,
@@ -592,11 +592,15 @@ __device__ __forceinline__ SoftChunk soft_chunk(uint4 (&buf)[kLoads], float c2, 
   SoftChunk out;
   out.ok = true;
   if (first) {
+    // the wave's first chunk: its exact maximum (once per wave)
     float r = -kInf;
 #pragma unroll
-    for (int k = 0; k < VE; ++k) r = fmaxf(r, elem<DT>(buf[0], k));
+    for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+      for (int k = 0; k < VE; ++k) r = fmaxf(r, elem<DT>(buf[i], k));
     r = wave_max(r);
     if (r > -kInf) raise_offset(sa, r * c2);
+    unpack_barrier(buf);  // unpack again below rather than hold 64 values
   }
   float em;
   out.zt = exp_terms<DT>(buf, c2, sa.o, emax, &em);
@@ -920,7 +924,6 @@ struct RowSmem {
   Hist h;
   float kx[kListMax];              // the kept set in vocabulary order: logits
   int ki[kListMax];                //   and vocabulary indices
-  float kp[kListMax];              //   and the draft's logits there (resample positions)
   float pub[kRowWaves];            // each wave's running maximum (nucleus) or cut (top-k)
   float ucut[kRowWaves];           // the largest listing cut each wave used
   int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
@@ -944,12 +947,14 @@ __device__ __forceinline__ float published_max(const RowSmem& sm) {
 }
 
 // Lists the lane's vectors flagged in `mask` (slot i holds logits
-// c0 + (i * 64 + lane) * VE + [0, VE)) in the wave's LDS list from position
-// n, as (first vocabulary index, key), in (slot, lane) order, which is
-// increasing vocabulary index.  Returns the new count; entries beyond
-// kCandVecs are counted, not stored.
-__device__ __forceinline__ int list_vectors(RowSmem& sm, int wv, int n, uint32_t mask, const float (&key)[kLoads],
-                                            int c0, int ve, int lane) {
+// c0 + (i * 64 + lane) * VE + [0, VE), its data in buf[i]) in the wave's
+// LDS list from position n, as (data, first vocabulary index, key), in
+// (slot, lane) order, which is increasing vocabulary index.  Returns the new
+// count; entries beyond kCandVecs are counted, not stored.
+// key(i) gives slot i's key; it is evaluated only for flagged slots.
+template <class Key>
+__device__ __forceinline__ int list_vectors(RowSmem& sm, int wv, int n, uint32_t mask, Key&& key,
+                                            const uint4 (&buf)[kLoads], int c0, int ve, int lane) {
   const int e0 = c0 + lane * ve;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -959,8 +964,9 @@ __device__ __forceinline__ int list_vectors(RowSmem& sm, int wv, int n, uint32_t
       if (h) {
         const int pos = n + lanes_below(bal);
         if (pos < kCandVecs) {
+          sm.cv[wv][pos] = buf[i];
           sm.ci[wv][pos] = e0 + i * kWave * ve;
-          sm.ck[wv][pos] = key[i];
+          sm.ck[wv][pos] = key(i);
         }
       }
       n += __popcll(bal);
@@ -978,11 +984,14 @@ __device__ __forceinline__ int compact_listed(RowSmem& sm, int wv, int n, float 
     const bool keep = j < n && sm.ck[wv][j] >= cut;
     const int idx = j < n ? sm.ci[wv][j] : 0;
     const float key = j < n ? sm.ck[wv][j] : 0.0f;
+    const uint4 v = j < n ? sm.cv[wv][j] : make_uint4(0, 0, 0, 0);
     const uint64_t bal = __ballot(keep);
     wave_sync();
     if (keep) {
-      sm.ci[wv][m + lanes_below(bal)] = idx;
-      sm.ck[wv][m + lanes_below(bal)] = key;
+      const int pos = m + lanes_below(bal);
+      sm.ci[wv][pos] = idx;
+      sm.ck[wv][pos] = key;
+      sm.cv[wv][pos] = v;
     }
     m += __popcll(bal);
     wave_sync();
@@ -1023,28 +1032,6 @@ __device__ __forceinline__ float raise_cut(const RowSmem& sm, int wv, int n, flo
     }
   }
   return best;
-}
-
-// After a wave's last chunk: keeps its listed vectors whose key reaches
-// `cut`, in order, and loads them from the row into the wave's part of the
-// LDS buffer (all loads of a lane in flight together).  Returns how many.
-template <int DT, bool VEC>
-__device__ __forceinline__ int gather_listed(RowSmem& sm, int wv, int n, float cut, const char* row, int V, int lane) {
-  constexpr int Q = kCandVecs / kWave;
-  const int m = compact_listed(sm, wv, n, cut, lane);
-  uint4 v[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = q * kWave + lane;
-    v[q] = make_uint4(0, 0, 0, 0);
-    if (j < m) v[q] = load_vec<DT, VEC>(row, sm.ci[wv][j], V);
-  }
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = q * kWave + lane;
-    if (j < m) sm.cv[wv][j] = v[q];
-  }
-  return m;
 }
 
 template <int DT>
@@ -1261,7 +1248,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       uint32_t mask = 0;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= cf ? (1u << i) : 0u;
-      int n = list_vectors(sm, wv, nc, mask, vmax, c0, VE, ln);
+      int n = list_vectors(sm, wv, nc, mask, [&](int i) { return vmax[i]; }, buf, c0, VE, ln);
       if (n > kCandVecs) {
         // Raise the cut to the need-th largest listed key (or near it),
         // drop the entries below it, and list the chunk again.
@@ -1274,7 +1261,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         mask = 0;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) mask |= vmax[i] >= cf2 ? (1u << i) : 0u;
-        n = list_vectors(sm, wv, nc, mask, vmax, c0, VE, ln);
+        n = list_vectors(sm, wv, nc, mask, [&](int i) { return vmax[i]; }, buf, c0, VE, ln);
       }
       if (n > kCandVecs) over = true;
       else nc = n;
@@ -1317,13 +1304,12 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
           // (the exponent is >= -10.01: o never exceeds g c2)
           const float thr = __builtin_amdgcn_exp2f((float)((double)cut * (double)c2 - (double)ch.o) - 0.00390625f);
           uint32_t mask = 0;
-          float key[kLoads];  // the vector's largest logit, from its largest term (fp32 suffices)
 #pragma unroll
-          for (int i = 0; i < kLoads; ++i) {
-            mask |= emax[i] >= thr ? (1u << i) : 0u;
-            key[i] = (__builtin_amdgcn_logf(emax[i]) + ch.o) * ic2f;  // only read where emax[i] >= thr
-          }
-          const int n = list_vectors(sm, wv, nc, mask, key, c0, VE, ln);
+          for (int i = 0; i < kLoads; ++i) mask |= emax[i] >= thr ? (1u << i) : 0u;
+          // the key: the vector's largest logit, from its largest term (fp32 suffices)
+          const float o = ch.o;
+          const int n = list_vectors(
+              sm, wv, nc, mask, [&](int i) { return (__builtin_amdgcn_logf(emax[i]) + o) * ic2f; }, buf, c0, VE, ln);
           if (n <= kCandVecs) {
             nc = n;
             done = true;
@@ -1363,14 +1349,13 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     }
   }
   if ((is_topk || is_topp) && !over && nc > 0) {
-    // Keep the listed vectors that can still hold a kept token and load
-    // them: for top-k those at or above the largest cut published, for a
-    // nucleus those within 10 log2 units of the largest chunk maximum
-    // known (keys are within 2^-8 / c2 of the vectors' maxima).
+    // Keep the listed vectors that can still hold a kept token: for top-k
+    // those at or above the largest cut published, for a nucleus those
+    // within 10 log2 units of the largest chunk maximum known (keys are
+    // within 2^-8 / c2 of the vectors' maxima).
     const float g = fmaxf(run, published_max(sm));
     const float fcut = is_topk ? g : (float)((double)g - kCandLog2 * ic2);
-    nc = gather_listed<DT, VEC>(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), row, P.V,
-                                lane);
+    nc = compact_listed(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), lane);
     ucut = fmaxf(ucut, fcut);
   }
   {
@@ -1470,24 +1455,6 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     v = sm.cv[w][pos];
     e0 = sm.ci[w][pos];
   };
-  // The draft's logits at the candidates of a target row whose position
-  // may be resampled: loaded now, while the selection runs, for the kept
-  // list (candidate j is thread j mod kThreads's, in round j / kThreads).
-  constexpr int kRounds = kRowWaves * kCandVecs / kThreads;
-  const bool want_p = selecting && tgt && t < sp.Kb && P.draft != nullptr;
-  const char* drow = want_p ? static_cast<const char*>(row_ptr<DT>(P, b, false, t)) : nullptr;
-  uint4 dv[kRounds];
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int j = q * kThreads + tid;
-    dv[q] = make_uint4(0, 0, 0, 0);
-    if (want_p && j < N) {
-      uint4 v;
-      int e0;
-      vec_at(j, v, e0);
-      dv[q] = load_vec<DT, VEC>(drow, e0, P.V);
-    }
-  }
   if (!(rr.flags & kErrBits)) {
     if (is_plain) {
       rr.Zs = Z;
@@ -1582,10 +1549,10 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
 
   if (list_ok) {
     // the kept set, in vocabulary order: the candidates >= T, compacted in
-    // buffer order by the work-group, then written out with the draft's
-    // logits at the same tokens (for a resample at this position)
+    // buffer order by the work-group, then written out
     rr.flags |= kRfListOk;
     int nk = 0;
+    constexpr int kRounds = kRowWaves * kCandVecs / kThreads;
 #pragma unroll
     for (int q = 0; q < kRounds; ++q) {
       const int j0 = q * kThreads;
@@ -1618,7 +1585,6 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
           if (off < kListMax) {
             sm.kx[off] = elem<DT>(v, k);
             sm.ki[off] = e0 + k;
-            sm.kp[off] = want_p ? elem<DT>(dv[q], k) : __builtin_nanf("");
           }
           ++off;
         }
@@ -1632,8 +1598,6 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       KeptEntry ke;
       ke.idx = sm.ki[j];
       ke.xq = sm.kx[j];
-      ke.xp = sm.kp[j];
-      ke.pad = 0;
       kl[j] = ke;
     }
   }
@@ -1741,11 +1705,13 @@ __device__ __forceinline__ float prob(const RowW& w, float x) {
 // Inverse CDF over the target's kept set in vocabulary order (one wave):
 // w = (q - p)+ when resampling, else w = q.  Entry i sits in slot i / 64 of
 // lane i % 64, so a set of up to 64 tokens costs one wave step per stage.
-// The set and the draft's logits at its tokens come from the row kernel's
-// kept list kl.  The draft's weights are fp32 terms as in prob().
+// The set comes from the row kernel's kept list kl; a resample reads the
+// draft's logits at its tokens from the draft row prow (only the row of the
+// first rejection is read, and only there).  The draft's weights are fp32
+// terms as in prob().
 template <int DT>
 __device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, const RowRec& rp,
-                                               const KeptEntry* kl, double u, int lane) {
+                                               const KeptEntry* kl, const void* prow, double u, int lane) {
   constexpr int E = kListMax / kWave;
   const int N = rq.n_keep;  // <= kListMax
   const int ns = (N + kWave - 1) / kWave;
@@ -1763,8 +1729,14 @@ __device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, 
     const int i = j * kWave + lane;
     ke[j].idx = 0;
     ke[j].xq = -kInf;
-    ke[j].xp = -kInf;
     if (j < ns && i < N) ke[j] = kl[i];
+  }
+  float xp[E];  // the draft's logits at the kept tokens (a resample only)
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int i = j * kWave + lane;
+    xp[j] = -kInf;
+    if (resample && j < ns && i < N) xp[j] = load_logit<DT>(prow, ke[j].idx);
   }
 #pragma unroll
   for (int j = 0; j < E; ++j) {
@@ -1775,7 +1747,7 @@ __device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, 
     if (j < ns && i < N) {
       iv[j] = ke[j].idx;
       qv[j] = (double)mass_of(ke[j].xq, c2q, oM, fM) * inv;
-      if (resample) pv[j] = prob(wp, ke[j].xp);
+      if (resample) pv[j] = prob(wp, xp[j]);
     }
   }
   Draw d;
@@ -2275,7 +2247,8 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
         write_tokens(P, b, n, y, st, lane, kWave);
       } else if (rq.flags & kRfListOk) {
         const KeptEntry* kl = P.kept + ((size_t)b * (KM + 1) + n) * (size_t)min(kListMax, P.V);
-        const Draw d = draw_from_list<DT>(rq, resample, rp, kl, u, lane);
+        const void* prow = resample && have_draft ? row_ptr<DT>(P, b, false, n) : nullptr;
+        const Draw d = draw_from_list<DT>(rq, resample && have_draft, rp, kl, prow, u, lane);
         write_tokens(P, b, n, d.y, st | d.flags, lane, kWave);
       } else {
         job = 1;
