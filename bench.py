@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="B of the named workload")
     ap.add_argument("--no-draft", action="store_true",
                     help="greedy workloads: call without the draft's logits (only target rows are read)")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="only sweep the read-only probe's loads per lane and waves per CU over rotating "
+                         "buffers of the headline's logit bytes and of 2 GiB; one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -87,6 +90,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy, args.steps)
+        return
+    if args.probe_sweep:
+        probe_sweep(torch, args.steps, args.warmup)
         return
 
     from speculative_sampling_amd import binding, loop_model, workloads
@@ -291,6 +297,54 @@ def calibrate_copy(torch, nbytes, steps):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
                       "launches": steps}), flush=True)
+
+
+def probe_sweep(torch, steps, warmup):
+    """Read rate of the persistent read-only probe for 4, 8 and 16 loads per
+    lane and 1 to 32 waves per CU, over rotating buffers (4 of the
+    headline's 147,750,912 logit bytes per call, 2 of 2 GiB), next to the
+    fixed probe (one wave per 8 KB block).  Each point: warmup untimed
+    launches, then steps launches between two events."""
+    from speculative_sampling_amd import binding
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    sizes = [(147750912, 4), (2 << 30, 2)]
+    out = {"probe_sweep": [], "steps": steps, "warmup": warmup}
+    for nbytes, nbuf in sizes:
+        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+
+        def rate(launch):
+            for i in range(warmup):
+                launch(bufs[i % nbuf])
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for i in range(steps):
+                launch(bufs[i % nbuf])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return nbytes / (t0.elapsed_time(t1) / steps * 1e-3) / 1e9
+
+        fixed = rate(lambda b: binding.spec_verify_stream_probe(b.data_ptr(), nbytes, sink.data_ptr(),
+                                                                stream.cuda_stream))
+        points = []
+        for loads in (4, 8, 16):
+            for waves in (1, 2, 4, 8, 12, 16, 24, 32):
+                g = rate(lambda b: binding.spec_verify_stream_probe_sweep(b.data_ptr(), nbytes, loads, waves,
+                                                                          sink.data_ptr(), stream.cuda_stream))
+                points.append({"loads_per_lane": loads, "waves_per_cu": waves, "GBps": round(g, 1)})
+                print(f"# bytes={nbytes} loads={loads} waves={waves}: {g:.1f} GB/s", file=sys.stderr, flush=True)
+        best = max(points, key=lambda q: q["GBps"])
+        out["probe_sweep"].append({"bytes_per_launch": nbytes, "buffers": nbuf,
+                                   "fixed_probe_GBps": round(fixed, 1), "best": best,
+                                   "best_pct_hbm_peak": 100.0 * best["GBps"] / HBM_PEAK_GBS, "points": points})
+        del bufs
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, budget_s, threads=1):

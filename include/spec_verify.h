@@ -208,17 +208,33 @@ uint64_t spec_verify_workspace_bytes(const sv_config* cfg);
 int spec_verify_profile_begin(sv_handle_t h, int max_calls);
 int spec_verify_profile_end(sv_handle_t h, double* ms, int n_stages);
 
-/* Streaming ceiling, for measurement: reads the first floor(bytes / 16384)
- * whole 16 KB blocks at data (a 16-byte aligned device pointer) once, with
- * the streaming pass's access pattern (one 16 KB block per wave, 16-byte
- * vectors, constant offsets, non-temporal loads) and no arithmetic beyond an
- * xor fold, on the
- * given stream (NULL = the default stream), asynchronously.  out is a device
+/* Streaming ceiling, for measurement: reads the first floor(bytes / 8192)
+ * whole 8 KB blocks at data (a 16-byte aligned device pointer) once, with
+ * the streaming pass's chunk (one 8 KB block per wave, 16-byte vectors,
+ * constant offsets, non-temporal loads) and no arithmetic beyond an xor
+ * fold, on the given stream (NULL = the default stream), asynchronously.
+ * One wave per block: the grid is as large as the data.  out is a device
  * pointer to at least 4 bytes; it is written only when the fold hits a
  * fixed value.  Allocates nothing.  Returns SV_OK, or SV_EINVAL / SV_EHIP
  * with spec_verify_last_error set.  It computes nothing of the method: it
  * gives the read rate the streaming pass is measured against. */
 int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* stream);
+
+/* One point of a read-rate sweep, for measurement: reads the first
+ * floor(bytes / (loads_per_lane * 1024)) whole blocks at data (16-byte
+ * aligned) once, a block being 64 lanes x loads_per_lane 16-byte vectors,
+ * with a persistent grid of waves_per_cu * 256 waves in work-groups of 4.
+ * Work-group g takes the g-th of equal contiguous ranges of blocks, its
+ * waves take the range's blocks in turn, and each wave keeps its next
+ * block's loads in flight while it folds the current one (non-temporal
+ * loads, an xor fold).  loads_per_lane is 4, 8 or 16; waves_per_cu is 1 to
+ * 32.  data, out and stream as for spec_verify_stream_probe; asynchronous,
+ * allocates nothing.  Returns SV_OK, or SV_EINVAL (a NULL or unaligned
+ * pointer, a parameter out of range: nothing is launched) / SV_EHIP, with
+ * spec_verify_last_error set.  Sweeping both parameters gives the read rate
+ * of the memory system apart from any one access pattern. */
+int spec_verify_stream_probe_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, void* out,
+                                   void* stream);
 
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Runs the

@@ -27,7 +27,7 @@ ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 EXPORTS = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy",
            "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_profile_begin",
            "spec_verify_profile_end", "spec_verify_stream_probe", "spec_verify_last_error",
-           "spec_verify_run_static")
+           "spec_verify_run_static", "spec_verify_stream_probe_sweep")
 
 # Size of the static device buffer spec_verify_run_static works in.
 SV_STATIC_SCRATCH_BYTES = 64 << 20
@@ -80,6 +80,9 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_profile_end.restype = ctypes.c_int
     lib.spec_verify_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.spec_verify_stream_probe.restype = ctypes.c_int
+    lib.spec_verify_stream_probe_sweep.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_verify_stream_probe_sweep.restype = ctypes.c_int
     lib.spec_verify_run_static.argtypes = [ctypes.POINTER(SvConfig), ctypes.POINTER(SvArgs), ctypes.c_void_p]
     lib.spec_verify_run_static.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
@@ -229,12 +232,24 @@ def spec_verify_profile_end(handle: int):
 
 
 def spec_verify_stream_probe(data_ptr: int, nbytes: int, out_ptr: int, stream: int = 0) -> None:
-    """Reads nbytes // 16384 whole 16 KB blocks at data_ptr once (a
+    """Reads nbytes // 8192 whole 8 KB blocks at data_ptr once (a
     measurement of the streaming ceiling; see the header)."""
     rc = load_library().spec_verify_stream_probe(ctypes.c_void_p(data_ptr), nbytes, ctypes.c_void_p(out_ptr),
                                                  ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_stream_probe")
+
+
+def spec_verify_stream_probe_sweep(data_ptr: int, nbytes: int, loads_per_lane: int, waves_per_cu: int,
+                                   out_ptr: int, stream: int = 0) -> None:
+    """One point of the read-rate sweep: whole blocks of 64 x loads_per_lane
+    16-byte vectors at data_ptr read once by a persistent grid of
+    waves_per_cu waves per compute unit (see the header)."""
+    rc = load_library().spec_verify_stream_probe_sweep(ctypes.c_void_p(data_ptr), nbytes, loads_per_lane,
+                                                       waves_per_cu, ctypes.c_void_p(out_ptr),
+                                                       ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_stream_probe_sweep")
 
 
 class Verifier:

@@ -321,6 +321,21 @@ int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* st
   return SV_OK;
 }
 
+int spec_verify_stream_probe_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, void* out,
+                                   void* stream) {
+  if (!data || !out) return fail(SV_EINVAL, "stream probe sweep: data and out must be device pointers");
+  if (reinterpret_cast<uintptr_t>(data) % 16 != 0)
+    return fail(SV_EINVAL, "stream probe sweep: data must be 16-byte aligned");
+  if (loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16)
+    return fail(SV_EINVAL, "stream probe sweep: loads_per_lane must be 4, 8 or 16");
+  if (waves_per_cu < 1 || waves_per_cu > 32)
+    return fail(SV_EINVAL, "stream probe sweep: waves_per_cu must be in [1, 32]");
+  const hipError_t e = sv::launch_stream_sweep(data, bytes, loads_per_lane, waves_per_cu, static_cast<uint32_t*>(out),
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("stream probe sweep launch failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}
+
 int spec_verify_destroy(sv_handle_t h) {
   if (!h) return SV_OK;
   int prev = 0;

@@ -98,7 +98,10 @@ struct KParams {
 // dispatch.
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream,
                          hipEvent_t* ev = nullptr);
-// Reads the first bytes / 16384 whole 16 KB blocks of data once (see spec_verify_stream_probe).
+// Reads the first bytes / 8192 whole 8 KB blocks of data once (see spec_verify_stream_probe).
 hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hipStream_t stream);
+// One point of the read-rate sweep (see spec_verify_stream_probe_sweep).
+hipError_t launch_stream_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, uint32_t* out,
+                               hipStream_t stream);
 
 }  // namespace sv

@@ -5,15 +5,16 @@
 //
 //   row_kernel   one work-group of 4 waves per logit row (target positions
 //                0..K_b and draft positions 0..K_b-1 of every sequence).
-//                The waves stream the row from HBM once, 16 KB per wave at a
-//                time into registers, and reduce it: the sum of the terms
-//                2^((x - m) c2) and the maximum of every chunk, the greedy
-//                argmax, and the candidate vectors of a top-k / nucleus kept
-//                set, which stay in LDS.  Then one wave finishes the row:
-//                log-sum-exp over the chunks, the threshold by radix
-//                selection over the candidates, the kept mass, the
-//                probability of the row's draft token and, for target rows,
-//                the kept set in vocabulary order.
+//                The waves stream the row from HBM once, 8 KB per wave at a
+//                time into registers, two chunks in flight, and reduce it:
+//                the sum of the terms 2^((x - m) c2) and the maximum of
+//                every chunk, the greedy argmax, and the candidate vectors
+//                of a top-k / nucleus kept set, which stay in LDS.  Then the
+//                whole work-group finishes the row: log-sum-exp over the
+//                chunks, the threshold by radix selection over the
+//                candidates, the kept mass, the probability of the row's
+//                draft token and, for target rows, the kept set in
+//                vocabulary order.
 //   seq_kernel   one work-group per sequence: the accept walk, the first
 //                rejection, the resample from normalize((q - p)+) or the
 //                bonus draw, and the outputs.
@@ -54,9 +55,10 @@ constexpr double kLog2e = 1.4426950408889634074;
 // accumulation makes histogram sums independent of atomic order.
 constexpr double kFix = 1099511627776.0;  // 2^40
 constexpr double kWindow = 1e-6;
-// Nucleus candidates: tokens whose term is within 2^-10 of the chunk's
-// largest term (on the pages' workloads a window of 2^-8 to 2^-9.4 already
-// covers the nucleus; a list that overflows is retried with 2^-8, 2^-6).
+// Nucleus candidates: tokens whose term is within 2^-10 of the largest term
+// known (on the pages' workloads a window of 2^-8 to 2^-9.4 already covers
+// the nucleus; a list that would overflow is compacted and retried with the
+// windows 2^-8, 2^-6, 2^-5, 2^-4, 2^-3, 2^-2).
 constexpr float kCandLog2 = 10.0f;
 
 constexpr uint32_t kPurposeAccept = 0, kPurposeResample = 1, kPurposeBonus = 2;
@@ -2307,7 +2309,7 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
 namespace {
 
 // Read-only streaming probe with the streaming pass's access pattern and
-// non-temporal loads: each wave reads one 16 KB block as 16 x 16-byte
+// non-temporal loads: each wave reads one 8 KB block as 8 x 16-byte
 // vectors per lane from one base address with constant offsets, and folds it
 // with xor.  out[0] is written only if the fold hits a fixed value, so the
 // loads cannot be dropped.
@@ -2326,6 +2328,57 @@ __global__ __launch_bounds__(kThreads) void stream_probe_kernel(const uint4* dat
 }
 
 }  // namespace
+
+// Read-rate sweep: work-group g reads blocks [g n / G, (g + 1) n / G) of
+// NL x 64 vectors each, its waves taking the blocks in turn, with the next
+// block's loads in flight while the current one is folded.
+template <int NL>
+__global__ __launch_bounds__(kThreads) void stream_sweep_kernel(const uint4* data, size_t nblocks, uint32_t* out) {
+  const int lane = (int)__lane_id();
+  const int wv = (int)(threadIdx.x / kWave);
+  const size_t G = gridDim.x;
+  const size_t b0 = nblocks * blockIdx.x / G, b1 = nblocks * (blockIdx.x + 1) / G;
+  uint4 a[NL], c[NL];
+  auto issue = [&](uint4 (&v)[NL], size_t b) {
+    const uint4* base = data + (b < b1 ? b : b1 - 1) * (size_t)(NL * kWave);  // (a block past the range: its last, again)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = load_stream(&base[i * kWave + lane]);
+  };
+  uint32_t x = 0;
+  auto fold = [&](const uint4 (&v)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  };
+  size_t b = b0 + wv;
+  if (b < b1) {
+    issue(a, b);
+    while (true) {
+      issue(c, b + kRowWaves);
+      fold(a);
+      b += kRowWaves;
+      if (b >= b1) break;
+      issue(a, b + kRowWaves);
+      fold(c);
+      b += kRowWaves;
+      if (b >= b1) break;
+    }
+  }
+  if (x == 0x9e3779b9u) out[0] = x;
+}
+
+hipError_t launch_stream_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, uint32_t* out,
+                               hipStream_t stream) {
+  const size_t nblocks = bytes / ((size_t)loads_per_lane * kWave * sizeof(uint4));
+  if (nblocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)(256 * waves_per_cu / kRowWaves)), block(kThreads);
+  const uint4* d = static_cast<const uint4*>(data);
+  switch (loads_per_lane) {
+    case 4: hipLaunchKernelGGL(stream_sweep_kernel<4>, grid, block, 0, stream, d, nblocks, out); break;
+    case 8: hipLaunchKernelGGL(stream_sweep_kernel<8>, grid, block, 0, stream, d, nblocks, out); break;
+    default: hipLaunchKernelGGL(stream_sweep_kernel<16>, grid, block, 0, stream, d, nblocks, out); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hipStream_t stream) {
   const size_t nblocks = bytes / (kLoads * kWave * sizeof(uint4));

@@ -172,6 +172,12 @@ def test_stream_probe_rejects_bad_pointers_on_the_host():
     assert lib.spec_verify_stream_probe(ctypes.c_void_p(64), 16384, None, None) == SV_EINVAL
     assert lib.spec_verify_stream_probe(ctypes.c_void_p(8), 16384, ctypes.byref(sink), None) == SV_EINVAL
     assert b"aligned" in lib.spec_verify_last_error()
+    # the sweep probe checks the same, and its block and grid parameters
+    assert lib.spec_verify_stream_probe_sweep(None, 16384, 8, 4, ctypes.byref(sink), None) == SV_EINVAL
+    assert lib.spec_verify_stream_probe_sweep(ctypes.c_void_p(8), 16384, 8, 4, ctypes.byref(sink), None) == SV_EINVAL
+    for loads, waves in [(2, 4), (12, 4), (8, 0), (8, 33), (32, 4)]:
+        assert lib.spec_verify_stream_probe_sweep(ctypes.c_void_p(64), 16384, loads, waves,
+                                                  ctypes.byref(sink), None) == SV_EINVAL
 
 
 def test_verifier_refuses_logits_that_disagree_with_the_handle():
