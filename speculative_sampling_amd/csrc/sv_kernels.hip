@@ -265,14 +265,42 @@ __device__ __forceinline__ int raw_mode(const KParams& P, int b) {
   return P.mode ? (int)P.mode[b] : P.dmode;
 }
 
-// The sequence's parameters as stored (the loads only) ...
-__device__ __forceinline__ SeqParams raw_params(const KParams& P, int b) {
+// A load whose address is the same for the whole wave, through the scalar
+// cache: its wait (lgkmcnt) is apart from that of the vector loads in
+// flight, so it never waits for a chunk of logits issued before it.  Only
+// for 4-byte values that no kernel of the call writes.
+template <class T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  static_assert(sizeof(T) == 4, "scalar loads of 4-byte values");
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// A load from global memory as such (not through a generic address), so
+// that waiting for it never waits for the loads issued after it.
+template <class T>
+__device__ __forceinline__ T global_load(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// The sequence's parameters as stored (the loads only) ...  kDirect: the
+// per-sequence values are loaded from global memory as such (the compiler
+// takes them through the scalar cache), else through generic addresses
+// (fewer scalar registers: the instance holding every mode's path).
+template <bool kDirect = true>
+__device__ __forceinline__ SeqParams raw_params(const KParams& P, int b, int mode) {
   SeqParams s;
-  s.Kb = P.kpr ? P.kpr[b] : P.K_max;
-  s.mode = raw_mode(P, b);
-  s.tau = P.temp ? P.temp[b] : P.dtemp;
-  s.topk = P.topk ? P.topk[b] : P.dtopk;
-  s.topp = P.topp ? P.topp[b] : P.dtopp;
+  s.mode = mode;
+  if constexpr (kDirect) {
+    s.Kb = P.kpr ? uniform_load(P.kpr + b) : P.K_max;
+    s.tau = P.temp ? global_load(P.temp + b) : P.dtemp;
+    s.topk = P.topk ? global_load(P.topk + b) : P.dtopk;
+    s.topp = P.topp ? global_load(P.topp + b) : P.dtopp;
+  } else {
+    s.Kb = P.kpr ? P.kpr[b] : P.K_max;
+    s.tau = P.temp ? P.temp[b] : P.dtemp;
+    s.topk = P.topk ? P.topk[b] : P.dtopk;
+    s.topp = P.topp ? P.topp[b] : P.dtopp;
+  }
   s.c2 = 0.0;
   s.valid = false;
   return s;
@@ -294,7 +322,7 @@ __device__ __forceinline__ SeqParams check_params(const KParams& P, SeqParams s)
 }
 
 __device__ __forceinline__ SeqParams load_params(const KParams& P, int b) {
-  return check_params(P, raw_params(P, b));
+  return check_params(P, raw_params(P, b, raw_mode(P, b)));
 }
 
 template <int DT>
@@ -1144,16 +1172,18 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const int cb = min(S, wv * per), ce = min(S, cb + per);
   constexpr int ES = Fmt<DT>::ES;
   const int row_bytes = P.V * ES;
-  // The first chunk's loads go out before the sequence's parameters have
-  // arrived (under a full stream their loads can take microseconds): its
-  // parameter loads are issued first, then the chunk's, and only K_b, when
-  // the call has a k_per_row array, is waited for (padding rows are never
-  // read: theirs read nothing, past the row's end).
-  const SeqParams raw = raw_params(P, b);
-  const bool used = tgt ? t <= raw.Kb : t < raw.Kb;
+  // The sequence's parameters come through the scalar cache, so that using
+  // them never waits for a chunk of logits in flight (under a full stream
+  // a vector load can take microseconds).  The first chunk's loads go out
+  // once K_b is known (padding rows are never read: theirs read nothing,
+  // past the row's end), before the other parameters are used.
   uint4 A[kLoads], B[kLoads];
   const __amdgpu_buffer_rsrc_t rs = row_resource(row, row_bytes);
   auto off = [&](int cc) { return cc < ce ? cc * P.L * ES : row_bytes; };
+  // (a per-sequence mode is one byte, loaded by the vector unit before the
+  // chunk, so that its wait does not include the chunk's)
+  const SeqParams raw = raw_params<!kAny>(P, b, raw_mode(P, b));
+  const bool used = tgt ? t <= raw.Kb : t < raw.Kb;
   if constexpr (VEC) issue_chunk<DT>(A, rs, used ? off(cb) : row_bytes, lane);
   const SeqParams sp = check_params(P, raw);
   if (!sp.valid) return;  // the sequence kernel reports the parameter error
@@ -1167,11 +1197,11 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const size_t rid = (size_t)b * R + r;
   const size_t slot0 = rid * S;
   const float c2 = (float)sp.c2;
-  const int tok = t < sp.Kb ? P.tokens[(size_t)b * P.K_max + t] : INT32_MIN;
-  const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
-  // the draft token's logit, used by the finish: loaded behind the first
-  // chunk, so that it arrives while the row streams
-  const float xtok = (tok_ok && threadIdx.x == 0) ? load_logit<DT>(row, tok) : 0.0f;
+  // The row's draft token: loaded here and first used after the stream,
+  // which also loads the token's logit.  (A load of the logit here would
+  // hold the stream until the token arrives, behind every row's first
+  // chunk.)
+  const int tok = t < sp.Kb ? uniform_load(P.tokens + (size_t)b * P.K_max + t) : INT32_MIN;
   if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
   lds_barrier();
 
@@ -1360,6 +1390,10 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     nc = compact_listed(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), lane);
     ucut = fmaxf(ucut, fcut);
   }
+  // the draft token's logit, for the finish; its load completes under the
+  // finish's first steps
+  const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
+  const float xtok = (tok_ok && threadIdx.x == 0) ? load_logit<DT>(row, tok) : 0.0f;
   {
     // the wave's record
     WaveRec wr;
@@ -1425,11 +1459,17 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
 
   double Z = 0.0;
   if (!(rr.flags & kErrBits) && (is_plain || is_topp)) {
+    // Z = sum_w z_w 2^(o_w - M c2): the offsets o_w are integers, so with
+    // F = floor(M c2) each 2^(o_w - F) is exact and one fp64 exp2 of
+    // F - M c2 (in (-1, 0]; M c2 is exact in fp64) scales the sum.
+    const double mc2 = (double)M * (double)c2;
+    const double F = floor(mc2);
 #pragma unroll
     for (int w = 0; w < kRowWaves; ++w) {
       const WaveRec& c = sm.wrec[w];
-      if (c.m > -kInf) Z += c.z * exp2((double)c.o - (double)M * (double)c2);
+      if (c.m > -kInf) Z += ldexp(c.z, (int)fmax((double)c.o - F, -2000.0));
     }
+    Z *= exp2(F - mc2);
     if (!(Z > 0.0) || !(Z < 1e300)) rr.flags |= SV_ST_NONFINITE;
     else if (chunk_sums) rr.flags |= kRfChunks;
   }
