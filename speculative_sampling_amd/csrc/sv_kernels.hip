@@ -709,13 +709,15 @@ struct SelOut {
   unsigned long long m_keep, m_above;
 };
 
-// One digit of a selection: scans the 256-bin histogram in ws from the top
-// digit down, with the counts and masses above it (above_c, above_m), for
-// the first digit whose inclusive cumulative count (top-k) or fixed-point
-// mass (nucleus) reaches `target`; without one (not reached), the lowest
-// non-empty digit.  Adds the exclusive sums at the digit to above_*, and
-// returns the digit with its own count and mass in last_*.
-__device__ __forceinline__ int pick_digit(const Hist& ws, bool by_mass, unsigned long long target,
+// One digit of a selection: scans the 256 digits from the top down, with
+// the counts and masses above them (above_c, above_m), for the first digit
+// whose inclusive cumulative count (top-k) or fixed-point mass (nucleus)
+// reaches `target`; without one (not reached), the lowest non-empty digit.
+// bin(dg, c, m) gives digit dg's count and mass.  Adds the exclusive sums
+// at the digit to above_*, and returns the digit with its own count and
+// mass in last_*.
+template <class Bin>
+__device__ __forceinline__ int pick_digit(Bin&& bin, bool by_mass, unsigned long long target,
                                           unsigned long long& above_c, unsigned long long& above_m,
                                           unsigned long long& last_c, unsigned long long& last_m, bool& reached,
                                           int lane) {
@@ -723,8 +725,7 @@ __device__ __forceinline__ int pick_digit(const Hist& ws, bool by_mass, unsigned
   unsigned long long c[4], m[4], lc = 0, lm = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    c[j] = ws.hc[255 - 4 * lane - j];
-    m[j] = ws.hm[255 - 4 * lane - j];
+    bin(255 - 4 * lane - j, c[j], m[j]);
     lc += c[j];
     lm += m[j];
   }
@@ -764,12 +765,24 @@ __device__ __forceinline__ int pick_digit(const Hist& ws, bool by_mass, unsigned
     ac = lane_at(yc, L);
     am = lane_at(ym, L);
   }
-  const int dg = 255 - 4 * L - J;
   above_c += ac;
   above_m += am;
-  last_c = ws.hc[dg];
-  last_m = ws.hm[dg];
-  return dg;
+  // the digit's own count and mass, from the lane holding it
+  last_c = lane_at(J == 0 ? c[0] : J == 1 ? c[1] : J == 2 ? c[2] : c[3], L);
+  last_m = lane_at(J == 0 ? m[0] : J == 1 ? m[1] : J == 2 ? m[2] : m[3], L);
+  return 255 - 4 * L - J;
+}
+// The same over a histogram's counts and masses.
+__device__ __forceinline__ int pick_digit_hist(const Hist& ws, bool by_mass, unsigned long long target,
+                                          unsigned long long& above_c, unsigned long long& above_m,
+                                          unsigned long long& last_c, unsigned long long& last_m, bool& reached,
+                                          int lane) {
+  return pick_digit(
+      [&](int dg, unsigned long long& c, unsigned long long& m) {
+        c = ws.hc[dg];
+        m = ws.hm[dg];
+      },
+      by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
 }
 
 __device__ __forceinline__ void clear_histogram(Hist& ws, int lane) {
@@ -805,7 +818,7 @@ __device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigne
       }
     });
     wave_sync();
-    const int dg = pick_digit(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+    const int dg = pick_digit_hist(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
     pkey |= (uint32_t)dg << shift;
     pmask |= 255u << shift;
     wave_sync();
@@ -822,7 +835,9 @@ __device__ __forceinline__ SelOut wave_select(Each&& each, bool by_mass, unsigne
 
 // Whether bf16 elements known to lie in [lo, hi] span fewer than 256
 // 16-bit keys: then one histogram level over the keys themselves gives the
-// selection (select_narrow).
+// selection: every digit is one bf16 value, so the histogram counts
+// elements only and each digit's mass is its count times the value's mass
+// (mass_of), the same integers as adding the elements' masses one by one.
 __device__ __forceinline__ bool narrow_range(float lo, float hi) {
   return lo <= hi && (fkey(hi) >> 16) - (fkey(lo) >> 16) < 256u;
 }
@@ -838,96 +853,6 @@ __device__ __forceinline__ unsigned long long mass_of(float x, float c2, float o
 __device__ __forceinline__ float bf16_of_key(uint32_t k16) {
   return key_value((k16 << 16) | ((k16 & 0x8000u) ? 0u : 0xFFFFu));
 }
-
-// The same selection as wave_select in one level, for bf16 elements in
-// [lo, hi] with narrow_range(lo, hi): digit 255 - (key(hi) - key).  Every
-// digit is one bf16 value, so the histogram counts elements only and each
-// digit's mass is its count times the value's mass (mass_of with c2, oM,
-// fM): the same integers as adding the elements' masses one by one.
-template <class Each>
-__device__ __forceinline__ SelOut select_narrow(Each&& each, bool by_mass, unsigned long long target, Hist& ws,
-                                                int lane, float hi, float c2, float oM, double fM) {
-  const uint32_t kb = (fkey(hi) >> 16) - 255u;  // the key of digit 0
-  unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
-  bool reached = true;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ws.hc[lane + kWave * j] = 0;
-  wave_sync();
-  each([&](float x, unsigned long long) {
-    const uint32_t dg = min(255u, (fkey(x) >> 16) - kb);  // the bound only guards the index
-    atomicAdd(&ws.hc[dg], 1u);
-  });
-  wave_sync();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int dg = lane + kWave * j;
-    const uint32_t c = ws.hc[dg];
-    ws.hm[dg] = c ? (unsigned long long)c * mass_of(bf16_of_key(kb + (uint32_t)dg), c2, oM, fM) : 0ull;
-  }
-  wave_sync();
-  const int dg = pick_digit(ws, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
-  wave_sync();
-  uint32_t pkey = (kb + (uint32_t)dg) << 16;
-  pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
-  SelOut r;
-  r.T = key_value(pkey);
-  r.reached = reached;
-  r.n_keep = (uint32_t)(above_c + last_c);
-  r.m_keep = above_m + last_m;
-  r.m_above = above_m;
-  return r;
-}
-
-// Selection over elements known to lie in [lo, hi].
-template <int DT, class Each>
-__device__ __forceinline__ SelOut select_bounded(Each&& each, bool by_mass, unsigned long long target,
-                                                 Hist& ws, int lane, float lo, float hi, float c2, float oM,
-                                                 double fM) {
-  if constexpr (DT == SV_BF16) {
-    if (narrow_range(lo, hi)) return select_narrow(each, by_mass, target, ws, lane, hi, c2, oM, fM);
-  }
-  return wave_select<DT>(each, by_mass, target, ws, lane);
-}
-
-// Appends the logits >= c of one vector per lane to (dx, di) at *n, in
-// (lane, element) order; entries beyond cap are counted but not stored.
-template <int DT>
-__device__ __forceinline__ void append_ge(bool have, const uint4& v, int e0, float c, int lane, float* dx, int* di,
-                                          int cap, int* n) {
-  constexpr int VE = Fmt<DT>::VE;
-  bool pass[VE];
-  int before = 0, total = 0;
-#pragma unroll
-  for (int k = 0; k < VE; ++k) {
-    pass[k] = have && elem<DT>(v, k) >= c;
-    const uint64_t bal = __ballot(pass[k]);
-    before += lanes_below(bal);  // passing logits of the lower lanes
-    total += __popcll(bal);
-  }
-  int pos = *n + before;
-#pragma unroll
-  for (int k = 0; k < VE; ++k) {
-    if (pass[k]) {
-      if (pos < cap) {
-        dx[pos] = elem<DT>(v, k);
-        di[pos] = e0 + k;
-      }
-      ++pos;
-    }
-  }
-  *n += total;
-}
-
-// ========================================================== row kernel ====
-//
-// One work-group of kRowWaves waves per logit row.  Wave w streams the w-th
-// quarter of the row's chunks, one chunk at a time into registers; the
-// candidate vectors of a top-k / nucleus kept set go to the wave's part of
-// an LDS buffer, so the buffer holds them in vocabulary order.  The waves
-// share their running maxima (nucleus) or cuts (top-k) through LDS without
-// waiting for each other: a value read early is only lower, which lists
-// more, never fewer, candidates.  After one barrier, wave 0 finishes the
-// row.
 
 template <bool B>
 struct BoolTag {
@@ -952,8 +877,6 @@ struct RowSmem {
   float ck[kRowWaves][kCandVecs];  // while listing: the largest logit of each vector (within 2^-8 / c2)
   WaveRec wrec[kRowWaves];         // each wave's record
   Hist h;
-  float kx[kListMax];              // the kept set in vocabulary order: logits
-  int ki[kListMax];                //   and vocabulary indices
   float pub[kRowWaves];            // each wave's running maximum (nucleus) or cut (top-k)
   float ucut[kRowWaves];           // the largest listing cut each wave used
   int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
@@ -1074,30 +997,37 @@ __device__ __forceinline__ float vector_max(const uint4& v) {
 
 // ---- the finish's selection, over the whole work-group ----
 //
-// The same selections as select_bounded, with the histogram filled by all
-// kThreads threads (one bin per thread to clear) and each digit picked by
-// wave 0 and passed to the others through LDS.  each(f, with_mass) calls
-// f(x, mass) for this thread's share of the elements (mass only when
-// with_mass is set).
+// The selection of wave_select over elements known to lie in [lo, hi],
+// with the histogram filled by all kThreads threads (one bin per thread to
+// clear) and each digit picked by wave 0 and passed to the others through
+// LDS.  bf16 elements spanning fewer than 256 values (narrow_range) take
+// one level whose digits are the values themselves: the histogram counts
+// them, and wave 0 takes each digit's mass from its count.  each(f,
+// with_mass) calls f(x, mass) for this thread's share of the elements
+// (mass only when with_mass is set).  clean: the counts are known to be 0.
 template <int DT, class Each>
 __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned long long target, RowSmem& sm,
                                             int tid, int wv, int lane, float lo, float hi, float c2, float oM,
-                                            double fM) {
+                                            double fM, bool clean) {
   static_assert(kThreads == 256, "one histogram bin per thread");
   unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
   bool reached = true;
   if (DT == SV_BF16 && narrow_range(lo, hi)) {
-    // one level: every digit is one bf16 value (see select_narrow)
-    const uint32_t kb = (fkey(hi) >> 16) - 255u;
-    sm.h.hc[tid] = 0;
-    lds_barrier();
+    const uint32_t kb = (fkey(hi) >> 16) - 255u;  // the key of digit 0
+    if (!clean) {
+      sm.h.hc[tid] = 0;
+      lds_barrier();
+    }
     each([&](float x, unsigned long long) { atomicAdd(&sm.h.hc[min(255u, (fkey(x) >> 16) - kb)], 1u); }, false);
     lds_barrier();
-    const uint32_t c = sm.h.hc[tid];
-    sm.h.hm[tid] = c ? (unsigned long long)c * mass_of(bf16_of_key(kb + (uint32_t)tid), c2, oM, fM) : 0ull;
-    lds_barrier();
     if (wv == 0) {
-      const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+      const int dg = pick_digit(
+          [&](int d, unsigned long long& c, unsigned long long& m) {
+            const uint32_t n = sm.h.hc[d];
+            c = n;
+            m = n ? (unsigned long long)n * mass_of(bf16_of_key(kb + (uint32_t)d), c2, oM, fM) : 0ull;
+          },
+          by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
       if (lane == 0) {
         uint32_t pkey = (kb + (uint32_t)dg) << 16;
         pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
@@ -1131,7 +1061,7 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
         true);
     lds_barrier();
     if (wv == 0) {
-      const int dg = pick_digit(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+      const int dg = pick_digit_hist(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
       if (lane == 0) sm.seldg = dg;
     }
     lds_barrier();
@@ -1325,28 +1255,31 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         // narrowing to 8, 6, 5, 4, 3, 2: everything at or above the
         // narrowest cut used stays listed.
         const double g = fmax(fmax((double)run, ma), (double)published_max(sm));
-        bool done = false;
         float cut = kInf;
-        for (int attempt = 0; attempt < 8 && !done; ++attempt) {
-          const double w = attempt <= 1 ? kCandLog2 : attempt == 2 ? 8.0 : (double)(9 - attempt);
-          // (keys are within 2^-8 / c2 of their vectors' maxima)
-          if (attempt >= 1) nc = compact_listed(sm, wv, nc, (float)(g - w * ic2 - 0.00390625 * ic2), ln);
+        const float o = ch.o;
+        auto list_window = [&](double w) {
           cut = (float)(g - w * ic2);
           // x >= cut implies a term >= 2^(cut c2 - o) up to roundings far below the margin
           // (the exponent is >= -10.01: o never exceeds g c2)
-          const float thr = __builtin_amdgcn_exp2f((float)((double)cut * (double)c2 - (double)ch.o) - 0.00390625f);
+          const float thr = __builtin_amdgcn_exp2f((float)((double)cut * (double)c2 - (double)o) - 0.00390625f);
           uint32_t mask = 0;
 #pragma unroll
           for (int i = 0; i < kLoads; ++i) mask |= emax[i] >= thr ? (1u << i) : 0u;
-          // the key: the vector's largest logit, from its largest term (fp32 suffices)
-          const float o = ch.o;
-          const int n = list_vectors(
+          // the key: the vector's largest logit, from its largest term (fp32
+          // suffices), taken only for the vectors listed
+          return list_vectors(
               sm, wv, nc, mask, [&](int i) { return (__builtin_amdgcn_logf(emax[i]) + o) * ic2f; }, buf, c0, VE, ln);
-          if (n <= kCandVecs) {
-            nc = n;
-            done = true;
-          }
+        };
+        int n = list_window(kCandLog2);
+        bool done = n <= kCandVecs;
+        for (int attempt = 1; attempt < 8 && !done; ++attempt) {
+          const double w = attempt == 1 ? kCandLog2 : attempt == 2 ? 8.0 : (double)(9 - attempt);
+          // (keys are within 2^-8 / c2 of their vectors' maxima)
+          nc = compact_listed(sm, wv, nc, (float)(g - w * ic2 - 0.00390625 * ic2), ln);
+          n = list_window(w);
+          done = n <= kCandVecs;
         }
+        if (done) nc = n;
         if (!done) over = true;
         ucut = fmaxf(ucut, cut);
         run = fmaxf(run, (float)ma);
@@ -1390,10 +1323,15 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     nc = compact_listed(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), lane);
     ucut = fmaxf(ucut, fcut);
   }
-  // the draft token's logit, for the finish; its load completes under the
+  // the draft token's logit, for the finish: its bits, loaded by every lane
+  // through the row's resource (an offset past the row reads 0), and
+  // decoded only where they are used, so that its load completes under the
   // finish's first steps
   const bool tok_ok = tok != INT32_MIN && tok >= 0 && tok < P.V;
-  const float xtok = (tok_ok && threadIdx.x == 0) ? load_logit<DT>(row, tok) : 0.0f;
+  const int xoff = tok_ok ? tok * ES : row_bytes;
+  uint32_t xbits;
+  if constexpr (DT == SV_BF16) xbits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, xoff, 0, 0);
+  else xbits = __builtin_amdgcn_raw_buffer_load_b32(rs, xoff, 0, 0);
   {
     // the wave's record
     WaveRec wr;
@@ -1428,6 +1366,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       sm.ucut[wv] = ucut;
     }
   }
+  sm.h.hc[threadIdx.x] = 0;  // the finish's first selection counts into these
   lds_barrier();
 
   // ---- finish ----
@@ -1445,12 +1384,23 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   rr.n_keep = -1;
   rr.flags = 0;
   rr.pad = 0;
+  // every record and list count read at once (LDS round trips in a row are
+  // the finish's latency)
+  WaveRec wrs[kRowWaves];
+  int ncw[kRowWaves];
+  float ucw[kRowWaves];
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    wrs[w] = sm.wrec[w];
+    ncw[w] = sm.ncand[w];
+    ucw[w] = sm.ucut[w];
+  }
   float mx = -kInf;
   uint32_t fl = 0;
 #pragma unroll
   for (int w = 0; w < kRowWaves; ++w) {
-    mx = fmaxf(mx, sm.wrec[w].m);
-    fl |= sm.wrec[w].flags;
+    mx = fmaxf(mx, wrs[w].m);
+    fl |= wrs[w].flags;
   }
   const float M = mx;
   rr.M = M;
@@ -1466,8 +1416,9 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     const double F = floor(mc2);
 #pragma unroll
     for (int w = 0; w < kRowWaves; ++w) {
-      const WaveRec& c = sm.wrec[w];
-      if (c.m > -kInf) Z += ldexp(c.z, (int)fmax((double)c.o - F, -2000.0));
+      // (a wave with no finite logit has z = 0 and o = -inf or 0)
+      const double zw = ldexp(wrs[w].z, (int)fmax((double)wrs[w].o - F, -2000.0));
+      Z += wrs[w].m > -kInf ? zw : 0.0;
     }
     Z *= exp2(F - mc2);
     if (!(Z > 0.0) || !(Z < 1e300)) rr.flags |= SV_ST_NONFINITE;
@@ -1483,13 +1434,14 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   int pre[kRowWaves + 1];
   float C = -kInf;  // every token >= C lies in a listed vector (+inf: incomplete)
   pre[0] = 0;
+  bool incomplete = false;
 #pragma unroll
   for (int w = 0; w < kRowWaves; ++w) {
-    const int n = sm.ncand[w];
-    if (n < 0) C = kInf;
-    else if (C < kInf) C = fmaxf(C, sm.ucut[w]);
-    pre[w + 1] = pre[w] + max(n, 0);
+    incomplete |= ncw[w] < 0;
+    C = fmaxf(C, ucw[w]);
+    pre[w + 1] = pre[w] + max(ncw[w], 0);
   }
+  if (incomplete) C = kInf;
   const int N = pre[kRowWaves];
   auto vec_at = [&](int j, uint4& v, int& e0) {
     const int w = (j >= pre[1]) + (j >= pre[2]) + (j >= pre[3]);
@@ -1504,7 +1456,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       int best = 0x7fffffff;
 #pragma unroll
       for (int w = 0; w < kRowWaves; ++w)
-        if (sm.wrec[w].m == M) best = min(best, sm.wrec[w].arg);
+        if (wrs[w].m == M) best = min(best, wrs[w].arg);
       rr.g = best;
       rr.T = M;
       rr.n_keep = 1;
@@ -1527,6 +1479,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       // candidates: every vector holds its own maximum, so the k-th largest
       // logit is at least that key.
       const bool narrow = DT == SV_BF16 && C < kInf && narrow_range(fmaxf(C, -kMaxFinite), Mhi);
+      bool hist_clean = true;  // the counts were cleared before the finish
       float C1 = (by_mass && !narrow) ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
       if (!by_mass && !narrow && C < kInf) {
         const SelOut sk = wg_select<DT>(
@@ -1539,7 +1492,8 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
                 if (vm >= C) f(vm, 0ull);
               }
             },
-            false, target, sm, tid, wv, lane, C, Mhi, c2, oM, fM);
+            false, target, sm, tid, wv, lane, C, Mhi, c2, oM, fM, hist_clean);
+        hist_clean = false;
         if (sk.reached) C1 = fmaxf(C, sk.T);
       }
       SelOut so;
@@ -1561,7 +1515,8 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
                 }
               }
             },
-            by_mass, target, sm, tid, wv, lane, Cuf, Mhi, c2, oM, fM);
+            by_mass, target, sm, tid, wv, lane, Cuf, Mhi, c2, oM, fM, hist_clean);
+        hist_clean = false;
         ok = so.reached && so.T >= Cu;
       }
       if (!ok) {
@@ -1591,8 +1546,9 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
 
   if (list_ok) {
     // the kept set, in vocabulary order: the candidates >= T, compacted in
-    // buffer order by the work-group, then written out
+    // buffer order by the work-group and stored as they are placed
     rr.flags |= kRfListOk;
+    KeptEntry* kl = P.kept + ((size_t)b * (P.K_max + 1) + t) * (size_t)min(kListMax, P.V);
     int nk = 0;
     constexpr int kRounds = kRowWaves * kCandVecs / kThreads;
 #pragma unroll
@@ -1621,26 +1577,21 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         off += w < wv ? sw : 0;
         tot += sw;
       }
+      // (n_keep <= kListMax, and every kept token is one of these)
 #pragma unroll
       for (int k = 0; k < VE; ++k) {
         if (pass[k]) {
           if (off < kListMax) {
-            sm.kx[off] = elem<DT>(v, k);
-            sm.ki[off] = e0 + k;
+            KeptEntry ke;
+            ke.idx = e0 + k;
+            ke.xq = elem<DT>(v, k);
+            kl[off] = ke;
           }
           ++off;
         }
       }
       nk += tot;
-      lds_barrier();
-    }
-    nk = min(nk, kListMax);
-    KeptEntry* kl = P.kept + ((size_t)b * (P.K_max + 1) + t) * (size_t)min(kListMax, P.V);
-    for (int j = tid; j < nk; j += kThreads) {
-      KeptEntry ke;
-      ke.idx = sm.ki[j];
-      ke.xq = sm.kx[j];
-      kl[j] = ke;
+      if (j0 + kThreads < N) lds_barrier();  // the next round writes wsum again
     }
   }
 
@@ -1650,7 +1601,10 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         rr.flags |= SV_ST_TOKEN;
       } else if (!(rr.flags & kErrBits)) {
         if (is_greedy) rr.pid = tok == rr.g ? 1.0 : 0.0;
-        else rr.pid = xtok >= rr.T ? exp2(((double)xtok - (double)M) * (double)c2) / rr.Zs : 0.0;
+        else {
+          const float xtok = __uint_as_float(DT == SV_BF16 ? xbits << 16 : xbits);
+          rr.pid = xtok >= rr.T ? exp2(((double)xtok - (double)M) * (double)c2) / rr.Zs : 0.0;
+        }
       }
     }
     P.rows[rid] = rr;
