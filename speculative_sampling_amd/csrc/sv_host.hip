@@ -50,8 +50,8 @@ int fail(int code, const std::string& msg) {
 }
 
 struct Geometry {
-  int S, L, R_max;
-  size_t off_chunks, off_rows, off_kept, total;
+  int S, L, R_max, D;
+  size_t off_chunks, off_rows, off_kept, off_dsums, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -83,6 +83,9 @@ Geometry geometry(const sv_config* cfg) {
   off = align_up(off + rows * sizeof(sv::RowRec), 256);
   g.off_kept = off;
   off = align_up(off + target_rows * std::min(sv::kListMax, V) * sizeof(sv::KeptEntry), 256);
+  g.D = (V + sv::kDrawSpan - 1) / sv::kDrawSpan;
+  g.off_dsums = off;
+  off = align_up(off + (size_t)cfg->max_batch * g.D * sizeof(sv::DrawSum), 256);
   g.total = off;
   return g;
 }
@@ -204,6 +207,17 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.chunks = reinterpret_cast<sv::ChunkRec*>(base + g.off_chunks);
   p.rows = reinterpret_cast<sv::RowRec*>(base + g.off_rows);
   p.kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
+  p.dsums = reinterpret_cast<sv::DrawSum*>(base + g.off_dsums);
+  p.D = g.D;
+  // Residual draws from the rows are spread over the chip when the call
+  // may hold plain rows (their first rejection always needs the rows);
+  // other calls draw the rare ones in the sequence kernel.
+  // (only where the sequence kernel alone would leave most CUs idle: fewer
+  // sequences than CUs, rows of at least 8 spans)
+  p.spread = (a->K_max > 0 && p.draft != nullptr && (a->mode != nullptr || a->default_mode == SV_PLAIN) &&
+              a->B <= 256 && g.D >= 8)
+                 ? 1
+                 : 0;
   return p;
 }
 
@@ -218,7 +232,10 @@ bool vector_loads(const sv_config& cfg, const sv_args* a) {
 // kMaxRowsPerLaunch rows; prof (or NULL) receives the stage events of the
 // first launch.
 hipError_t launch_call(sv::KParams p, int dtype, bool vec, hipStream_t s, hipEvent_t* prof) {
-  const int seq_per_launch = (int)std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxRowsPerLaunch / p.R));
+  size_t per = std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxRowsPerLaunch / p.R));
+  // the draw-sum grid, nseq x D work-groups of kThreads, stays below 2^32 work-items
+  if (p.spread) per = std::min(per, std::max<size_t>(1, kMaxRowsPerLaunch / (size_t)p.D));
+  const int seq_per_launch = (int)per;
   hipError_t e = hipSuccess;
   for (int b0 = 0; b0 < p.B && e == hipSuccess; b0 += seq_per_launch) {
     p.b_base = b0;

@@ -13,8 +13,8 @@ namespace sv {
 constexpr int kRowWaves = 4;
 constexpr int kThreads = 64 * kRowWaves;
 // Each wave streams its share of a row in chunks: every lane keeps kLoads
-// 16-byte vectors of a chunk in registers (64 VGPRs), 128 bf16 or 64 fp32
-// logits, so a chunk holds 8192 bf16 / 4096 fp32 logits.
+// 16-byte vectors of a chunk in registers (32 VGPRs), 64 bf16 or 32 fp32
+// logits, so a chunk (8 KB) holds 4096 bf16 / 2048 fp32 logits.
 constexpr int kLoads = 8;
 // Candidate vectors (the 16-byte logit vectors that may hold a token of a
 // top-k / nucleus kept set) one wave can keep in LDS for its share of a row.
@@ -22,8 +22,10 @@ constexpr int kCandVecs = 256;
 // Largest kept set of a target row that is written out as a list, so that
 // the final draw needs no second read of the logit rows.
 constexpr int kListMax = 512;
-// Waves of the per-sequence kernel (accept walk and final draw).
+// Waves of the per-sequence kernel (accept walk and final draw) for calls
+// of fewer than kSmallSeqWgMin sequences; 4 waves for larger calls.
 constexpr int kSeqWaves = 8;
+constexpr int kSmallSeqWgMin = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxVocab = 1 << 22;
 
@@ -63,6 +65,20 @@ struct KeptEntry {
   float xq;
 };
 
+// Residual draws spread over the chip: a sequence whose first rejection n
+// (< K_b) needs the rows themselves (plain rows, a kept set not listed)
+// draws from (q_n - p_n)+ in vocabulary order.  Before the sequence
+// kernel, one work-group per kDrawSpan tokens of each sequence repeats the
+// accept walk and, for such a sequence, sums its span's weights into a
+// DrawSum; the sequence kernel then locates the span holding the target
+// and draws in it.
+constexpr int kDrawSpan = 8192;
+struct DrawSum {
+  double s;       // sum of the span's weights, fp32 groups of 8 added in fp64
+  int32_t first;  // first token of the span's first group of 8 with weight (INT32_MAX: none)
+  int32_t last;   // last token of its last group of 8 with weight (-1: none)
+};
+
 struct KParams {
   int32_t B, K_max, V, R, S, L;
   int32_t b_base, b_end;  // sequences [b_base, b_end) of this launch
@@ -87,6 +103,9 @@ struct KParams {
   ChunkRec* chunks;  // [B][R][S]  (plain target rows)
   RowRec* rows;      // [B][R]
   KeptEntry* kept;   // [B][K_max + 1][min(kListMax, V)]  (target rows)
+  DrawSum* dsums;    // [B][D]  (spread draws)
+  int32_t D;         // spans of kDrawSpan tokens per row
+  int32_t spread;    // residual draws from the rows go to the draw kernels
 };
 
 // Enqueues the kernels of one call for sequences

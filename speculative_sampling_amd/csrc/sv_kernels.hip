@@ -268,7 +268,8 @@ __device__ __forceinline__ int raw_mode(const KParams& P, int b) {
 // A load whose address is the same for the whole wave, through the scalar
 // cache: its wait (lgkmcnt) is apart from that of the vector loads in
 // flight, so it never waits for a chunk of logits issued before it.  Only
-// for 4-byte values that no kernel of the call writes.
+// for 4-byte values that the same kernel does not write (the scalar cache
+// is invalidated when a kernel starts, not while it runs).
 template <class T>
 __device__ __forceinline__ T uniform_load(const T* p) {
   static_assert(sizeof(T) == 4, "scalar loads of 4-byte values");
@@ -1619,20 +1620,21 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
 // set; a draw that needs the full rows (plain rows, large kept sets) is
 // done by the whole work-group.
 
-constexpr int kSeqThreads = kSeqWaves * kWave;
+constexpr int kSeqThreads = kSeqWaves * kWave;  // (the work-group of small batches)
 constexpr int kDrawTiles = 4;   // tiles of a row draw whose loads are in flight together
 constexpr int kTileCap = 384;   // tile sums per wave of a row draw held in LDS
 constexpr int kMaxRows = 2 * kMaxK + 1;
 
+template <int NW>
 struct SmemSeq {
   RowRec rows[kMaxRows];
-  double rd[kSeqWaves];
-  int ri[kSeqWaves];
+  double rd[NW];
+  int ri[NW];
   uint32_t misc[4];
   double rx[2];
   double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
   double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
-  double tsum[kSeqWaves][kTileCap];
+  double tsum[NW][kTileCap];
 };
 
 // ------------------------------------------------------------- draws ----
@@ -1642,28 +1644,31 @@ struct Draw {
   uint32_t flags;
 };
 
-__device__ __forceinline__ int seq_min_i(int v, SmemSeq& sm) {
+template <int NW>
+__device__ __forceinline__ int seq_min_i(int v, SmemSeq<NW>& sm) {
   v = wave_min_i(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.ri[threadIdx.x >> 6] = v;
   __syncthreads();
   int s = sm.ri[0];
 #pragma unroll
-  for (int w = 1; w < kSeqWaves; ++w) s = min(s, sm.ri[w]);
+  for (int w = 1; w < NW; ++w) s = min(s, sm.ri[w]);
   return s;
 }
-__device__ __forceinline__ int seq_max_i(int v, SmemSeq& sm) {
+template <int NW>
+__device__ __forceinline__ int seq_max_i(int v, SmemSeq<NW>& sm) {
   v = wave_max_i(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.ri[threadIdx.x >> 6] = v;
   __syncthreads();
   int s = sm.ri[0];
 #pragma unroll
-  for (int w = 1; w < kSeqWaves; ++w) s = max(s, sm.ri[w]);
+  for (int w = 1; w < NW; ++w) s = max(s, sm.ri[w]);
   return s;
 }
 // Exclusive prefix over the work-group in thread order; *total = the sum.
-__device__ __forceinline__ double seq_exclusive_scan(double v, double* total, SmemSeq& sm) {
+template <int NW>
+__device__ __forceinline__ double seq_exclusive_scan(double v, double* total, SmemSeq<NW>& sm) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const double inc = wave_incl_scan(v, lane);
   __syncthreads();
@@ -1671,7 +1676,7 @@ __device__ __forceinline__ double seq_exclusive_scan(double v, double* total, Sm
   __syncthreads();
   double base = 0.0, tot = 0.0;
 #pragma unroll
-  for (int j = 0; j < kSeqWaves; ++j) {
+  for (int j = 0; j < NW; ++j) {
     base += j < w ? sm.rd[j] : 0.0;
     tot += sm.rd[j];
   }
@@ -1865,9 +1870,9 @@ __device__ __forceinline__ float weights8(const RowW& wq, bool use_p, const RowW
 // that the chunk records place the target in) is split into one segment
 // per wave; pass 1 sums the weights of each 512-token tile into LDS, pass 2
 // scans the one tile that holds the target.
-template <int DT, bool VEC>
+template <int DT, bool VEC, int NW>
 __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
-                                               const char* qrow, const char* prow, double u, SmemSeq& sm, int lane,
+                                               const char* qrow, const char* prow, double u, SmemSeq<NW>& sm, int lane,
                                                int wv, const ChunkRec* qrec) {
   const int tid = threadIdx.x;
   Draw d;
@@ -1883,7 +1888,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     // plain bonus draw: the chunk sums give the chunk holding u
     const int S = P.S;
     // kCpt consecutive chunks per thread cover every row (V <= 2^22)
-    constexpr int kCpt = (kMaxVocab / (kWave * kLoads * 4) + kSeqThreads - 1) / kSeqThreads;
+    constexpr int kCpt = (kMaxVocab / (kWave * kLoads * 4) + NW * kWave - 1) / (NW * kWave);
     double wc[kCpt];
     double wsum = 0.0;
 #pragma unroll
@@ -1933,7 +1938,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   int nzlo = 0x7fffffff, nzhi = -1, per = 0, v0 = 0, v1 = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int n8 = (hi - lo + 7) / 8;
-    per = (n8 + kSeqWaves - 1) / kSeqWaves;
+    per = (n8 + NW - 1) / NW;
     v0 = min(n8, wv * per);
     v1 = min(n8, v0 + per);
     double seg = 0.0;
@@ -1984,7 +1989,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     S = 0.0;
     nzlo = 0x7fffffff;
 #pragma unroll
-    for (int w = 0; w < kSeqWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       S += sm.rd[w];
       nzlo = min(nzlo, sm.ri[w]);
     }
@@ -1993,7 +1998,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
     __syncthreads();
     nzhi = -1;
 #pragma unroll
-    for (int w = 0; w < kSeqWaves; ++w) nzhi = max(nzhi, sm.ri[w]);
+    for (int w = 0; w < NW; ++w) nzhi = max(nzhi, sm.ri[w]);
     if (!(S > 0.0) && use_p) {
       d.flags |= SV_ST_ZERO_RESIDUAL;  // (q - p)+ has no mass: draw from q
       use_p = false;
@@ -2009,7 +2014,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   double before = 0.0;
   {
     double c = 0.0;
-    for (int w = 0; w < kSeqWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const double sw = sm.rd[w];
       if (ws_ < 0 && sw > 0.0 && c + sw > target) {
         ws_ = w;
@@ -2113,6 +2118,229 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
   return d;
 }
 
+// ======================================================= spread draws ====
+//
+// A residual draw from the rows (n < K_b, plain rows or a kept set not
+// listed): inverse CDF over (q_n - p_n)+ in vocabulary order.  Before the
+// sequence kernel, one work-group per kDrawSpan tokens of each sequence
+// repeats the accept walk (the same uniforms and tests, so the same n) and,
+// when the sequence needs such a draw, sums its span's weights; the
+// sequence kernel scans the span sums, finds the span holding u * S and
+// the token in it.  Both use the weights of weights8 (fp32, in groups of 8
+// added pairwise), so the span the sums locate holds the crossing of the
+// group-level running sum.
+
+static_assert(kMaxVocab / kDrawSpan <= kSeqThreads, "one span sum per thread of the sequence's work-group");
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void draw_sum_kernel(const KParams P) {
+  __shared__ double red[kRowWaves];
+  __shared__ int rlo[kRowWaves], rhi[kRowWaves];
+  __shared__ int sh_n;
+  const int D = P.D;
+  const int b = P.b_base + (int)(blockIdx.x / (uint32_t)D);
+  const int sp_ = (int)(blockIdx.x % (uint32_t)D);
+  const int tid = (int)threadIdx.x, lane = (int)__lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid || sp.mode == SV_GREEDY) return;  // (whole work-group)
+  const int Kb = sp.Kb, KM = P.K_max, R = P.R;
+  if (wv == 0) {
+    // the walk of the sequence kernel: error rows, then the first t with
+    // u_t p_t(d_t) >= q_t(d_t) (K_b <= 64: one lane per position)
+    const RowRec* rows = P.rows + (size_t)b * R;
+    uint32_t st = 0;
+    for (int t = lane; t <= Kb; t += kWave) st |= rows[t].flags;
+    for (int t = lane; t < Kb; t += kWave) st |= rows[KM + 1 + t].flags;
+    st = wave_or_u(st);
+    bool rej = false;
+    if (lane < Kb) {
+      const uint64_t g = P.row_offset + (uint64_t)b;
+      const double ua = uniform24(P.seed, g, (uint32_t)lane, kPurposeAccept);
+      rej = !(ua * rows[KM + 1 + lane].pid < rows[lane].pid);
+    }
+    const uint64_t rb = __ballot(rej);
+    const int n = rb ? __ffsll((long long)rb) - 1 : Kb;
+    const bool need = !(st & kErrBits) && n < Kb && !(rows[n].flags & kRfListOk);
+    if (lane == 0) sh_n = need ? n : -1;
+  }
+  __syncthreads();
+  const int n = sh_n;
+  if (n < 0) return;
+  const RowRec rq = P.rows[(size_t)b * R + n], rp = P.rows[(size_t)b * R + KM + 1 + n];
+  const RowW wq = row_w(rq), wp = row_w(rp);
+  const bool all = __builtin_amdgcn_readfirstlane((int)(wq.T == -kInf && wp.T == -kInf)) != 0;
+  const char* qrow = static_cast<const char*>(row_ptr<DT>(P, b, true, n));
+  const char* prow = static_cast<const char*>(row_ptr<DT>(P, b, false, n));
+  const int lo = sp_ * kDrawSpan, hi = min(P.V, lo + kDrawSpan);
+  // thread t takes groups t, t + 256, t + 512, t + 768 of the span (all
+  // loads in flight together)
+  constexpr int kG = kDrawSpan / 8 / kThreads;
+  uint4 aq[kG][2], ap[kG][2];
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const int e = lo + 8 * (tid + kThreads * k);
+    const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+    aq[k][0] = aq[k][1] = ap[k][0] = ap[k][1] = make_uint4(ninf, ninf, ninf, ninf);
+    if (e < hi) {
+      load8<DT, VEC>(P, qrow, e, aq[k]);
+      load8<DT, VEC>(P, prow, e, ap[k]);
+    }
+  }
+  double s = 0.0;
+  int zl = 0x7fffffff, zh = -1;
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const int e = lo + 8 * (tid + kThreads * k);
+    float w[8];
+    const float s8 = weights8<DT>(wq, true, wp, all, aq[k], ap[k], w);
+    s += (double)s8;
+    if (s8 > 0.0f) {
+      zl = min(zl, e);
+      zh = max(zh, e + 7);
+    }
+  }
+  s = wave_sum(s);
+  zl = wave_min_i(zl);
+  zh = wave_max_i(zh);
+  if (lane == 0) {
+    red[wv] = s;
+    rlo[wv] = zl;
+    rhi[wv] = zh;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    DrawSum ds;
+    ds.s = (red[0] + red[1]) + (red[2] + red[3]);
+    ds.first = min(min(rlo[0], rlo[1]), min(rlo[2], rlo[3]));
+    ds.last = max(max(rhi[0], rhi[1]), max(rhi[2], rhi[3]));
+    P.dsums[(size_t)b * D + sp_] = ds;
+  }
+}
+
+// Inverse CDF inside the span [lo, hi) (at most kDrawSpan tokens): thread
+// t holds groups 2t and 2t + 1, the work-group's running sum of the group
+// sums (from `base`, the weight before lo) finds the group crossing
+// `target` (+inf: none), then the token in it.  Without a crossing (the
+// target beyond the rounded total) the last token with weight is taken.
+// S: the row's total weight, for the CDF margins against u.
+template <int DT, bool VEC>
+__device__ __forceinline__ Draw draw_in_span(const KParams& P, const RowW& wq, const RowW& wp, bool all,
+                                             const char* qrow, const char* prow, int lo, int hi, double base,
+                                             double target, double S, int nzlo, int nzhi, double u,
+                                             SmemSeq<kSeqWaves>& sm) {
+  static_assert(kDrawSpan == 16 * kSeqThreads, "two groups of 8 per thread");
+  const int tid = threadIdx.x;
+  uint4 aq[2][2], ap[2][2];
+  float w[2][8], s8[2];
+  int e[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    e[h] = lo + 8 * (2 * tid + h);
+    const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+    aq[h][0] = aq[h][1] = ap[h][0] = ap[h][1] = make_uint4(ninf, ninf, ninf, ninf);
+    if (e[h] < hi) {
+      load8<DT, VEC>(P, qrow, e[h], aq[h]);
+      load8<DT, VEC>(P, prow, e[h], ap[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) s8[h] = weights8<DT>(wq, true, wp, all, aq[h], ap[h], w[h]);
+  double tot;
+  const double ex = seq_exclusive_scan((double)s8[0] + (double)s8[1], &tot, sm);
+  const double c0 = base + ex, c1 = c0 + (double)s8[0];
+  // the group crossing the target, and the last group with weight
+  const int h = (s8[0] > 0.0f && c0 + (double)s8[0] > target) ? 0
+                : (s8[1] > 0.0f && c1 + (double)s8[1] > target) ? 1
+                                                                  : -1;
+  const int gx = seq_min_i(h >= 0 ? 2 * tid + h : 0x7fffffff, sm);
+  const int gl = seq_max_i(s8[1] > 0.0f ? 2 * tid + 1 : s8[0] > 0.0f ? 2 * tid : -1, sm);
+  Draw d;
+  d.flags = 0;
+  d.y = 0;
+  const int g = gx != 0x7fffffff ? gx : gl;
+  if (g >= 0 && tid == g / 2) {
+    int y = -1, ylast = -1;
+    double cl = 0.0, ch = 0.0, ll = 0.0, lh = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh != (g & 1)) continue;  // (static indices into w and e)
+      double r = hh ? c1 : c0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wk = w[hh][k];
+        const double rn = r + (double)wk;
+        if (wk > 0.0f) {
+          if (y < 0 && gx != 0x7fffffff && rn > target) {
+            y = e[hh] + k;
+            cl = r;
+            ch = rn;
+          }
+          ylast = e[hh] + k;
+          ll = r;
+          lh = rn;
+        }
+        r = rn;
+      }
+    }
+    if (y < 0) {  // rounding inside the group, or no crossing at all
+      y = ylast;
+      cl = gx != 0x7fffffff ? ll : S;
+      ch = gx != 0x7fffffff ? lh : S;
+    }
+    sm.misc[3] = (uint32_t)y;
+    sm.rx[0] = cl;
+    sm.rx[1] = ch;
+  }
+  __syncthreads();
+  if (g >= 0) {
+    d.y = (int)sm.misc[3];
+    const double plo = sm.rx[0] / S, phi = sm.rx[1] / S;
+    if (nzlo < d.y && u - plo < kWindow) d.flags |= SV_ST_MARGIN;
+    if (nzhi > d.y && phi - u < kWindow) d.flags |= SV_ST_MARGIN;
+  }
+  return d;
+}
+
+// The residual draw of sequence b at its first rejection n from the span
+// sums draw_sum_kernel made (whole work-group).  Without residual mass it
+// is the rows' own draw, which falls back to q.
+template <int DT, bool VEC>
+__device__ __forceinline__ Draw draw_spread(const KParams& P, int b, int n, const RowRec& rq, const RowRec& rp,
+                                            double u, SmemSeq<kSeqWaves>& sm, int lane, int wv) {
+  const int tid = threadIdx.x, D = P.D;
+  const RowW wq = row_w(rq), wp = row_w(rp);
+  const bool all = __builtin_amdgcn_readfirstlane((int)(wq.T == -kInf && wp.T == -kInf)) != 0;
+  const char* qrow = static_cast<const char*>(row_ptr<DT>(P, b, true, n));
+  const char* prow = static_cast<const char*>(row_ptr<DT>(P, b, false, n));
+  DrawSum ds;
+  ds.s = 0.0;
+  ds.first = 0x7fffffff;
+  ds.last = -1;
+  if (tid < D) ds = P.dsums[(size_t)b * D + tid];
+  double S;
+  const double ex = seq_exclusive_scan(ds.s, &S, sm);
+  const int nzlo = seq_min_i(ds.first, sm), nzhi = seq_max_i(ds.last, sm);
+  if (!(S > 0.0)) {
+    __syncthreads();
+    return draw_from_rows<DT, VEC, kSeqWaves>(P, rq, true, rp, qrow, prow, u, sm, lane, wv, nullptr);
+  }
+  const double target = u * S;
+  const int cs = seq_min_i((tid < D && ds.s > 0.0 && ex + ds.s > target) ? tid : 0x7fffffff, sm);
+  const int cl = seq_max_i((tid < D && ds.s > 0.0) ? tid : -1, sm);
+  const bool beyond = cs == 0x7fffffff;  // u * S beyond the rounded total: the last token with weight
+  const int c = beyond ? cl : cs;
+  __syncthreads();
+  if (tid == c) sm.rd[0] = ex;
+  __syncthreads();
+  const double base = sm.rd[0];
+  __syncthreads();
+  Draw d = draw_in_span<DT, VEC>(P, wq, wp, all, qrow, prow, c * kDrawSpan, min(P.V, (c + 1) * kDrawSpan), base,
+                                 beyond ? kInf : target, S, nzlo, nzhi, u, sm);
+  d.flags |= SV_ST_REREAD;
+  return d;
+}
+
 // An error row: accepted = -1, every token -1, diagnostics NaN (threads
 // first, first + stride, ... of the caller's group).
 __device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st, int first, int stride) {
@@ -2143,15 +2371,19 @@ __device__ __forceinline__ void write_tokens(const KParams& P, int b, int n, int
 }
 
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
-  __shared__ SmemSeq sm;
+// NW waves per work-group: kSeqWaves for small batches (a sequence's draw
+// from the rows then has the most waves), 4 for large ones (more sequences
+// resident per CU).
+template <int DT, bool VEC, int NW>
+__global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
+  constexpr int NT = NW * kWave;
+  __shared__ SmemSeq<NW> sm;
   const int tid = threadIdx.x, lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int b = P.b_base + (int)blockIdx.x;
   const SeqParams sp = load_params(P, b);
   if (!sp.valid) {
-    write_error(P, b, SV_ST_PARAM, tid, kSeqThreads);
+    write_error(P, b, SV_ST_PARAM, tid, NT);
     return;
   }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
@@ -2160,14 +2392,14 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   // greedy calls may come without draft logits: the rule then needs only
   // the target's argmax (the draft rows' records are not made)
   const bool have_draft = P.draft != nullptr;
-  for (int r = tid; r < R; r += kSeqThreads) {
+  for (int r = tid; r < R; r += NT) {
     const bool used = r <= KM ? r <= Kb : (r - KM - 1 < Kb && have_draft);
     if (used) sm.rows[r] = P.rows[(size_t)b * R + r];
   }
   // The walk's uniforms depend only on seed, sequence, position and
   // purpose: the last wave draws those of positions 0..63 while the records
   // load.  Greedy rows use none (u p < q with p, q in {0, 1} holds iff q = 1).
-  if (!greedy && wv == kSeqWaves - 1) {
+  if (!greedy && wv == NW - 1) {
     const int t = lane;
     if (t < Kb) sm.ua[t] = uniform24(P.seed, g, (uint32_t)t, kPurposeAccept);
     if (t <= Kb) sm.ud[t] = uniform24(P.seed, g, (uint32_t)t, t < Kb ? kPurposeResample : kPurposeBonus);
@@ -2267,10 +2499,17 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const KParams P) {
   const RowRec rq = sm.rows[n];
   const RowRec rp = resample ? sm.rows[KM + 1 + n] : rq;
   __syncthreads();  // sm.misc / sm.rx are reused by the draw
-  const Draw d = draw_from_rows<DT, VEC>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
-                                         resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr,
-                                         u, sm, lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
-  write_tokens(P, b, n, d.y, st | d.flags, tid, kSeqThreads);
+  // a residual draw with the span sums made before this kernel, or the
+  // work-group's own pass over the rows
+  Draw d;
+  if constexpr (NW == kSeqWaves) {
+    if (P.spread && resample) d = draw_spread<DT, VEC>(P, b, n, rq, rp, u, sm, lane, wv);
+  }
+  if (!(NW == kSeqWaves && P.spread && resample))
+    d = draw_from_rows<DT, VEC, NW>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
+                                    resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr, u,
+                                    sm, lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
+  write_tokens(P, b, n, d.y, st | d.flags, tid, NT);
 }
 
 // start / stop: events recorded on the kernel's own dispatch (NULL: none).
@@ -2292,8 +2531,21 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
   // path when the call gives a mode per sequence
   const dim3 grid((unsigned)((size_t)nseq * p.R));
   launch_rows<DT, VEC>(p, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
-  hipExtLaunchKernelGGL((seq_kernel<DT, VEC>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream,
-                        ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, p);
+  hipEvent_t seq_start = ev ? ev[2] : nullptr;
+  if (p.spread) {
+    // the span sums of the residual draws over the whole chip, then the
+    // walk and draws
+    hipExtLaunchKernelGGL((draw_sum_kernel<DT, VEC>), dim3((unsigned)((size_t)nseq * p.D)), dim3(kThreads), 0,
+                          stream, seq_start, nullptr, 0, p);
+    seq_start = nullptr;
+  }
+  // several sequences per CU: smaller work-groups, more of them resident
+  if (nseq >= kSmallSeqWgMin)
+    hipExtLaunchKernelGGL((seq_kernel<DT, VEC, 4>), dim3((unsigned)nseq), dim3(4 * kWave), 0, stream, seq_start,
+                          ev ? ev[3] : nullptr, 0, p);
+  else
+    hipExtLaunchKernelGGL((seq_kernel<DT, VEC, kSeqWaves>), dim3((unsigned)nseq), dim3(kSeqThreads), 0, stream,
+                          seq_start, ev ? ev[3] : nullptr, 0, p);
   return hipSuccess;
 }
 

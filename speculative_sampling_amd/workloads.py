@@ -224,6 +224,10 @@ def config(name: str, device="cpu", **kw) -> Workload:
                           device=device, **kw)
     if name == "nucleus_b64":
         return peaked(64, 4, 128256, device=device, **kw)
+    if name in ("plain_b64", "topk50_b64", "greedy_b64"):
+        # the nucleus workload's shape and logits with another filter
+        mode = {"plain_b64": PLAIN, "topk50_b64": TOPK, "greedy_b64": GREEDY}[name]
+        return peaked(64, 4, 128256, mode=mode, top_k=50, device=device, **kw)
     if name.startswith("topk_f32"):
         sigma = float(name.split("_s")[-1]) if "_s" in name else 1.0
         greedy = "greedy" in name
