@@ -131,7 +131,11 @@ typedef struct {
  * B * (K_max + 1) * vocab elements and draft_logits B * K_max * vocab
  * elements of the handle's dtype (vocab is the row stride), and the index
  * arrays the sizes above.  A shorter buffer is read out of bounds; nothing
- * on the device can detect it. */
+ * on the device can detect it.
+ * Rows longer than 4096 bf16 / 2048 fp32 logits must be whole 16-byte
+ * vectors: vocab * element size a multiple of 16 and both logit buffers
+ * 16-byte aligned; otherwise validation returns SV_EINVAL (shorter rows
+ * may be unaligned). */
 typedef struct {
   int32_t B;
   int32_t K_max;

@@ -92,6 +92,13 @@ Geometry geometry(const sv_config* cfg) {
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
+// 16-byte vector loads need every row start on a 16-byte boundary.
+bool vector_loads(const sv_config& cfg, const sv_args* a) {
+  const int es = cfg.dtype == SV_BF16 ? 2 : 4;
+  return ((size_t)cfg.vocab * es) % 16 == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
+         (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);  // NULL is aligned
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +126,13 @@ int spec_verify_validate(const sv_config* cfg, const sv_args* a) {
   if (a->K_max > 0 && !a->draft_logits && (a->mode || a->default_mode != SV_GREEDY))
     return fail(SV_EINVAL, "draft_logits is required when K_max > 0 (unless every row is greedy)");
   if (!a->accepted || !a->out_tokens) return fail(SV_EINVAL, "accepted and out_tokens are required");
+  // Rows that are not whole 16-byte vectors (V * element size not a
+  // multiple of 16, or a logit buffer not 16-byte aligned) are streamed
+  // element by element, which is supported for rows of one chunk only.
+  if (!vector_loads(*cfg, a) && cfg->vocab > sv::chunk_capacity(cfg->dtype))
+    return fail(SV_EINVAL,
+                "rows that are not whole 16-byte vectors (V * element size a multiple of 16, logit buffers "
+                "16-byte aligned) are supported only up to 4096 bf16 / 2048 fp32 logits");
   // Defaults are checked only where some row can use them.
   if (!a->mode && (a->default_mode < SV_PLAIN || a->default_mode > SV_GREEDY))
     return fail(SV_EINVAL, "default_mode is not an sv_mode");
@@ -221,12 +235,6 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   return p;
 }
 
-// 16-byte vector loads need every row start on a 16-byte boundary.
-bool vector_loads(const sv_config& cfg, const sv_args* a) {
-  const int es = cfg.dtype == SV_BF16 ? 2 : 4;
-  return ((size_t)cfg.vocab * es) % 16 == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
-         (a->K_max == 0 || (reinterpret_cast<uintptr_t>(a->draft_logits) % 16) == 0);  // NULL is aligned
-}
 
 // Enqueues the call in launches of at most kMaxSeqPerLaunch sequences and
 // kMaxRowsPerLaunch rows; prof (or NULL) receives the stage events of the

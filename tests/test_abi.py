@@ -110,6 +110,24 @@ def test_validate_rejects(kw, code):
 
 
 @needs_lib
+def test_validate_refuses_long_rows_that_are_not_whole_vectors():
+    # rows of more than one chunk (4096 bf16 / 2048 fp32 logits) are streamed
+    # as 16-byte vectors only: V * element size a multiple of 16 and the
+    # logit buffers 16-byte aligned; shorter rows may be anything
+    assert validate(_args(), vocab=65536) == SV_OK
+    assert validate(_args(), vocab=65543) == SV_EINVAL
+    assert b"16-byte" in binding.load_library().spec_verify_last_error()
+    assert validate(_args(target=0x10002), vocab=65536) == SV_EINVAL
+    assert validate(_args(draft=0x20008), vocab=65536) == SV_EINVAL
+    assert validate(_args(), vocab=4096) == SV_OK
+    assert validate(_args(), vocab=4097) == SV_EINVAL
+    assert validate(_args(), vocab=4095) == SV_OK
+    assert validate(_args(), vocab=2049, dtype=SV_F32) == SV_EINVAL
+    assert validate(_args(), vocab=2047, dtype=SV_F32) == SV_OK
+    assert validate(_args(target=0x10004), vocab=1001) == SV_OK
+
+
+@needs_lib
 def test_validate_ignores_defaults_no_row_uses():
     # greedy ignores the temperature; plain ignores top-k / top-p defaults
     assert validate(_args(default_mode=SV_GREEDY, tau=0.0)) == SV_OK

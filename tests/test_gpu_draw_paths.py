@@ -1,0 +1,86 @@
+"""Residual draws from the rows, in each of the library's launch shapes,
+against the oracle on every row.
+
+A first rejection whose kept set is not listed (plain rows, or a kept set
+above the list's size) draws from normalize((q - p)+) over the rows in
+vocabulary order (FDE Interviews breakdown of Chen et al., section 01;
+paperlayer.ai summary of arXiv 2302.01318, "Modified Rejection Sampling").
+The library does this in one of three ways, chosen from the call's shape:
+
+  * calls of at most 256 sequences that may hold plain rows and rows of at
+    least 8 spans of 8192 tokens: the span sums are made over the whole
+    chip before the sequence kernel, which locates the span and draws;
+  * other calls of fewer than 1024 sequences: the sequence kernel's 8
+    waves walk the rows;
+  * calls of 1024 sequences or more: the same with 4-wave work-groups.
+
+The decisions are the same in all three; only the order of the fp64 sums
+differs, inside the 1e-6 window that flags a row for inexact comparison.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import compare, run_gpu, run_oracle, with_oracle_drafts
+from speculative_sampling_amd import workloads
+from speculative_sampling_amd.binding import ST_ERRORS, ST_REREAD, SV_PLAIN
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def check_all(w, label):
+    w = with_oracle_drafts(w)
+    ref = run_oracle(w)
+    print(f"[{label}] B={w.B} K={w.K_max} V={w.V} {w.dtype}", flush=True)
+    gpu = run_gpu(w)
+    n_flag, err = compare(gpu, ref, w.dtype, label)
+    print(f"[{label}] flagged={n_flag} max|diag err|={err:.2e}", flush=True)
+    assert np.all(gpu["row_status"] & ST_ERRORS == 0) or w.k_per_row is not None
+    return w, gpu, ref
+
+
+def resampled(gpu, w):
+    kb = w.K_max if w.k_per_row is None else w.k_per_row.cpu().numpy()
+    return gpu["accepted"] < kb
+
+
+def test_spread_draw_plain_bf16_headline_vocab():
+    # 16 spans per row, every sequence in one call of 16
+    w, gpu, _ = check_all(workloads.iid_normal(16, 4, 128256, sigma_t=3.0, sigma_d=1.0, gen_seed=61, seed=60),
+                          "spread_plain_bf16")
+    r = resampled(gpu, w)
+    assert r.sum() >= 8   # the draws under test happened
+    assert np.all(gpu["row_status"][r] & ST_REREAD)
+
+
+def test_spread_draw_fp32_ragged_last_span():
+    # V = 70000: nine spans, the last one partial
+    check_all(workloads.iid_normal(10, 3, 70000, sigma_t=2.5, sigma_d=1.5, dtype="f32", temperature=1.2,
+                                   gen_seed=63, seed=62), "spread_plain_f32")
+
+
+@pytest.mark.skip(reason="rows of more than one chunk that are not whole 16-byte vectors faulted the GPU "
+                         "(element-by-element streaming); the library now refuses such calls on the host "
+                         "(test_abi.py) until the cause is found")
+def test_spread_draw_mixed_modes_unaligned_vocab():
+    # a mode per sequence (so the call may hold plain rows), ragged K_b, and
+    # a vocabulary that is not a whole number of 16-byte vectors
+    check_all(workloads.zipf_ragged(24, 5, 65543, gen_seed=65, seed=64), "spread_mixed_unaligned")
+
+
+def test_spread_draw_mixed_modes():
+    # a mode per sequence (so the call may hold plain rows) and ragged K_b
+    check_all(workloads.zipf_ragged(24, 5, 65536, gen_seed=65, seed=64), "spread_mixed")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_four_wave_sequence_kernel(dtype):
+    # 1200 sequences: the sequence kernel runs with 4-wave work-groups
+    w, gpu, _ = check_all(workloads.iid_normal(1200, 4, 3000, sigma_t=3.0, sigma_d=1.0, dtype=dtype,
+                                               gen_seed=67, seed=66), f"four_wave_{dtype}")
+    assert resampled(gpu, w).sum() > 500
+
+
+def test_four_wave_sequence_kernel_mixed():
+    check_all(workloads.zipf_ragged(1100, 4, 4096, gen_seed=69, seed=68), "four_wave_mixed")

@@ -9,8 +9,10 @@ used for that sequence.
   * B=512, ragged K_b ~ U{1..8}, V=256000 bf16, Zipf-shaped logits with a
     per-row vocabulary permutation, modes cycling plain / top-k 50 /
     top-p 0.9 at temperature 0.7;
-  * the headline B=64, K=4, V=128256 bf16 nucleus shape is checked on
-    sampled sequences in test_gpu_parity.py.
+  * B=100,000, K=4, V=32000 bf16, plain at temperature 1 (the batch-1
+    serving rounds in one call);
+  * the headline B=64, K=4, V=128256 bf16 shape in plain mode; its nucleus
+    form is checked on sampled sequences in test_gpu_parity.py.
 
 Draft tokens come from the library's own K = 0 step on the draft rows; the
 GPU sampler is compared with the oracle's in test_gpu_parity.py.
@@ -62,5 +64,23 @@ def test_zipf_ragged_full():
     gpu = check_sampled(w, (0, 1, 2, 256, 510, 511), "zipf_ragged_full")
     kb = w.k_per_row.cpu().numpy()
     assert np.all(gpu["accepted"] >= 0) and np.all(gpu["accepted"] <= kb)
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_plain_b100000_full():
+    dev = torch.device("cuda", 0)
+    w = workloads.config("latency_b1", device=dev, B=100000, gen_seed=34, seed=6)
+    gpu = check_sampled(w, (0, 1, 4097, 50000, 99998, 99999), "plain_b100000_full")
+    assert np.all(gpu["row_status"] & ST_ERRORS == 0)
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_plain_headline_shape_full():
+    dev = torch.device("cuda", 0)
+    w = workloads.config("plain_b64", device=dev, gen_seed=35, seed=7)
+    gpu = check_sampled(w, (0, 21, 42, 63), "plain_b64_full")
+    assert np.all(gpu["row_status"] & ST_ERRORS == 0)
     del w
     torch.cuda.empty_cache()
