@@ -877,13 +877,12 @@ struct RowSmem {
   int ci[kRowWaves][kCandVecs];    // the vocabulary index of each one's first logit
   float ck[kRowWaves][kCandVecs];  // while listing: the largest logit of each vector (within 2^-8 / c2)
   WaveRec wrec[kRowWaves];         // each wave's record
-  Hist h;
+  Hist h[3];                       // the finish's selection histograms (rotating)
   float pub[kRowWaves];            // each wave's running maximum (nucleus) or cut (top-k)
   float ucut[kRowWaves];           // the largest listing cut each wave used
   int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
-  SelOut sel;                      // the finish: a selection's result, for every wave
-  int seldg;                       //   a selection level's digit
   int wsum[kRowWaves];             //   each wave's part of a work-group sum
+  unsigned long long msum[kRowWaves];  //   each wave's part of a kept mass
 };
 
 __device__ __forceinline__ float lds_load_relaxed(const float* p) {
@@ -988,97 +987,117 @@ __device__ __forceinline__ float raise_cut(const RowSmem& sm, int wv, int n, flo
   return best;
 }
 
-template <int DT>
-__device__ __forceinline__ float vector_max(const uint4& v) {
-  float m = -kInf;
-#pragma unroll
-  for (int k = 0; k < Fmt<DT>::VE; ++k) m = fmaxf(m, elem<DT>(v, k));
-  return m;
-}
-
 // ---- the finish's selection, over the whole work-group ----
 //
 // The selection of wave_select over elements known to lie in [lo, hi],
-// with the histogram filled by all kThreads threads (one bin per thread to
-// clear) and each digit picked by wave 0 and passed to the others through
-// LDS.  bf16 elements spanning fewer than 256 values (narrow_range) take
-// one level whose digits are the values themselves: the histogram counts
-// them, and wave 0 takes each digit's mass from its count.  each(f,
-// with_mass) calls f(x, mass) for this thread's share of the elements
-// (mass only when with_mass is set).  clean: the counts are known to be 0.
+// with the histogram filled by all kThreads threads and every wave picking
+// each digit itself from it (the same reads give the same digit), so a
+// level costs one barrier.  Three histograms rotate: a level counts into
+// sm.h[hb], clears the one after it for the next level, and the one after
+// that is still being read by slower waves' previous picks.  hb: in, a
+// histogram known to be clear; out, the next such one.
+//   bf16 elements spanning fewer than 256 values (narrow_range) take one
+// level whose digits are the values themselves: the histogram counts them,
+// and each digit's mass is its count times the value's mass.  Otherwise
+// MSB-first 8-bit digits; for fp32 only the bits below the prefix shared
+// by fkey(lo) and fkey(hi) (fixed top digits would put nearly every
+// candidate in one or two bins, whose atomics then serialise).  A nucleus
+// selection adds masses per digit; a top-k one counts elements only, and
+// its kept mass (keep_mass) is summed once T is known: the same integers.
+// each(f, with_mass) calls f(x, mass) for this thread's share of the
+// elements (mass only when with_mass is set).
 template <int DT, class Each>
 __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned long long target, RowSmem& sm,
                                             int tid, int wv, int lane, float lo, float hi, float c2, float oM,
-                                            double fM, bool clean) {
+                                            double fM, int& hb, bool keep_mass = true) {
   static_assert(kThreads == 256, "one histogram bin per thread");
   unsigned long long above_c = 0, above_m = 0, last_c = 0, last_m = 0;
   bool reached = true;
+  SelOut r;
   if (DT == SV_BF16 && narrow_range(lo, hi)) {
     const uint32_t kb = (fkey(hi) >> 16) - 255u;  // the key of digit 0
-    if (!clean) {
-      sm.h.hc[tid] = 0;
-      lds_barrier();
-    }
-    each([&](float x, unsigned long long) { atomicAdd(&sm.h.hc[min(255u, (fkey(x) >> 16) - kb)], 1u); }, false);
+    Hist& h = sm.h[hb];
+    each([&](float x, unsigned long long) { atomicAdd(&h.hc[min(255u, (fkey(x) >> 16) - kb)], 1u); }, false);
+    const int nx = hb == 2 ? 0 : hb + 1;
+    sm.h[nx].hc[tid] = 0;
+    sm.h[nx].hm[tid] = 0;
     lds_barrier();
-    if (wv == 0) {
-      const int dg = pick_digit(
-          [&](int d, unsigned long long& c, unsigned long long& m) {
-            const uint32_t n = sm.h.hc[d];
-            c = n;
-            m = n ? (unsigned long long)n * mass_of(bf16_of_key(kb + (uint32_t)d), c2, oM, fM) : 0ull;
-          },
-          by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
-      if (lane == 0) {
-        uint32_t pkey = (kb + (uint32_t)dg) << 16;
-        pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
-        sm.sel.T = key_value(pkey);
-        sm.sel.reached = reached;
-        sm.sel.n_keep = (uint32_t)(above_c + last_c);
-        sm.sel.m_keep = above_m + last_m;
-        sm.sel.m_above = above_m;
-      }
-    }
-    lds_barrier();
-    return sm.sel;
+    const int dg = pick_digit(
+        [&](int d, unsigned long long& c, unsigned long long& m) {
+          const uint32_t n = h.hc[d];
+          c = n;
+          m = n ? (unsigned long long)n * mass_of(bf16_of_key(kb + (uint32_t)d), c2, oM, fM) : 0ull;
+        },
+        by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+    hb = nx;
+    uint32_t pkey = (kb + (uint32_t)dg) << 16;
+    pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
+    r.T = key_value(pkey);
+    r.reached = reached;
+    r.n_keep = (uint32_t)(above_c + last_c);
+    r.m_keep = above_m + last_m;
+    r.m_above = above_m;
+    return r;
   }
-  // MSB-first 8-bit digits over the 32-bit keys (bf16: the top 16 bits)
-  const int levels = DT == SV_BF16 ? 2 : 4;
+  int levels = 2, shift0 = 24;
   uint32_t pkey = 0, pmask = 0;
+  if constexpr (DT != SV_BF16) {
+    const uint32_t klo = fkey(lo), khi = fkey(hi);
+    const uint32_t diff = klo <= khi ? klo ^ khi : 0xFFFFFFFFu;
+    const int nb = diff ? 32 - __clz(diff) : 0;  // the varying low bits
+    pmask = nb >= 32 ? 0u : ~((1u << nb) - 1u);
+    pkey = klo & pmask;
+    shift0 = max(nb - 8, 0);
+    levels = (shift0 + 7) / 8 + 1;
+  }
   for (int lv = 0; lv < levels; ++lv) {
-    const int shift = 24 - 8 * lv;
-    sm.h.hc[tid] = 0;
-    sm.h.hm[tid] = 0;
-    lds_barrier();
+    const int shift = max(shift0 - 8 * lv, 0);
+    Hist& h = sm.h[hb];
     each(
         [&](float x, unsigned long long m) {
           const uint32_t key = fkey(x);
           if ((key & pmask) == pkey) {
             const uint32_t dg = (key >> shift) & 255u;
-            atomicAdd(&sm.h.hc[dg], 1u);
-            atomicAdd(&sm.h.hm[dg], m);
+            atomicAdd(&h.hc[dg], 1u);
+            if (by_mass) atomicAdd(&h.hm[dg], m);
           }
         },
-        true);
+        by_mass);
+    const int nx = hb == 2 ? 0 : hb + 1;
+    sm.h[nx].hc[tid] = 0;
+    sm.h[nx].hm[tid] = 0;
     lds_barrier();
-    if (wv == 0) {
-      const int dg = pick_digit_hist(sm.h, by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
-      if (lane == 0) sm.seldg = dg;
-    }
-    lds_barrier();
-    pkey |= (uint32_t)sm.seldg << shift;
+    const int dg = pick_digit(
+        [&](int d, unsigned long long& c, unsigned long long& m) {
+          c = h.hc[d];
+          m = by_mass ? h.hm[d] : 0ull;
+        },
+        by_mass, target, above_c, above_m, last_c, last_m, reached, lane);
+    hb = nx;
+    pkey |= (uint32_t)dg << shift;
     pmask |= 255u << shift;
   }
   if (DT == SV_BF16) pkey |= (pkey >> 31) ? 0u : 0xFFFFu;
-  if (wv == 0 && lane == 0) {
-    sm.sel.T = key_value(pkey);
-    sm.sel.reached = reached;
-    sm.sel.n_keep = (uint32_t)(above_c + last_c);
-    sm.sel.m_keep = above_m + last_m;
-    sm.sel.m_above = above_m;
+  r.T = key_value(pkey);
+  r.reached = reached;
+  r.n_keep = (uint32_t)(above_c + last_c);
+  r.m_keep = above_m + last_m;
+  r.m_above = above_m;
+  if (!by_mass && keep_mass) {
+    // the elements >= T are those counted in n_keep
+    const float T = r.T;
+    unsigned long long acc = 0;
+    each([&](float x, unsigned long long m) { acc += x >= T ? m : 0ull; }, true);
+    acc = lane63(wave_scan(acc, 0ull, [](unsigned long long a, unsigned long long b) { return a + b; }));
+    if (lane == 0) sm.msum[wv] = acc;
+    lds_barrier();
+    unsigned long long mk = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) mk += sm.msum[w];
+    r.m_keep = mk;
+    // (msum is written again only after this call's next barrier)
   }
-  lds_barrier();
-  return sm.sel;
+  return r;
 }
 
 template <int DT, bool VEC, int MODE>
@@ -1367,7 +1386,8 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       sm.ucut[wv] = ucut;
     }
   }
-  sm.h.hc[threadIdx.x] = 0;  // the finish's first selection counts into these
+  sm.h[0].hc[threadIdx.x] = 0;  // the finish's first selection counts into these
+  sm.h[0].hm[threadIdx.x] = 0;
   lds_barrier();
 
   // ---- finish ----
@@ -1475,28 +1495,11 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       const float Mhi = M + (fabsf(M) + 1.0f) * 0.001953125f;
       // Candidates spanning fewer than 256 bf16 values take one histogram
       // pass over all of them.  Otherwise a nucleus first tries the cut 8
-      // log2 units below the row maximum (the lists reach 10), then C, and
-      // top-k first selects the k-th largest vector key over the
-      // candidates: every vector holds its own maximum, so the k-th largest
-      // logit is at least that key.
+      // log2 units below the row maximum (the lists reach 10), then C; a
+      // top-k selection runs over every candidate >= C at once.
       const bool narrow = DT == SV_BF16 && C < kInf && narrow_range(fmaxf(C, -kMaxFinite), Mhi);
-      bool hist_clean = true;  // the counts were cleared before the finish
-      float C1 = (by_mass && !narrow) ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
-      if (!by_mass && !narrow && C < kInf) {
-        const SelOut sk = wg_select<DT>(
-            [&](auto&& f, bool) {
-              for (int j = tid; j < N; j += kThreads) {
-                uint4 v;
-                int e0;
-                vec_at(j, v, e0);
-                const float vm = vector_max<DT>(v);
-                if (vm >= C) f(vm, 0ull);
-              }
-            },
-            false, target, sm, tid, wv, lane, C, Mhi, c2, oM, fM, hist_clean);
-        hist_clean = false;
-        if (sk.reached) C1 = fmaxf(C, sk.T);
-      }
+      int hb = 0;  // a clear histogram (cleared before the finish)
+      const float C1 = (by_mass && !narrow) ? fmaxf(C, (float)((double)M - 8.0 / (double)c2)) : C;
       SelOut so;
       bool ok = false;
       for (int pass = 0; pass < 2 && !ok && C < kInf; ++pass) {
@@ -1516,8 +1519,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
                 }
               }
             },
-            by_mass, target, sm, tid, wv, lane, Cuf, Mhi, c2, oM, fM, hist_clean);
-        hist_clean = false;
+            by_mass, target, sm, tid, wv, lane, Cuf, Mhi, c2, oM, fM, hb);
         ok = so.reached && so.T >= Cu;
       }
       if (!ok) {
@@ -1530,7 +1532,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
                 f(x, mass_of(x, c2, oM, fM));
               }
             },
-            by_mass, target, sm.h, lane);
+            by_mass, target, sm.h[hb], lane);  // (a histogram no wave reads any more)
         rr.flags |= SV_ST_FULLSELECT;
       }
       rr.T = so.T;
