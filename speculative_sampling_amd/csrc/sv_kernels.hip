@@ -1147,11 +1147,21 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const size_t rid = (size_t)b * R + r;
   const size_t slot0 = rid * S;
   const float c2 = (float)sp.c2;
-  // The row's draft token: loaded here and first used after the stream,
-  // which also loads the token's logit.  (A load of the logit here would
-  // hold the stream until the token arrives, behind every row's first
-  // chunk.)
-  const int tok = t < sp.Kb ? uniform_load(P.tokens + (size_t)b * P.K_max + t) : INT32_MIN;
+  // The row's draft token: a vector load issued here and first used after
+  // the stream, which also loads the token's logit.  (Through the scalar
+  // cache its wait would share the LDS counter, and the barrier below would
+  // hold the stream until the token arrived, behind every row's first chunk;
+  // a load of the logit here would do the same.)
+  int tok = INT32_MIN;
+  if (t < sp.Kb) {
+    const __amdgpu_buffer_rsrc_t trs = row_resource(reinterpret_cast<const char*>(P.tokens + (size_t)b * P.K_max),
+                                                    P.K_max * 4);
+    // (an offset the compiler cannot see is uniform keeps the value in a
+    // vector register, so that nothing waits for it before it is used)
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    tok = (int)__builtin_amdgcn_raw_buffer_load_b32(trs, t * 4 + z, 0, 0);
+  }
   if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
   lds_barrier();
 
