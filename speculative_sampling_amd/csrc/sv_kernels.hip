@@ -1644,6 +1644,11 @@ struct SmemSeq {
   int ri[NW];
   uint32_t misc[4];
   double rx[2];
+  int rj[NW];
+  // a draw located by precomputed sums: its range, the weight before it,
+  // the row's total and its first / last tokens with weight
+  int dl_lo, dl_hi, dl_nzlo, dl_nzhi, dl_beyond;
+  double dl_base, dl_S;
   double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
   double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
   double tsum[NW][kTileCap];
@@ -2230,18 +2235,24 @@ __global__ __launch_bounds__(kThreads) void draw_sum_kernel(const KParams P) {
   }
 }
 
-// Inverse CDF inside the span [lo, hi) (at most kDrawSpan tokens): thread
-// t holds groups 2t and 2t + 1, the work-group's running sum of the group
-// sums (from `base`, the weight before lo) finds the group crossing
-// `target` (+inf: none), then the token in it.  Without a crossing (the
-// target beyond the rounded total) the last token with weight is taken.
-// S: the row's total weight, for the CDF margins against u.
-template <int DT, bool VEC>
-__device__ __forceinline__ Draw draw_in_span(const KParams& P, const RowW& wq, const RowW& wp, bool all,
-                                             const char* qrow, const char* prow, int lo, int hi, double base,
-                                             double target, double S, int nzlo, int nzhi, double u,
-                                             SmemSeq<kSeqWaves>& sm) {
-  static_assert(kDrawSpan == 16 * kSeqThreads, "two groups of 8 per thread");
+// Inverse CDF over the tokens [lo, hi) of one row (pair) by the whole
+// work-group, with two barriers: thread t holds groups 2t and 2t + 1 of 8
+// tokens (so at most 16 NW 64 tokens); each wave sums its groups, every
+// wave finds from the wave sums the wave whose running sum (from `base`)
+// crosses `target` (+inf: none), and that wave finds the group and the
+// token in it, the groups' sums and the tokens' weights added as in the
+// other draws.  Without a crossing the last token with weight is taken.
+struct RangeDraw {
+  int y;           // the token, -1 if the range has no weight
+  bool crossed;    // the target was crossed (else: the last token with weight)
+  int glo, ghi;    // first / last token of the range's groups with weight
+  double clo, chi; // running sum just below and at y
+  double total;    // the range's weight
+};
+template <int DT, bool VEC, int NW>
+__device__ __forceinline__ RangeDraw draw_range(const KParams& P, const RowW& wq, bool use_p, const RowW& wp,
+                                                bool all, const char* qrow, const char* prow, int lo, int hi,
+                                                double base, double target, SmemSeq<NW>& sm, int lane, int wv) {
   const int tid = threadIdx.x;
   uint4 aq[2][2], ap[2][2];
   float w[2][8], s8[2];
@@ -2253,103 +2264,185 @@ __device__ __forceinline__ Draw draw_in_span(const KParams& P, const RowW& wq, c
     aq[h][0] = aq[h][1] = ap[h][0] = ap[h][1] = make_uint4(ninf, ninf, ninf, ninf);
     if (e[h] < hi) {
       load8<DT, VEC>(P, qrow, e[h], aq[h]);
-      load8<DT, VEC>(P, prow, e[h], ap[h]);
+      if (use_p) load8<DT, VEC>(P, prow, e[h], ap[h]);
     }
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) s8[h] = weights8<DT>(wq, true, wp, all, aq[h], ap[h], w[h]);
-  double tot;
-  const double ex = seq_exclusive_scan((double)s8[0] + (double)s8[1], &tot, sm);
-  const double c0 = base + ex, c1 = c0 + (double)s8[0];
-  // the group crossing the target, and the last group with weight
-  const int h = (s8[0] > 0.0f && c0 + (double)s8[0] > target) ? 0
-                : (s8[1] > 0.0f && c1 + (double)s8[1] > target) ? 1
-                                                                  : -1;
-  const int gx = seq_min_i(h >= 0 ? 2 * tid + h : 0x7fffffff, sm);
-  const int gl = seq_max_i(s8[1] > 0.0f ? 2 * tid + 1 : s8[0] > 0.0f ? 2 * tid : -1, sm);
-  Draw d;
-  d.flags = 0;
-  d.y = 0;
-  const int g = gx != 0x7fffffff ? gx : gl;
-  if (g >= 0 && tid == g / 2) {
-    int y = -1, ylast = -1;
-    double cl = 0.0, ch = 0.0, ll = 0.0, lh = 0.0;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh != (g & 1)) continue;  // (static indices into w and e)
-      double r = hh ? c1 : c0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float wk = w[hh][k];
-        const double rn = r + (double)wk;
-        if (wk > 0.0f) {
-          if (y < 0 && gx != 0x7fffffff && rn > target) {
-            y = e[hh] + k;
-            cl = r;
-            ch = rn;
-          }
-          ylast = e[hh] + k;
-          ll = r;
-          lh = rn;
-        }
-        r = rn;
-      }
-    }
-    if (y < 0) {  // rounding inside the group, or no crossing at all
-      y = ylast;
-      cl = gx != 0x7fffffff ? ll : S;
-      ch = gx != 0x7fffffff ? lh : S;
-    }
-    sm.misc[3] = (uint32_t)y;
-    sm.rx[0] = cl;
-    sm.rx[1] = ch;
+  for (int h = 0; h < 2; ++h) s8[h] = weights8<DT>(wq, use_p, wp, all, aq[h], ap[h], w[h]);
+  const double ts = (double)s8[0] + (double)s8[1];
+  const double inc = wave_incl_scan(ts, lane);
+  const int fz = wave_min_i(s8[0] > 0.0f ? e[0] : s8[1] > 0.0f ? e[1] : 0x7fffffff);
+  const int lz = wave_max_i(s8[1] > 0.0f ? e[1] + 7 : s8[0] > 0.0f ? e[0] + 7 : -1);
+  if (lane == kWave - 1) sm.rd[wv] = inc;  // the wave's sum
+  if (lane == 0) {
+    sm.ri[wv] = fz;
+    sm.rj[wv] = lz;
   }
   __syncthreads();
-  if (g >= 0) {
-    d.y = (int)sm.misc[3];
-    const double plo = sm.rx[0] / S, phi = sm.rx[1] / S;
-    if (nzlo < d.y && u - plo < kWindow) d.flags |= SV_ST_MARGIN;
-    if (nzhi > d.y && phi - u < kWindow) d.flags |= SV_ST_MARGIN;
+  // the wave whose running sum crosses the target, else the last wave with weight
+  double run = base, cb = 0.0, lb = 0.0;
+  int cw = -1, lw = -1;
+  RangeDraw r;
+  r.glo = 0x7fffffff;
+  r.ghi = -1;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const double sw = sm.rd[x];
+    if (sw > 0.0) {
+      if (cw < 0 && run + sw > target) {
+        cw = x;
+        cb = run;
+      }
+      lw = x;
+      lb = run;
+    }
+    run += sw;
+    r.glo = min(r.glo, sm.ri[x]);
+    r.ghi = max(r.ghi, sm.rj[x]);
   }
-  return d;
+  r.total = run - base;
+  r.crossed = cw >= 0;
+  const int ww = cw >= 0 ? cw : lw;
+  if (wv == ww) {
+    const double c0 = (cw >= 0 ? cb : lb) + inc - ts;  // the running sum before this lane's groups
+    const uint64_t bc = __ballot(cw >= 0 && ts > 0.0 && c0 + ts > target);
+    const uint64_t bw = __ballot(ts > 0.0);
+    const int src = bc ? __ffsll((long long)bc) - 1 : 63 - __clzll((long long)bw);
+    if (lane == src) {
+      int y = -1, ylast = -1;
+      double cl = 0.0, ch = 0.0, ll = 0.0, lh = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        double rr = hh ? c0 + (double)s8[0] : c0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float wk = w[hh][k];
+          const double rn = rr + (double)wk;
+          if (wk > 0.0f) {
+            if (y < 0 && cw >= 0 && rn > target) {
+              y = e[hh] + k;
+              cl = rr;
+              ch = rn;
+            }
+            ylast = e[hh] + k;
+            ll = rr;
+            lh = rn;
+          }
+          rr = rn;
+        }
+      }
+      if (y < 0) {  // rounding inside the group, or no crossing at all
+        y = ylast;
+        cl = ll;
+        ch = lh;
+      }
+      sm.misc[3] = (uint32_t)y;
+      sm.rx[0] = cl;
+      sm.rx[1] = ch;
+    }
+  }
+  __syncthreads();
+  r.y = ww >= 0 ? (int)sm.misc[3] : -1;
+  r.clo = sm.rx[0];
+  r.chi = sm.rx[1];
+  return r;
 }
 
 // The residual draw of sequence b at its first rejection n from the span
-// sums draw_sum_kernel made (whole work-group).  Without residual mass it
-// is the rows' own draw, which falls back to q.
+// sums draw_sum_kernel made (whole work-group).  Wave 0 locates the span
+// holding u S from the sums (lane l holding spans [l m, l m + m); `pre`,
+// loaded with the records, is lane l's span when there is one span per
+// lane), then the work-group draws inside it.  Without residual mass it is
+// the rows' own draw, which falls back to q.
 template <int DT, bool VEC>
 __device__ __forceinline__ Draw draw_spread(const KParams& P, int b, int n, const RowRec& rq, const RowRec& rp,
-                                            double u, SmemSeq<kSeqWaves>& sm, int lane, int wv) {
-  const int tid = threadIdx.x, D = P.D;
+                                            double u, const DrawSum& pre, SmemSeq<kSeqWaves>& sm, int lane,
+                                            int wv) {
+  const int D = P.D;
   const RowW wq = row_w(rq), wp = row_w(rp);
   const bool all = __builtin_amdgcn_readfirstlane((int)(wq.T == -kInf && wp.T == -kInf)) != 0;
   const char* qrow = static_cast<const char*>(row_ptr<DT>(P, b, true, n));
   const char* prow = static_cast<const char*>(row_ptr<DT>(P, b, false, n));
-  DrawSum ds;
-  ds.s = 0.0;
-  ds.first = 0x7fffffff;
-  ds.last = -1;
-  if (tid < D) ds = P.dsums[(size_t)b * D + tid];
-  double S;
-  const double ex = seq_exclusive_scan(ds.s, &S, sm);
-  const int nzlo = seq_min_i(ds.first, sm), nzhi = seq_max_i(ds.last, sm);
-  if (!(S > 0.0)) {
-    __syncthreads();
-    return draw_from_rows<DT, VEC, kSeqWaves>(P, rq, true, rp, qrow, prow, u, sm, lane, wv, nullptr);
+  if (wv == 0) {
+    const int m = (D + kWave - 1) / kWave;
+    double ls = 0.0;
+    int lf = 0x7fffffff, ll = -1;
+    if (m == 1) {
+      ls = pre.s;
+      lf = pre.first;
+      ll = pre.last;
+    } else {
+      for (int k = 0; k < m; ++k) {
+        const int sp = lane * m + k;
+        if (sp < D) {
+          const DrawSum d = P.dsums[(size_t)b * D + sp];
+          ls += d.s;
+          lf = min(lf, d.first);
+          ll = max(ll, d.last);
+        }
+      }
+    }
+    const double inc = wave_incl_scan(ls, lane);
+    const double S = lane63(inc);
+    const int nzlo = wave_min_i(lf), nzhi = wave_max_i(ll);
+    const double target = u * S;
+    // the first lane whose running sum crosses u S (else, u S beyond the
+    // rounded total: the last lane with weight), then its span
+    const uint64_t bc = __ballot(ls > 0.0 && inc > target);
+    const uint64_t bw = __ballot(ls > 0.0);
+    const bool beyond = bc == 0;
+    const int src = !beyond ? __ffsll((long long)bc) - 1 : bw ? 63 - __clzll((long long)bw) : 0;
+    if (lane == src) {
+      double run = inc - ls;
+      int c = -1, cl = -1;
+      double cb = 0.0, lb = 0.0;
+      for (int k = 0; k < m; ++k) {
+        const int sp = lane * m + k;
+        if (sp >= D) break;
+        const double sk = m == 1 ? pre.s : P.dsums[(size_t)b * D + sp].s;
+        if (sk > 0.0) {
+          if (c < 0 && run + sk > target) {
+            c = sp;
+            cb = run;
+          }
+          cl = sp;
+          lb = run;
+        }
+        run += sk;
+      }
+      if (c < 0) {  // beyond, or rounding between the lane's sum and its spans'
+        c = cl;
+        cb = lb;
+      }
+      sm.dl_lo = c * kDrawSpan;
+      sm.dl_hi = min(P.V, (c + 1) * kDrawSpan);
+      sm.dl_base = cb;
+      sm.dl_beyond = beyond ? 1 : 0;
+    }
+    if (lane == 0) {
+      sm.dl_S = S;
+      sm.dl_nzlo = nzlo;
+      sm.dl_nzhi = nzhi;
+    }
   }
-  const double target = u * S;
-  const int cs = seq_min_i((tid < D && ds.s > 0.0 && ex + ds.s > target) ? tid : 0x7fffffff, sm);
-  const int cl = seq_max_i((tid < D && ds.s > 0.0) ? tid : -1, sm);
-  const bool beyond = cs == 0x7fffffff;  // u * S beyond the rounded total: the last token with weight
-  const int c = beyond ? cl : cs;
   __syncthreads();
-  if (tid == c) sm.rd[0] = ex;
-  __syncthreads();
-  const double base = sm.rd[0];
-  __syncthreads();
-  Draw d = draw_in_span<DT, VEC>(P, wq, wp, all, qrow, prow, c * kDrawSpan, min(P.V, (c + 1) * kDrawSpan), base,
-                                 beyond ? kInf : target, S, nzlo, nzhi, u, sm);
-  d.flags |= SV_ST_REREAD;
+  const double S = sm.dl_S;
+  if (!(S > 0.0)) return draw_from_rows<DT, VEC, kSeqWaves>(P, rq, true, rp, qrow, prow, u, sm, lane, wv, nullptr);
+  const int lo = sm.dl_lo, hi = sm.dl_hi, nzlo = sm.dl_nzlo, nzhi = sm.dl_nzhi;
+  const bool beyond = sm.dl_beyond != 0;
+  const double base = sm.dl_base;
+  const RangeDraw r = draw_range<DT, VEC, kSeqWaves>(P, wq, true, wp, all, qrow, prow, lo, hi, base,
+                                                     beyond ? kInf : u * S, sm, lane, wv);
+  Draw d;
+  d.flags = SV_ST_REREAD;
+  d.y = r.y;
+  if (r.y >= 0) {
+    const double plo = (r.crossed ? r.clo : S) / S, phi = (r.crossed ? r.chi : S) / S;
+    if (nzlo < d.y && u - plo < kWindow) d.flags |= SV_ST_MARGIN;
+    if (nzhi > d.y && phi - u < kWindow) d.flags |= SV_ST_MARGIN;
+  } else {
+    d.y = 0;
+  }
   return d;
 }
 
@@ -2407,6 +2500,21 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
   for (int r = tid; r < R; r += NT) {
     const bool used = r <= KM ? r <= Kb : (r - KM - 1 < Kb && have_draft);
     if (used) sm.rows[r] = P.rows[(size_t)b * R + r];
+  }
+  // Loaded with the records by wave 0, for draws that may follow the walk:
+  // the span sums of a spread residual draw (lane l: span l) and the chunk
+  // sums of target row K_b for a plain bonus draw (lane l: chunk l).
+  DrawSum dsp;
+  dsp.s = 0.0;
+  dsp.first = 0x7fffffff;
+  dsp.last = -1;
+  ChunkRec crp;
+  crp.z = 0.0;
+  crp.o = 0.0f;
+  crp.pad = 0;
+  if (wv == 0) {
+    if (NW == kSeqWaves && P.spread && P.D <= kWave && lane < P.D) dsp = P.dsums[(size_t)b * P.D + lane];
+    if (P.S <= kWave && lane < P.S) crp = P.chunks[((size_t)b * R + Kb) * P.S + lane];
   }
   // The walk's uniforms depend only on seed, sequence, position and
   // purpose: the last wave draws those of positions 0..63 while the records
@@ -2492,6 +2600,27 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
         write_tokens(P, b, n, d.y, st | d.flags, lane, kWave);
       } else {
         job = 1;
+        if (!resample && (rq.flags & kRfChunks) && P.S <= kWave) {
+          // a plain bonus draw: the chunk holding u, from the chunk sums
+          // (lane l: chunk l; the weights of draw_from_rows), and the work-
+          // group draws inside it
+          const float c2f = (float)rq.c2;
+          const double wc = crp.z > 0.0 ? crp.z * exp2((double)crp.o - (double)rq.M * (double)c2f) / rq.Zs : 0.0;
+          const double inc = wave_incl_scan(wc, lane);
+          const uint64_t bc = __ballot(wc > 0.0 && inc > u);
+          const uint64_t bw = __ballot(wc > 0.0);
+          if (bw) {
+            job = 2;
+            const int c = bc ? __ffsll((long long)bc) - 1 : 63 - __clzll((long long)bw);
+            const double base = bc ? lane_at(inc - wc, c) : 0.0;  // (u beyond the rounded total: the last token with weight)
+            if (lane == 0) {
+              sm.dl_lo = c * P.L;
+              sm.dl_hi = min(P.V, c * P.L + P.L);
+              sm.dl_base = base;
+              sm.dl_beyond = bc ? 0 : 1;
+            }
+          }
+        }
         if (lane == 0) {
           sm.misc[0] = (uint32_t)n;
           sm.misc[1] = st;
@@ -2502,7 +2631,8 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
     if (lane == 0) sm.misc[2] = (uint32_t)job;
   }
   __syncthreads();
-  if (sm.misc[2] == 0u) return;
+  const uint32_t job = sm.misc[2];
+  if (job == 0u) return;
   // draw from the rows (plain rows, or a kept set not held as a list)
   const int n = (int)sm.misc[0];
   uint32_t st = sm.misc[1];
@@ -2511,11 +2641,29 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
   const RowRec rq = sm.rows[n];
   const RowRec rp = resample ? sm.rows[KM + 1 + n] : rq;
   __syncthreads();  // sm.misc / sm.rx are reused by the draw
+  if (job == 2u) {
+    // a plain bonus draw inside the chunk located by wave 0
+    const RowW wq = row_w(rq);
+    const bool all = __builtin_amdgcn_readfirstlane((int)(wq.T == -kInf)) != 0;
+    const double base = sm.dl_base;
+    const RangeDraw r =
+        draw_range<DT, VEC, NW>(P, wq, false, wq, all, static_cast<const char*>(row_ptr<DT>(P, b, true, n)), nullptr,
+                                sm.dl_lo, sm.dl_hi, 0.0, sm.dl_beyond ? kInf : u - base, sm, lane, wv);
+    if (r.y >= 0) {
+      uint32_t fl = SV_ST_REREAD;
+      const double plo = base + (r.crossed ? r.clo : r.total), phi = base + (r.crossed ? r.chi : r.total);
+      if (r.glo < r.y && u - plo < kWindow) fl |= SV_ST_MARGIN;
+      if (r.ghi > r.y && phi - u < kWindow) fl |= SV_ST_MARGIN;
+      write_tokens(P, b, n, r.y, st | fl, tid, NT);
+      return;
+    }
+    __syncthreads();  // (no weight in the chunk after all: the draw below)
+  }
   // a residual draw with the span sums made before this kernel, or the
   // work-group's own pass over the rows
   Draw d;
   if constexpr (NW == kSeqWaves) {
-    if (P.spread && resample) d = draw_spread<DT, VEC>(P, b, n, rq, rp, u, sm, lane, wv);
+    if (P.spread && resample) d = draw_spread<DT, VEC>(P, b, n, rq, rp, u, dsp, sm, lane, wv);
   }
   if (!(NW == kSeqWaves && P.spread && resample))
     d = draw_from_rows<DT, VEC, NW>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
