@@ -51,7 +51,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, R_max, D;
-  size_t off_chunks, off_rows, off_kept, off_dsums, total;
+  size_t off_pcount, off_chunks, off_rows, off_kept, off_dsums, off_phdr, off_pvec, off_pik, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -77,6 +77,10 @@ Geometry geometry(const sv_config* cfg) {
   const size_t rows = (size_t)cfg->max_batch * g.R_max;
   const size_t target_rows = (size_t)cfg->max_batch * (cfg->max_k + 1);
   size_t off = 0;
+  // the arrival counters of split rows come first, at the same place in
+  // every layout: each call leaves them at zero
+  g.off_pcount = off;
+  off = align_up(off + sv::kMaxSplitRows * sizeof(int32_t), 256);
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
   g.off_rows = off;
@@ -86,6 +90,14 @@ Geometry geometry(const sv_config* cfg) {
   g.D = (V + sv::kDrawSpan - 1) / sv::kDrawSpan;
   g.off_dsums = off;
   off = align_up(off + (size_t)cfg->max_batch * g.D * sizeof(sv::DrawSum), 256);
+  // part records of split rows (only launches of 2 to 3 rows per CU split)
+  const size_t n_parts = rows > 2 * (size_t)sv::kRowCUs && g.S >= 2 * sv::kRowWaves ? sv::kRowCUs : 0;
+  g.off_phdr = off;
+  off = align_up(off + n_parts * sizeof(sv::PartHdr), 256);
+  g.off_pvec = off;
+  off = align_up(off + n_parts * sv::kRowWaves * sv::kCandVecs * sizeof(uint4), 256);
+  g.off_pik = off;
+  off = align_up(off + n_parts * sv::kRowWaves * sv::kCandVecs * sizeof(uint2), 256);
   g.total = off;
   return g;
 }
@@ -171,7 +183,9 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     (void)hipSetDevice(prev);
     return fail(SV_ENOMEM, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
   }
-  e = hipDeviceSynchronize();
+  // the arrival counters of split rows start at zero (each call leaves them so)
+  e = hipMemset(static_cast<char*>(h->ws) + g.off_pcount, 0, sv::kMaxSplitRows * sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
     delete h;
@@ -223,6 +237,13 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.kept = reinterpret_cast<sv::KeptEntry*>(base + g.off_kept);
   p.dsums = reinterpret_cast<sv::DrawSum*>(base + g.off_dsums);
   p.D = g.D;
+  p.full = 0;  // set per launch
+  p.parts = 1;
+  p.nsplit = 0;
+  p.pcount = reinterpret_cast<int32_t*>(base + g.off_pcount);
+  p.phdr = reinterpret_cast<sv::PartHdr*>(base + g.off_phdr);
+  p.pvec = reinterpret_cast<uint4*>(base + g.off_pvec);
+  p.pik = reinterpret_cast<uint2*>(base + g.off_pik);
   // Residual draws from the rows are spread over the chip when the call
   // may hold plain rows (their first rejection always needs the rows);
   // other calls draw the rare ones in the sequence kernel.

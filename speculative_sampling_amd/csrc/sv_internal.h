@@ -79,6 +79,47 @@ struct DrawSum {
   int32_t last;   // last token of its last group of 8 with weight (-1: none)
 };
 
+// Balanced launches.  The nucleus, plain and greedy row kernels hold at
+// least three work-groups per CU.  A launch of between two and three rows
+// per CU (kRowCUs CUs) would leave some CUs a third row while the others
+// have two; instead the first 2 kRowCUs rows are streamed whole and each
+// remaining row is split into `parts` contiguous ranges of chunks, one
+// work-group each, so that every CU streams about the same bytes.  A part
+// leaves its waves' records and candidate lists in a PartHdr and the part
+// lists; the last part of a row to arrive (a counter per row) merges them
+// and finishes the row.
+constexpr int kRowCUs = 256;
+constexpr int kMaxParts = 4;
+// The split of a launch of `rows` rows of S chunks: rows [0, *full) whole,
+// the rest in the returned number of parts each (1: no split).
+inline int row_split(size_t rows, int S, int* full) {
+  *full = (int)rows;
+  if (rows <= 2 * (size_t)kRowCUs || rows >= 3 * (size_t)kRowCUs) return 1;
+  const int extra = (int)(rows - 2 * (size_t)kRowCUs);
+  int p = kRowCUs / extra;
+  p = p < kMaxParts ? p : kMaxParts;
+  p = p < S / kRowWaves ? p : S / kRowWaves;  // at least one chunk per wave of every part
+  if (p < 2) return 1;
+  *full = 2 * kRowCUs;
+  return p;
+}
+// What one part's waves found (written with coherent stores).
+struct PartWave {
+  double z;        // the wave's softmax sum (see the row kernel's WaveRec)
+  float m, o;      // largest logit; exponent offset of z
+  int32_t arg;     // greedy: lowest index holding m
+  uint32_t flags;  // kCfNonFinite
+  int32_t ncand;   // candidate vectors listed, -1 after an overflow
+  float ucut;      // the largest listing cut used
+  float pub;       // the part's running maximum (nucleus) at its end
+  int32_t pad;
+};
+struct PartHdr {
+  PartWave w[kRowWaves];
+};
+// Split rows per launch: at most kRowCUs parts (extra rows x parts).
+constexpr int kMaxSplitRows = kRowCUs / 2;
+
 struct KParams {
   int32_t B, K_max, V, R, S, L;
   int32_t b_base, b_end;  // sequences [b_base, b_end) of this launch
@@ -106,6 +147,13 @@ struct KParams {
   DrawSum* dsums;    // [B][D]  (spread draws)
   int32_t D;         // spans of kDrawSpan tokens per row
   int32_t spread;    // residual draws from the rows go to the draw kernels
+  int32_t full;      // rows [0, full) of the launch streamed whole (row_split)
+  int32_t parts;     // work-groups per remaining row
+  int32_t nsplit;    // the part work-groups, (rows - full) x parts, launched first
+  int32_t* pcount;   // [kMaxSplitRows] arrivals per split row (0 between calls)
+  PartHdr* phdr;     // [kRowCUs] part records
+  uint4* pvec;       // [kRowCUs][kRowWaves][kCandVecs] listed vectors
+  uint2* pik;        // [kRowCUs][kRowWaves][kCandVecs] (first index, key bits)
 };
 
 // Enqueues the kernels of one call for sequences

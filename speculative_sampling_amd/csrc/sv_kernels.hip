@@ -220,6 +220,9 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ double wave_sum(double v) {
   return lane63(wave_scan(v, 0.0, [](double a, double b) { return a + b; }));
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+  return lane63(wave_scan(v, 0, [](int a, int b) { return a + b; }));
+}
 __device__ __forceinline__ int wave_min_i(int v) {
   return lane63(wave_scan(v, 0x7fffffff, [](int a, int b) { return min(a, b); }));
 }
@@ -872,6 +875,20 @@ struct WaveRec {
   uint32_t flags;  // kCfNonFinite
 };
 
+// Stores and loads that are coherent across the chip's L2s (agent scope,
+// relaxed): the parts of a split row exchange their records and lists
+// through them.  A part's stores are complete (vmcnt(0)) before its
+// arrival is counted, and the last part loads only after it has seen every
+// arrival, so no fence of a whole L2 is needed (such fences at the end of
+// every work-group cost more than the balance gains).
+__device__ __forceinline__ void cstore64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cload64(const void* p) {
+  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) { return (uint64_t)lo | ((uint64_t)hi << 32); }
+
 struct RowSmem {
   uint4 cv[kRowWaves][kCandVecs];  // candidate vectors of each wave, in vocabulary order
   int ci[kRowWaves][kCandVecs];    // the vocabulary index of each one's first logit
@@ -883,6 +900,11 @@ struct RowSmem {
   int ncand[kRowWaves];            // candidates listed by each wave, -1 after an overflow
   int wsum[kRowWaves];             //   each wave's part of a work-group sum
   unsigned long long msum[kRowWaves];  //   each wave's part of a kept mass
+  int pseg[kMaxParts * kRowWaves + 1];  // split rows: where each part-wave's list starts in the merged order
+  int parrive;                     //   the part's arrival number
+  int pinc;                        //   a part's list overflowed
+  float pg, pu;                    //   the parts' largest maximum / cut, and listing cut
+  int pwin[8][kRowWaves];          //   candidates per listing window, per wave
 };
 
 __device__ __forceinline__ float lds_load_relaxed(const float* p) {
@@ -1100,6 +1122,174 @@ __device__ __forceinline__ SelOut wg_select(Each&& each, bool by_mass, unsigned 
   return r;
 }
 
+// The last part of a split row to arrive (its part records from q0 on):
+// the parts' wave records are merged into one record (M the largest
+// maximum, Z the exact power-of-two rescaling of every sum to the largest
+// offset, flags or-ed, the greedy argmax the lowest index holding M) in
+// wrec[0], the other three left empty; their candidate lists are read in
+// part and wave order, which is vocabulary order, and those at or above the
+// row's cut are placed in the work-group's lists as one list of up to
+// kRowWaves * kCandVecs vectors (wave w's buffer holding positions 256 w
+// on).  A nucleus whose candidates within 10 log2 units of M do not fit
+// takes the widest narrower window that fits, as the waves do while
+// listing; lists that still do not fit, or a part's overflowed list, leave
+// the row to the whole-row selection.  Ends with the records, counts and
+// cuts in LDS as the finish reads them (without the barrier).
+template <int DT>
+__device__ __forceinline__ void merge_parts(const KParams& P, RowSmem& sm, size_t q0, int NP, bool is_topk,
+                                            bool is_topp, double ic2, int lane, int wv) {
+  constexpr int kSeg = kMaxParts * kRowWaves;
+  const int tid = (int)threadIdx.x;
+  const int NR = NP * kRowWaves;
+  if (wv == 0) {
+    double z = 0.0;
+    float m = -kInf, o = 0.0f, uc = -kInf, pb = -kInf;
+    int arg = 0x7fffffff, ncd = 0;
+    uint32_t flags = 0;
+    if (lane < NR) {
+      const uint64_t* d = reinterpret_cast<const uint64_t*>(&P.phdr[q0 + lane / kRowWaves].w[lane % kRowWaves]);
+      const uint64_t w0 = cload64(d), w1 = cload64(d + 1), w2 = cload64(d + 2), w3 = cload64(d + 3),
+                     w4 = cload64(d + 4);
+      z = __longlong_as_double((long long)w0);
+      m = __uint_as_float((uint32_t)w1);
+      o = __uint_as_float((uint32_t)(w1 >> 32));
+      arg = (int)(uint32_t)w2;
+      flags = (uint32_t)(w2 >> 32);
+      ncd = (int)(uint32_t)w3;
+      uc = __uint_as_float((uint32_t)(w3 >> 32));
+      pb = __uint_as_float((uint32_t)w4);
+    }
+    const bool fin = m > -kInf;  // (a wave with no finite logit has z = 0)
+    const float M = wave_max(m);
+    const float om = wave_max(fin ? o : -kInf);
+    const double zs = wave_sum(fin ? ldexp(z, (int)fmax((double)o - (double)om, -2000.0)) : 0.0);
+    const uint32_t fl = wave_or_u(flags);
+    const int ag = wave_min_i(fin && m == M ? arg : 0x7fffffff);
+    const bool inc = __ballot(lane < NR && ncd < 0) != 0;
+    const float ucm = wave_max(uc), gm = wave_max(pb);
+    const int cnt = (lane < NR && ncd > 0) ? ncd : 0;
+    const int incl = wave_incl_scan_i(cnt, lane);
+    if (lane < NR) sm.pseg[lane + 1] = incl;
+    if (lane == 0) {
+      sm.pseg[0] = 0;
+      WaveRec mr;
+      mr.z = zs;
+      mr.m = M;
+      mr.o = M > -kInf ? om : 0.0f;
+      mr.arg = ag;
+      mr.flags = fl;
+      sm.wrec[0] = mr;
+      WaveRec e;
+      e.z = 0.0;
+      e.m = -kInf;
+      e.o = 0.0f;
+      e.arg = 0x7fffffff;
+      e.flags = 0u;
+      sm.wrec[1] = e;
+      sm.wrec[2] = e;
+      sm.wrec[3] = e;
+      sm.pg = gm;
+      sm.pu = ucm;
+      sm.pinc = inc ? 1 : 0;
+    }
+  }
+  lds_barrier();
+  const bool lists = is_topk || is_topp;
+  bool incomplete = sm.pinc != 0;
+  const float g = sm.pg;
+  float C = sm.pu;
+  int Nk = 0;
+  if (lists && !incomplete) {
+    const int T = sm.pseg[NR];
+    // thread tid reads list positions [j0, j1) of the parts' lists in order
+    const int per = (T + kThreads - 1) / kThreads;
+    const int j0 = min(T, tid * per), j1 = min(T, j0 + per);
+    float key[kSeg];
+    int idx[kSeg], pos[kSeg];
+    int sg = 0;
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      const int j = j0 + k;
+      key[k] = -kInf;
+      idx[k] = 0;
+      pos[k] = -1;
+      if (j < j1) {
+        while (j >= sm.pseg[sg + 1]) ++sg;
+        pos[k] = (int)((q0 * kRowWaves + sg) * kCandVecs) + (j - sm.pseg[sg]);
+        const uint64_t w = cload64(&P.pik[pos[k]]);
+        idx[k] = (int)(uint32_t)w;
+        key[k] = __uint_as_float((uint32_t)(w >> 32));
+      }
+    }
+    // the cut: top-k's largest cut; a nucleus's widest window that fits
+    // (10, 8, 6, 5, 4, 3, 2 log2 units below the largest chunk maximum;
+    // keys are within 2^-8 / c2 of their vectors' maxima)
+    constexpr int kWin = 7;
+    float kc[kWin];
+#pragma unroll
+    for (int wi = 0; wi < kWin; ++wi) {
+      const double w = wi == 0 ? (double)kCandLog2 : wi == 1 ? 8.0 : (double)(8 - wi);
+      kc[wi] = is_topk ? g : (float)((double)g - w * ic2 - 0.00390625 * ic2);
+    }
+#pragma unroll
+    for (int wi = 0; wi < kWin; ++wi) {
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) c += (pos[k] >= 0 && key[k] >= kc[wi]) ? 1 : 0;
+      c = wave_sum_i(c);
+      if (lane == 0) sm.pwin[wi][wv] = c;
+    }
+    lds_barrier();
+    int wsel = -1;
+#pragma unroll
+    for (int wi = kWin - 1; wi >= 0; --wi) {
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) tot += sm.pwin[wi][w];
+      if (tot <= kRowWaves * kCandVecs && (wi == 0 || !is_topk)) wsel = wi;
+    }
+    if (wsel < 0) {
+      incomplete = true;
+    } else {
+      const double wsw = wsel == 0 ? (double)kCandLog2 : wsel == 1 ? 8.0 : (double)(8 - wsel);
+      float kcs = kc[0];
+#pragma unroll
+      for (int wi = 1; wi < kWin; ++wi) kcs = wi == wsel ? kc[wi] : kcs;
+      C = fmaxf(C, is_topk ? g : (float)((double)g - wsw * ic2));
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) cnt += (pos[k] >= 0 && key[k] >= kcs) ? 1 : 0;
+      const int incl = wave_incl_scan_i(cnt, lane);
+      if (lane == kWave - 1) sm.wsum[wv] = incl;
+      lds_barrier();
+      int off = incl - cnt;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) {
+        const int sw = sm.wsum[w];
+        off += w < wv ? sw : 0;
+        Nk += sw;
+      }
+      // the vectors of the positions kept, placed in order
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) {
+        if (pos[k] >= 0 && key[k] >= kcs) {
+          const uint64_t* dv = reinterpret_cast<const uint64_t*>(P.pvec + pos[k]);
+          const uint64_t a = cload64(dv), bb = cload64(dv + 1);
+          sm.cv[off / kCandVecs][off % kCandVecs] = make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)bb,
+                                                               (uint32_t)(bb >> 32));
+          sm.ci[off / kCandVecs][off % kCandVecs] = idx[k];
+          sm.ck[off / kCandVecs][off % kCandVecs] = key[k];
+          ++off;
+        }
+      }
+    }
+  }
+  if (tid < kRowWaves) {
+    sm.ncand[tid] = (lists && incomplete) ? (tid == 0 ? -1 : 0) : min(max(Nk - kCandVecs * tid, 0), kCandVecs);
+    sm.ucut[tid] = C;
+  }
+}
+
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   constexpr int VE = Fmt<DT>::VE;
@@ -1108,8 +1298,17 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const int lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int R = P.R, S = P.S;
-  const int b = P.b_base + (int)(blockIdx.x / (uint32_t)R);
-  const int r = (int)(blockIdx.x % (uint32_t)R);
+  // work-group blockIdx.x streams the launch's row rowg whole, or part
+  // `part` of NP of it (rows from P.full on).  The parts come first: the
+  // wave scheduler favours older waves, and a split row's parts must end
+  // early for its hand-off to be hidden.
+  const uint32_t bid = blockIdx.x;
+  const bool split = bid < (uint32_t)P.nsplit;
+  const int NP = split ? P.parts : 1;
+  const uint32_t rowg = split ? (uint32_t)P.full + bid / (uint32_t)NP : bid - (uint32_t)P.nsplit;
+  const int part = split ? (int)(bid % (uint32_t)NP) : 0;
+  const int b = P.b_base + (int)(rowg / (uint32_t)R);
+  const int r = (int)(rowg % (uint32_t)R);
   // Row r of the padded layout: target positions 0..K_max, then draft
   // positions; whether the sequence uses it depends on its K_b.
   // Whole work-groups return here, before any barrier.
@@ -1117,9 +1316,11 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const int t = tgt ? r : r - P.K_max - 1;
   if (!tgt && P.draft == nullptr) return;  // greedy calls without draft logits
   const char* row = static_cast<const char*>(row_ptr<DT>(P, b, tgt, t));
-  // wave wv streams chunks [cb, ce) of the row
-  const int per = (S + kRowWaves - 1) / kRowWaves;
-  const int cb = min(S, wv * per), ce = min(S, cb + per);
+  // the work-group streams chunks [ps, pe) of the row, wave wv chunks [cb, ce)
+  const int PS = (S + NP - 1) / NP;
+  const int ps = min(S, part * PS), pe = min(S, ps + PS);
+  const int per = (pe - ps + kRowWaves - 1) / kRowWaves;
+  const int cb = min(pe, ps + wv * per), ce = min(pe, cb + per);
   constexpr int ES = Fmt<DT>::ES;
   const int row_bytes = P.V * ES;
   // The sequence's parameters come through the scalar cache, so that using
@@ -1343,12 +1544,14 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       do_chunk(c, buf, false);
     }
   }
+  // the largest chunk maximum (nucleus) or cut (top-k) known to the work-group
+  const float gpub = (is_topk || is_topp) ? fmaxf(run, published_max(sm)) : -kInf;
   if ((is_topk || is_topp) && !over && nc > 0) {
     // Keep the listed vectors that can still hold a kept token: for top-k
     // those at or above the largest cut published, for a nucleus those
     // within 10 log2 units of the largest chunk maximum known (keys are
     // within 2^-8 / c2 of the vectors' maxima).
-    const float g = fmaxf(run, published_max(sm));
+    const float g = gpub;
     const float fcut = is_topk ? g : (float)((double)g - kCandLog2 * ic2);
     nc = compact_listed(sm, wv, nc, is_topk ? fcut : (float)((double)fcut - 0.00390625 * ic2), lane);
     ucut = fmaxf(ucut, fcut);
@@ -1390,11 +1593,47 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         wr.o = sa.o;
       }
     }
-    if (lane == 0) {
-      sm.wrec[wv] = wr;
-      sm.ncand[wv] = over ? -1 : nc;
-      sm.ucut[wv] = ucut;
+    if (!split) {
+      if (lane == 0) {
+        sm.wrec[wv] = wr;
+        sm.ncand[wv] = over ? -1 : nc;
+        sm.ucut[wv] = ucut;
+      }
+    } else {
+      // a part of a split row: the wave's record and list, for the part
+      // that finishes the row
+      const size_t qw = ((size_t)(rowg - (uint32_t)P.full) * NP + part) * kRowWaves + wv;
+      if (lane == 0) {
+        uint64_t* d = reinterpret_cast<uint64_t*>(&P.phdr[qw / kRowWaves].w[wv]);
+        cstore64(d + 0, (uint64_t)__double_as_longlong(wr.z));
+        cstore64(d + 1, pack2(__float_as_uint(wr.m), __float_as_uint(wr.o)));
+        cstore64(d + 2, pack2((uint32_t)wr.arg, wr.flags));
+        cstore64(d + 3, pack2((uint32_t)(over ? -1 : nc), __float_as_uint(ucut)));
+        cstore64(d + 4, pack2(__float_as_uint(gpub), 0u));
+      }
+      wave_sync();  // the wave's own list writes
+      const int nl = over ? 0 : nc;
+      for (int j = lane; j < nl; j += kWave) {
+        const uint4 v = sm.cv[wv][j];
+        uint64_t* dv = reinterpret_cast<uint64_t*>(P.pvec + qw * kCandVecs + j);
+        cstore64(dv, pack2(v.x, v.y));
+        cstore64(dv + 1, pack2(v.z, v.w));
+        cstore64(P.pik + qw * kCandVecs + j, pack2((uint32_t)sm.ci[wv][j], __float_as_uint(sm.ck[wv][j])));
+      }
     }
+  }
+  if (split) {
+    // Count this part's arrival once every store of its waves is complete;
+    // the last part of the row merges and finishes it, the others end here.
+    const uint32_t srow = rowg - (uint32_t)P.full;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (threadIdx.x == 0)
+      sm.parrive = __hip_atomic_fetch_add(&P.pcount[srow], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    if (sm.parrive != NP - 1) return;  // (work-group uniform)
+    if (threadIdx.x == 0) __hip_atomic_store(&P.pcount[srow], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_parts<DT>(P, sm, (size_t)srow * NP, NP, is_topk, is_topp, ic2, lane, wv);
   }
   sm.h[0].hc[threadIdx.x] = 0;  // the finish's first selection counts into these
   sm.h[0].hm[threadIdx.x] = 0;
@@ -2689,8 +2928,18 @@ template <int DT, bool VEC>
 hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
   // one row-kernel instance: the default mode's, or the one holding every
   // path when the call gives a mode per sequence
-  const dim3 grid((unsigned)((size_t)nseq * p.R));
-  launch_rows<DT, VEC>(p, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+  // A launch of two to three rows per CU streams the rows beyond two per
+  // CU in parts, one per CU (calls with one filter of plain, nucleus or
+  // greedy, whose row kernels hold three work-groups per CU; top-k lists
+  // cut per part would not fit the merge).
+  KParams q = p;
+  const size_t rows = (size_t)nseq * p.R;
+  q.full = (int)rows;
+  q.parts = 1;
+  if (VEC && !p.mode && p.dmode != SV_TOPK) q.parts = row_split(rows, p.S, &q.full);
+  q.nsplit = (int)((rows - (size_t)q.full) * q.parts);
+  const dim3 grid((unsigned)((size_t)q.full + (size_t)q.nsplit));
+  launch_rows<DT, VEC>(q, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipEvent_t seq_start = ev ? ev[2] : nullptr;
   if (p.spread) {
     // the span sums of the residual draws over the whole chip, then the

@@ -66,6 +66,16 @@ def test_static_entry_matches_handle_entry_on_two_calls():
     _both(with_oracle_drafts(small), "second call (smaller, mixed modes, ragged K)")
 
 
+def test_static_entry_with_rows_streamed_in_parts():
+    # 540 rows: the rows beyond two per CU are streamed in parts, whose
+    # arrival counters sit in the static buffer and must be left at zero
+    split = with_oracle_drafts(workloads.peaked(60, 4, 40000, gen_seed=507, seed=508))
+    _both(split, "rows in parts")
+    _both(split, "rows in parts, again")
+    plain = workloads.iid_normal(58, 4, 40000, sigma_t=3.0, sigma_d=1.0, mode=SV_PLAIN, gen_seed=509, seed=510)
+    _both(with_oracle_drafts(plain), "rows in parts, plain, smaller")
+
+
 def test_static_entry_refuses_a_call_beyond_its_buffer():
     dev = torch.device("cuda", 0)
     B, K, V = 4096, 8, 256000
