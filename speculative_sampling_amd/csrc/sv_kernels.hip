@@ -1364,6 +1364,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     tok = (int)__builtin_amdgcn_raw_buffer_load_b32(trs, t * 4 + z, 0, 0);
   }
   if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
+  __builtin_amdgcn_s_setprio(3);
   lds_barrier();
 
   // ---- streaming: wave wv takes chunks [cb, ce) ----
@@ -1534,6 +1535,14 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       do_chunk(c, A, true);
       issue_chunk<DT>(A, rs, off(c + 2), lane);
       do_chunk(c + 1, B, true);
+      // The wave's issue priority falls as it progresses, so that on a SIMD
+      // the waves furthest behind issue first (the arbiter otherwise favours
+      // the oldest, and a CU's last row would stream alone at the end).
+      const int pr = 3 - (3 * (k + 2)) / n;
+      if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+      else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
     }
     if (n & 1) do_chunk(c, A, true);  // the last chunk
     else unpack_barrier(A);           // loads past the row's end
@@ -1635,6 +1644,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     if (threadIdx.x == 0) __hip_atomic_store(&P.pcount[srow], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     merge_parts<DT>(P, sm, (size_t)srow * NP, NP, is_topk, is_topp, ic2, lane, wv);
   }
+  __builtin_amdgcn_s_setprio(0);
   sm.h[0].hc[threadIdx.x] = 0;  // the finish's first selection counts into these
   sm.h[0].hm[threadIdx.x] = 0;
   lds_barrier();
