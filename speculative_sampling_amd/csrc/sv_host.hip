@@ -240,6 +240,7 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.full = 0;  // set per launch
   p.parts = 1;
   p.nsplit = 0;
+  p.prio = 0;
   p.pcount = reinterpret_cast<int32_t*>(base + g.off_pcount);
   p.phdr = reinterpret_cast<sv::PartHdr*>(base + g.off_phdr);
   p.pvec = reinterpret_cast<uint4*>(base + g.off_pvec);

@@ -150,6 +150,7 @@ struct KParams {
   int32_t full;      // rows [0, full) of the launch streamed whole (row_split)
   int32_t parts;     // work-groups per remaining row
   int32_t nsplit;    // the part work-groups, (rows - full) x parts, launched first
+  int32_t prio;      // waves lower their issue priority as they progress (launches of one round)
   int32_t* pcount;   // [kMaxSplitRows] arrivals per split row (0 between calls)
   PartHdr* phdr;     // [kRowCUs] part records
   uint4* pvec;       // [kRowCUs][kRowWaves][kCandVecs] listed vectors

@@ -1364,7 +1364,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     tok = (int)__builtin_amdgcn_raw_buffer_load_b32(trs, t * 4 + z, 0, 0);
   }
   if (lane == 0) lds_store_relaxed(&sm.pub[wv], -kInf);
-  __builtin_amdgcn_s_setprio(3);
+  if (P.prio) __builtin_amdgcn_s_setprio(3);
   lds_barrier();
 
   // ---- streaming: wave wv takes chunks [cb, ce) ----
@@ -1535,14 +1535,17 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       do_chunk(c, A, true);
       issue_chunk<DT>(A, rs, off(c + 2), lane);
       do_chunk(c + 1, B, true);
-      // The wave's issue priority falls as it progresses, so that on a SIMD
-      // the waves furthest behind issue first (the arbiter otherwise favours
-      // the oldest, and a CU's last row would stream alone at the end).
-      const int pr = 3 - (3 * (k + 2)) / n;
-      if (pr >= 3) __builtin_amdgcn_s_setprio(3);
-      else if (pr == 2) __builtin_amdgcn_s_setprio(2);
-      else if (pr == 1) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
+      // In a launch whose work-groups are all resident at once, the wave's
+      // issue priority falls as it progresses, so that on a SIMD the waves
+      // furthest behind issue first (the arbiter otherwise favours the
+      // oldest, and a CU's last row would stream alone at the end).
+      if (P.prio) {
+        const int pr = 3 - (3 * (k + 2)) / n;
+        if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+        else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
     }
     if (n & 1) do_chunk(c, A, true);  // the last chunk
     else unpack_barrier(A);           // loads past the row's end
@@ -2948,7 +2951,9 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
   q.parts = 1;
   if (VEC && !p.mode && p.dmode != SV_TOPK) q.parts = row_split(rows, p.S, &q.full);
   q.nsplit = (int)((rows - (size_t)q.full) * q.parts);
-  const dim3 grid((unsigned)((size_t)q.full + (size_t)q.nsplit));
+  const size_t wgs = (size_t)q.full + (size_t)q.nsplit;
+  q.prio = wgs > 2 * (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs ? 1 : 0;
+  const dim3 grid((unsigned)wgs);
   launch_rows<DT, VEC>(q, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipEvent_t seq_start = ev ? ev[2] : nullptr;
   if (p.spread) {
