@@ -90,8 +90,8 @@ Geometry geometry(const sv_config* cfg) {
   g.D = (V + sv::kDrawSpan - 1) / sv::kDrawSpan;
   g.off_dsums = off;
   off = align_up(off + (size_t)cfg->max_batch * g.D * sizeof(sv::DrawSum), 256);
-  // part records of split rows (only launches of 2 to 3 rows per CU split)
-  const size_t n_parts = rows > 2 * (size_t)sv::kRowCUs && g.S >= 2 * sv::kRowWaves ? sv::kRowCUs : 0;
+  // part records of split rows (only launches of 1 to 3 rows per CU split)
+  const size_t n_parts = rows > (size_t)sv::kRowCUs && g.S >= 2 * sv::kRowWaves ? sv::kRowCUs : 0;
   g.off_phdr = off;
   off = align_up(off + n_parts * sizeof(sv::PartHdr), 256);
   g.off_pvec = off;

@@ -80,11 +80,12 @@ struct DrawSum {
 };
 
 // Balanced launches.  The nucleus, plain and greedy row kernels hold at
-// least three work-groups per CU.  A launch of between two and three rows
-// per CU (kRowCUs CUs) would leave some CUs a third row while the others
-// have two; instead the first 2 kRowCUs rows are streamed whole and each
-// remaining row is split into `parts` contiguous ranges of chunks, one
-// work-group each, so that every CU streams about the same bytes.  A part
+// least three work-groups per CU.  A launch of between one and three rows
+// per CU (kRowCUs CUs), not a whole number of them, would leave some CUs a
+// row more than the others; instead the first k kRowCUs rows (k = 1, 2)
+// are streamed whole and each remaining row is split into `parts`
+// contiguous ranges of chunks, one work-group each, so that every CU
+// streams about the same bytes.  A part
 // leaves its waves' records and candidate lists in a PartHdr and the part
 // lists; the last part of a row to arrive (a counter per row) merges them
 // and finishes the row.
@@ -94,13 +95,14 @@ constexpr int kMaxParts = 4;
 // the rest in the returned number of parts each (1: no split).
 inline int row_split(size_t rows, int S, int* full) {
   *full = (int)rows;
-  if (rows <= 2 * (size_t)kRowCUs || rows >= 3 * (size_t)kRowCUs) return 1;
-  const int extra = (int)(rows - 2 * (size_t)kRowCUs);
+  if (rows <= (size_t)kRowCUs || rows >= 3 * (size_t)kRowCUs || rows % kRowCUs == 0) return 1;
+  const size_t whole = rows / kRowCUs * kRowCUs;
+  const int extra = (int)(rows - whole);
   int p = kRowCUs / extra;
   p = p < kMaxParts ? p : kMaxParts;
   p = p < S / kRowWaves ? p : S / kRowWaves;  // at least one chunk per wave of every part
   if (p < 2) return 1;
-  *full = 2 * kRowCUs;
+  *full = (int)whole;
   return p;
 }
 // What one part's waves found (written with coherent stores).

@@ -1307,8 +1307,11 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const int NP = split ? P.parts : 1;
   const uint32_t rowg = split ? (uint32_t)P.full + bid / (uint32_t)NP : bid - (uint32_t)P.nsplit;
   const int part = split ? (int)(bid % (uint32_t)NP) : 0;
-  const int b = P.b_base + (int)(rowg / (uint32_t)R);
-  const int r = (int)(rowg % (uint32_t)R);
+  // rows launched per sequence: all 2 K_max + 1, or the K_max + 1 target
+  // rows of a greedy call without the draft's logits
+  const int Rl = P.draft ? R : P.K_max + 1;
+  const int b = P.b_base + (int)(rowg / (uint32_t)Rl);
+  const int r = (int)(rowg % (uint32_t)Rl);
   // Row r of the padded layout: target positions 0..K_max, then draft
   // positions; whether the sequence uses it depends on its K_b.
   // Whole work-groups return here, before any barrier.
@@ -2941,12 +2944,12 @@ template <int DT, bool VEC>
 hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t* ev) {
   // one row-kernel instance: the default mode's, or the one holding every
   // path when the call gives a mode per sequence
-  // A launch of two to three rows per CU streams the rows beyond two per
-  // CU in parts, one per CU (calls with one filter of plain, nucleus or
-  // greedy, whose row kernels hold three work-groups per CU; top-k lists
-  // cut per part would not fit the merge).
+  // A launch of one to three rows per CU streams the rows beyond a whole
+  // number per CU in parts, one per CU (calls with one filter of plain,
+  // nucleus or greedy, whose row kernels hold three work-groups per CU;
+  // top-k lists cut per part would not fit the merge).
   KParams q = p;
-  const size_t rows = (size_t)nseq * p.R;
+  const size_t rows = (size_t)nseq * (p.draft ? p.R : p.K_max + 1);
   q.full = (int)rows;
   q.parts = 1;
   if (VEC && !p.mode && p.dmode != SV_TOPK) q.parts = row_split(rows, p.S, &q.full);

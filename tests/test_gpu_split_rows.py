@@ -1,9 +1,10 @@
 """Rows streamed in parts, against the oracle on every row.
 
-A call of between 2 and 3 rows per CU (513..767 rows of at least 8 chunks,
-one filter of plain, nucleus or greedy) streams its first 512 rows whole
-and splits every further row into 2 to 4 parts, one work-group each, so
-that every CU streams about the same bytes; the last part of a row to
+A call of between 1 and 3 rows per CU, not a whole number of them (257..767
+rows of at least 8 chunks, one filter of plain, nucleus or greedy), streams
+its first 256 or 512 rows whole and splits every further row into 2 to 4
+parts, one work-group each, so that every CU streams about the same bytes;
+the last part of a row to
 arrive merges the parts' softmax records and candidate lists and finishes
 the row.  The merged row must give the same filtered distributions as one
 work-group over the whole row (FDE Interviews breakdown of Chen et al.,
@@ -30,10 +31,11 @@ def split_plan(rows, V, dtype):
     """(rows streamed whole, parts per further row) as the library plans a
     launch (the same rule as its row_split)."""
     S = -(-V // (4096 if dtype == "bf16" else 2048))
-    if rows <= 2 * CUS or rows >= 3 * CUS:
+    if rows <= CUS or rows >= 3 * CUS or rows % CUS == 0:
         return rows, 1
-    p = min(CUS // (rows - 2 * CUS), MAX_PARTS, S // ROW_WAVES)
-    return (2 * CUS, p) if p >= 2 else (rows, 1)
+    whole = rows // CUS * CUS
+    p = min(CUS // (rows - whole), MAX_PARTS, S // ROW_WAVES)
+    return (whole, p) if p >= 2 else (rows, 1)
 
 
 def check(w, label):
@@ -77,6 +79,27 @@ def test_split_nucleus_wide_lists():
     narrows the row's window or hands the row to the whole-row selection."""
     check(workloads.iid_normal(58, 4, 40000, sigma_t=1.0, sigma_d=0.3, mode=SV_TOPP, temperature=1.0,
                                top_p=0.95, gen_seed=89, seed=88), "split_nucleus_wide")
+
+
+def test_split_one_row_per_cu_and_parts():
+    # 288 rows: 256 whole, 32 in 2 parts; and 270 plain rows, 14 in 4 parts
+    check(workloads.peaked(32, 4, 40000, gen_seed=97, seed=96), "split_nucleus_256")
+    check(workloads.iid_normal(30, 4, 70000, sigma_t=3.0, sigma_d=1.0, gen_seed=99, seed=98), "split_plain_256")
+
+
+def test_split_greedy_without_draft_logits():
+    # without the draft's logits only the target rows are launched: 60
+    # sequences x 5 = 300 rows, 256 whole and 44 in 2 parts
+    w = workloads.iid_normal(60, 4, 40000, sigma_t=3.0, sigma_d=1.0, mode=SV_GREEDY, gen_seed=101, seed=100)
+    w = with_oracle_drafts(w)
+    ref = run_oracle(w)
+    w.draft = None
+    full, parts = split_plan(60 * 5, 40000, "bf16")
+    assert parts > 1
+    print(f"[split_greedy_nodraft] 300 target rows: {300 - full} in {parts} parts", flush=True)
+    gpu = run_gpu(w)
+    assert np.array_equal(gpu["accepted"], ref["accepted"])
+    assert np.array_equal(gpu["out_tokens"], ref["out_tokens"])
 
 
 def test_split_rows_with_errors_and_ragged_k():
