@@ -51,7 +51,7 @@ int fail(int code, const std::string& msg) {
 
 struct Geometry {
   int S, L, R_max, D;
-  size_t off_pcount, off_chunks, off_rows, off_kept, off_dsums, off_phdr, off_pvec, off_pik, total;
+  size_t off_pcount, off_scount, off_chunks, off_rows, off_kept, off_dsums, off_phdr, off_pvec, off_pik, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -81,6 +81,8 @@ Geometry geometry(const sv_config* cfg) {
   // every layout: each call leaves them at zero
   g.off_pcount = off;
   off = align_up(off + sv::kMaxSplitRows * sizeof(int32_t), 256);
+  g.off_scount = off;  // (also at a fixed place: the sequence counters of fused calls)
+  off = align_up(off + sv::kMaxFusedSeq * sizeof(int32_t), 256);
   g.off_chunks = off;
   off = align_up(off + rows * g.S * sizeof(sv::ChunkRec), 256);
   g.off_rows = off;
@@ -184,7 +186,7 @@ int spec_verify_create(sv_handle_t* out, const sv_config* cfg) {
     return fail(SV_ENOMEM, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
   }
   // the arrival counters of split rows start at zero (each call leaves them so)
-  e = hipMemset(static_cast<char*>(h->ws) + g.off_pcount, 0, sv::kMaxSplitRows * sizeof(int32_t));
+  e = hipMemset(static_cast<char*>(h->ws) + g.off_pcount, 0, g.off_chunks - g.off_pcount);  // (and the sequence counters)
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->ws);
@@ -241,6 +243,7 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   p.parts = 1;
   p.nsplit = 0;
   p.prio = 0;
+  p.scount = reinterpret_cast<int32_t*>(base + g.off_scount);
   p.pcount = reinterpret_cast<int32_t*>(base + g.off_pcount);
   p.phdr = reinterpret_cast<sv::PartHdr*>(base + g.off_phdr);
   p.pvec = reinterpret_cast<uint4*>(base + g.off_pvec);
@@ -254,6 +257,9 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
               a->B <= 256 && g.D >= 8)
                  ? 1
                  : 0;
+  // other calls may run the sequence step in the row kernel (decided per
+  // launch from its size)
+  p.fuse = p.spread ? 0 : 1;
   return p;
 }
 
@@ -265,6 +271,7 @@ hipError_t launch_call(sv::KParams p, int dtype, bool vec, hipStream_t s, hipEve
   size_t per = std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxRowsPerLaunch / p.R));
   // the draw-sum grid, nseq x D work-groups of kThreads, stays below 2^32 work-items
   if (p.spread) per = std::min(per, std::max<size_t>(1, kMaxRowsPerLaunch / (size_t)p.D));
+  if (p.fuse) per = std::min(per, (size_t)sv::kMaxFusedSeq);
   const int seq_per_launch = (int)per;
   hipError_t e = hipSuccess;
   for (int b0 = 0; b0 < p.B && e == hipSuccess; b0 += seq_per_launch) {

@@ -121,6 +121,11 @@ struct PartHdr {
 };
 // Split rows per launch: at most kRowCUs parts (extra rows x parts).
 constexpr int kMaxSplitRows = kRowCUs / 2;
+// Fused calls: calls whose residual draws are not spread over the chip run
+// the per-sequence accept walk and draw in the row kernel, by the last row
+// of each sequence to finish (a counter per sequence), instead of in a
+// second kernel.  Launches of at most kMaxFusedSeq sequences.
+constexpr int kMaxFusedSeq = 1 << 18;
 
 struct KParams {
   int32_t B, K_max, V, R, S, L;
@@ -153,6 +158,8 @@ struct KParams {
   int32_t parts;     // work-groups per remaining row
   int32_t nsplit;    // the part work-groups, (rows - full) x parts, launched first
   int32_t prio;      // waves lower their issue priority as they progress (launches of one round)
+  int32_t fuse;      // the sequence step runs in the row kernel (the last row of each sequence); set per launch
+  int32_t* scount;   // [kMaxFusedSeq] arrivals per sequence of a fused launch (0 between calls)
   int32_t* pcount;   // [kMaxSplitRows] arrivals per split row (0 between calls)
   PartHdr* phdr;     // [kRowCUs] part records
   uint4* pvec;       // [kRowCUs][kRowWaves][kCandVecs] listed vectors

@@ -875,6 +875,27 @@ struct WaveRec {
   uint32_t flags;  // kCfNonFinite
 };
 
+constexpr int kDrawTiles = 4;   // tiles of a row draw whose loads are in flight together
+constexpr int kTileCap = 384;   // tile sums per wave of a row draw held in LDS
+constexpr int kMaxRows = 2 * kMaxK + 1;
+
+template <int NW>
+struct SmemSeq {
+  RowRec rows[kMaxRows];
+  double rd[NW];
+  int ri[NW];
+  uint32_t misc[4];
+  double rx[2];
+  int rj[NW];
+  // a draw located by precomputed sums: its range, the weight before it,
+  // the row's total and its first / last tokens with weight
+  int dl_lo, dl_hi, dl_nzlo, dl_nzhi, dl_beyond;
+  double dl_base, dl_S;
+  double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
+  double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
+  double tsum[NW][kTileCap];
+};
+
 // Stores and loads that are coherent across the chip's L2s (agent scope,
 // relaxed): the parts of a split row exchange their records and lists
 // through them.  A part's stores are complete (vmcnt(0)) before its
@@ -888,6 +909,30 @@ __device__ __forceinline__ uint64_t cload64(const void* p) {
   return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) { return (uint64_t)lo | ((uint64_t)hi << 32); }
+// Row records, kept entries and chunk sums through coherent stores and
+// loads (the sequence step of a fused call reads what other work-groups of
+// the same kernel wrote).
+static_assert(sizeof(RowRec) == 48 && sizeof(ChunkRec) == 16 && sizeof(KeptEntry) == 8, "record layouts");
+template <class T>
+__device__ __forceinline__ void cstore_rec(T* p, const T& v) {
+  uint64_t w[sizeof(T) / 8];
+  __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 8); ++k) cstore64(reinterpret_cast<uint64_t*>(p) + k, w[k]);
+}
+template <bool kCoh, class T>
+__device__ __forceinline__ T load_rec(const T* p) {
+  if constexpr (!kCoh) {
+    return *p;
+  } else {
+    uint64_t w[sizeof(T) / 8];
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 8); ++k) w[k] = cload64(reinterpret_cast<const uint64_t*>(p) + k);
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+  }
+}
 
 struct RowSmem {
   uint4 cv[kRowWaves][kCandVecs];  // candidate vectors of each wave, in vocabulary order
@@ -906,6 +951,19 @@ struct RowSmem {
   float pg, pu;                    //   the parts' largest maximum / cut, and listing cut
   int pwin[8][kRowWaves];          //   candidates per listing window, per wave
 };
+
+// A row work-group's LDS: the row's streaming and finish, then, in a fused
+// call, the sequence step of the sequence's last row (4 waves).
+union RowSeqSmem {
+  RowSmem r;
+  SmemSeq<kRowWaves> q;
+};
+static_assert(offsetof(RowSmem, parrive) >= sizeof(SmemSeq<kRowWaves>),
+              "the arrival number is read after the sequence step may write its LDS");
+
+template <int DT, bool VEC, int NW, bool kCoh>
+__device__ __forceinline__ void seq_body(const KParams& P, int b, const SeqParams& sp, SmemSeq<NW>& sm);
+__device__ __forceinline__ void write_error(const KParams& P, int b, uint32_t st, int first, int stride);
 
 __device__ __forceinline__ float lds_load_relaxed(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1294,7 +1352,9 @@ template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   constexpr int VE = Fmt<DT>::VE;
   constexpr bool kAny = MODE == kAnyMode;
-  __shared__ RowSmem sm;
+  // (the sequence step of a fused call reuses the finished row's LDS)
+  __shared__ RowSeqSmem U;
+  RowSmem& sm = U.r;
   const int lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int R = P.R, S = P.S;
@@ -1340,7 +1400,12 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const bool used = tgt ? t <= raw.Kb : t < raw.Kb;
   if constexpr (VEC) issue_chunk<DT>(A, rs, used ? off(cb) : row_bytes, lane);
   const SeqParams sp = check_params(P, raw);
-  if (!sp.valid) return;  // the sequence kernel reports the parameter error
+  if (!sp.valid) {
+    // the sequence step reports the parameter error: in a fused call the
+    // work-group of the sequence's first row (or its first part)
+    if (!kAny && P.fuse && r == 0 && part == 0) write_error(P, b, SV_ST_PARAM, (int)threadIdx.x, kThreads);
+    return;
+  }
   if (!used) return;      // a padding row
   // the row's filter (work-group uniform)
   // (a greedy instance only ever sees greedy rows: the mode is never remapped)
@@ -1477,7 +1542,8 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
           cr.z = zc;
           cr.o = ch.o;
           cr.pad = 0;
-          P.chunks[slot0 + c] = cr;
+          if (!kAny && P.fuse) cstore_rec(P.chunks + slot0 + c, cr);
+          else P.chunks[slot0 + c] = cr;
         }
       }
       if (is_topp && !over) {
@@ -1656,6 +1722,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   lds_barrier();
 
   // ---- finish ----
+  {
   // Every wave derives the row's statistics from the wave records; the
   // selection and the kept list of a top-k / nucleus row use the whole
   // work-group, other rows only wave 0.
@@ -1711,7 +1778,13 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
     else if (chunk_sums) rr.flags |= kRfChunks;
   }
   const bool selecting = !(rr.flags & kErrBits) && (is_topk || is_topp);  // work-group uniform
-  if (!selecting && wv != 0) return;
+  if (!selecting && wv != 0) {
+    // (in a fused call every wave joins the sequence step)
+    if constexpr (!kAny) {
+      if (P.fuse) goto arrive;
+    }
+    return;
+  }
 
   const float oM = M * c2;
   const double fM = exp2_small((double)oM - (double)M * (double)c2);
@@ -1789,7 +1862,12 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       }
       if (!ok) {
         // full-row selection by wave 0: re-read the row
-        if (wv != 0) return;
+        if (wv != 0) {
+          if constexpr (!kAny) {
+            if (P.fuse) goto arrive;
+          }
+          return;
+        }
         so = wave_select<DT>(
             [&](auto&& f) {
               for (int e = lane; e < P.V; e += kWave) {
@@ -1853,7 +1931,8 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
             KeptEntry ke;
             ke.idx = e0 + k;
             ke.xq = elem<DT>(v, k);
-            kl[off] = ke;
+            if (!kAny && P.fuse) cstore_rec(kl + off, ke);
+            else kl[off] = ke;
           }
           ++off;
         }
@@ -1875,7 +1954,27 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         }
       }
     }
-    P.rows[rid] = rr;
+    if (!kAny && P.fuse) cstore_rec(P.rows + rid, rr);
+    else P.rows[rid] = rr;
+  }
+  }
+arrive:
+  if constexpr (!kAny) {
+  if (P.fuse) {
+    // A fused call: once every output of this row is complete, count its
+    // arrival; the sequence's last row to arrive runs the accept walk and
+    // the draw, with 4 waves, on records read back with coherent loads.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    const uint32_t sq = (uint32_t)(b - P.b_base);
+    if (threadIdx.x == 0)
+      sm.parrive = __hip_atomic_fetch_add(&P.scount[sq], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    const int rows_used = sp.Kb + 1 + (P.draft ? sp.Kb : 0);
+    if (sm.parrive != rows_used - 1) return;  // (work-group uniform)
+    if (threadIdx.x == 0) __hip_atomic_store(&P.scount[sq], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seq_body<DT, VEC, kRowWaves, true>(P, b, sp, U.q);
+  }
   }
 }
 
@@ -1888,26 +1987,6 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
 // done by the whole work-group.
 
 constexpr int kSeqThreads = kSeqWaves * kWave;  // (the work-group of small batches)
-constexpr int kDrawTiles = 4;   // tiles of a row draw whose loads are in flight together
-constexpr int kTileCap = 384;   // tile sums per wave of a row draw held in LDS
-constexpr int kMaxRows = 2 * kMaxK + 1;
-
-template <int NW>
-struct SmemSeq {
-  RowRec rows[kMaxRows];
-  double rd[NW];
-  int ri[NW];
-  uint32_t misc[4];
-  double rx[2];
-  int rj[NW];
-  // a draw located by precomputed sums: its range, the weight before it,
-  // the row's total and its first / last tokens with weight
-  int dl_lo, dl_hi, dl_nzlo, dl_nzhi, dl_beyond;
-  double dl_base, dl_S;
-  double ua[kWave];  // uniforms of the accept tests at positions 0..63, and of
-  double ud[kWave];  //   the resample (t < K_b) or bonus (t = K_b) draws
-  double tsum[NW][kTileCap];
-};
 
 // ------------------------------------------------------------- draws ----
 
@@ -1982,7 +2061,7 @@ __device__ __forceinline__ float prob(const RowW& w, float x) {
 // draft's logits at its tokens from the draft row prow (only the row of the
 // first rejection is read, and only there).  The draft's weights are fp32
 // terms as in prob().
-template <int DT>
+template <int DT, bool kCoh = false>
 __device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, const RowRec& rp,
                                                const KeptEntry* kl, const void* prow, double u, int lane) {
   constexpr int E = kListMax / kWave;
@@ -2002,7 +2081,7 @@ __device__ __forceinline__ Draw draw_from_list(const RowRec& rq, bool resample, 
     const int i = j * kWave + lane;
     ke[j].idx = 0;
     ke[j].xq = -kInf;
-    if (j < ns && i < N) ke[j] = kl[i];
+    if (j < ns && i < N) ke[j] = load_rec<kCoh>(kl + i);
   }
   float xp[E];  // the draft's logits at the kept tokens (a resample only)
 #pragma unroll
@@ -2142,7 +2221,7 @@ __device__ __forceinline__ float weights8(const RowW& wq, bool use_p, const RowW
 // that the chunk records place the target in) is split into one segment
 // per wave; pass 1 sums the weights of each 512-token tile into LDS, pass 2
 // scans the one tile that holds the target.
-template <int DT, bool VEC, int NW>
+template <int DT, bool VEC, int NW, bool kCoh = false>
 __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& rq, bool resample, const RowRec& rp,
                                                const char* qrow, const char* prow, double u, SmemSeq<NW>& sm, int lane,
                                                int wv, const ChunkRec* qrec) {
@@ -2168,7 +2247,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
       const int c = kCpt * tid + j;
       wc[j] = 0.0;
       if (c < S) {
-        const ChunkRec r = qrec[c];
+        const ChunkRec r = load_rec<kCoh>(qrec + c);
         if (r.z > 0.0) wc[j] = r.z * exp2((double)r.o - (double)rq.M * (double)wq.c2) / rq.Zs;
       }
       wsum += wc[j];
@@ -2734,18 +2813,15 @@ __device__ __forceinline__ void write_tokens(const KParams& P, int b, int n, int
 // NW waves per work-group: kSeqWaves for small batches (a sequence's draw
 // from the rows then has the most waves), 4 for large ones (more sequences
 // resident per CU).
-template <int DT, bool VEC, int NW>
-__global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
+// The accept walk and the draw of sequence b, by a work-group of NW waves.
+// kCoh: the row records, kept lists and chunk sums were written by other
+// work-groups of the running kernel (a fused call's last row of the
+// sequence) and are read with coherent loads.
+template <int DT, bool VEC, int NW, bool kCoh>
+__device__ __forceinline__ void seq_body(const KParams& P, int b, const SeqParams& sp, SmemSeq<NW>& sm) {
   constexpr int NT = NW * kWave;
-  __shared__ SmemSeq<NW> sm;
   const int tid = threadIdx.x, lane = (int)__lane_id();
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  const int b = P.b_base + (int)blockIdx.x;
-  const SeqParams sp = load_params(P, b);
-  if (!sp.valid) {
-    write_error(P, b, SV_ST_PARAM, tid, NT);
-    return;
-  }
   const int Kb = sp.Kb, KM = P.K_max, R = P.R;
   const uint64_t g = P.row_offset + (uint64_t)b;
   const bool greedy = sp.mode == SV_GREEDY;
@@ -2754,7 +2830,7 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
   const bool have_draft = P.draft != nullptr;
   for (int r = tid; r < R; r += NT) {
     const bool used = r <= KM ? r <= Kb : (r - KM - 1 < Kb && have_draft);
-    if (used) sm.rows[r] = P.rows[(size_t)b * R + r];
+    if (used) sm.rows[r] = load_rec<kCoh>(P.rows + (size_t)b * R + r);
   }
   // Loaded with the records by wave 0, for draws that may follow the walk:
   // the span sums of a spread residual draw (lane l: span l) and the chunk
@@ -2769,7 +2845,7 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
   crp.pad = 0;
   if (wv == 0) {
     if (NW == kSeqWaves && P.spread && P.D <= kWave && lane < P.D) dsp = P.dsums[(size_t)b * P.D + lane];
-    if (P.S <= kWave && lane < P.S) crp = P.chunks[((size_t)b * R + Kb) * P.S + lane];
+    if (P.S <= kWave && lane < P.S) crp = load_rec<kCoh>(P.chunks + ((size_t)b * R + Kb) * P.S + lane);
   }
   // The walk's uniforms depend only on seed, sequence, position and
   // purpose: the last wave draws those of positions 0..63 while the records
@@ -2851,7 +2927,7 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
       } else if (rq.flags & kRfListOk) {
         const KeptEntry* kl = P.kept + ((size_t)b * (KM + 1) + n) * (size_t)min(kListMax, P.V);
         const void* prow = resample && have_draft ? row_ptr<DT>(P, b, false, n) : nullptr;
-        const Draw d = draw_from_list<DT>(rq, resample && have_draft, rp, kl, prow, u, lane);
+        const Draw d = draw_from_list<DT, kCoh>(rq, resample && have_draft, rp, kl, prow, u, lane);
         write_tokens(P, b, n, d.y, st | d.flags, lane, kWave);
       } else {
         job = 1;
@@ -2921,10 +2997,22 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
     if (P.spread && resample) d = draw_spread<DT, VEC>(P, b, n, rq, rp, u, dsp, sm, lane, wv);
   }
   if (!(NW == kSeqWaves && P.spread && resample))
-    d = draw_from_rows<DT, VEC, NW>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
+    d = draw_from_rows<DT, VEC, NW, kCoh>(P, rq, resample, rp, static_cast<const char*>(row_ptr<DT>(P, b, true, n)),
                                     resample ? static_cast<const char*>(row_ptr<DT>(P, b, false, n)) : nullptr, u,
                                     sm, lane, wv, P.chunks + ((size_t)b * R + n) * P.S);
   write_tokens(P, b, n, d.y, st | d.flags, tid, NT);
+}
+
+template <int DT, bool VEC, int NW>
+__global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
+  __shared__ SmemSeq<NW> sm;
+  const int b = P.b_base + (int)blockIdx.x;
+  const SeqParams sp = load_params(P, b);
+  if (!sp.valid) {
+    write_error(P, b, SV_ST_PARAM, (int)threadIdx.x, NW * kWave);
+    return;
+  }
+  seq_body<DT, VEC, NW, false>(P, b, sp, sm);
 }
 
 // start / stop: events recorded on the kernel's own dispatch (NULL: none).
@@ -2956,9 +3044,23 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
   q.nsplit = (int)((rows - (size_t)q.full) * q.parts);
   const size_t wgs = (size_t)q.full + (size_t)q.nsplit;
   q.prio = wgs > 2 * (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs ? 1 : 0;
+  // The sequence step is fused into the row kernel for launches of one
+  // round of one to three work-groups per CU (one filter): there it runs
+  // while other rows stream, and the second launch is saved.  Larger
+  // launches keep the sequence kernel (its smaller work-groups hold more
+  // sequences per CU than a row work-group does).
+  q.fuse = p.fuse && !p.mode && wgs > (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs ? 1 : 0;
   const dim3 grid((unsigned)wgs);
   launch_rows<DT, VEC>(q, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipEvent_t seq_start = ev ? ev[2] : nullptr;
+  if (q.fuse) {
+    // the sequence step ran in the row kernel: the second stage is empty
+    if (ev) {
+      (void)hipEventRecord(ev[2], stream);
+      (void)hipEventRecord(ev[3], stream);
+    }
+    return hipSuccess;
+  }
   if (p.spread) {
     // the span sums of the residual draws over the whole chip, then the
     // walk and draws
