@@ -240,6 +240,20 @@ int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* st
 int spec_verify_stream_probe_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, void* out,
                                    void* stream);
 
+/* The step's random numbers, for verification: writes to out[i] (device
+ * memory, n words) word 0 of Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ * SC'11) at key `seed` and counter (g[i] low 32 bits, t[i], purpose[i],
+ * g[i] high 32 bits) -- the word from which run takes each uniform as
+ * (word >> 8) / 2^24, with g the sequence's global index (row_offset + b),
+ * t its position and purpose 0 (accept test), 1 (resample) or 2 (bonus).
+ * g, t and purpose are device arrays of n entries; n >= 0.  Asynchronous on
+ * `stream`, allocates nothing.  Returns SV_OK, or SV_EINVAL (a NULL array
+ * with n > 0, n negative: nothing is launched) / SV_EHIP, with
+ * spec_verify_last_error set.  It lets a test compare the device generator
+ * with an independent one word for word. */
+int spec_verify_philox_words(uint64_t seed, const uint64_t* g, const uint32_t* t, const uint32_t* purpose,
+                             int64_t n, uint32_t* out, void* stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Runs the
  * same step as spec_verify_run with the same kernels and results, on

@@ -27,7 +27,7 @@ ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 EXPORTS = ("spec_verify_create", "spec_verify_run", "spec_verify_destroy",
            "spec_verify_validate", "spec_verify_workspace_bytes", "spec_verify_profile_begin",
            "spec_verify_profile_end", "spec_verify_stream_probe", "spec_verify_last_error",
-           "spec_verify_run_static", "spec_verify_stream_probe_sweep")
+           "spec_verify_run_static", "spec_verify_stream_probe_sweep", "spec_verify_philox_words")
 
 # Size of the static device buffer spec_verify_run_static works in.
 SV_STATIC_SCRATCH_BYTES = 64 << 20
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_stream_probe_sweep.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.spec_verify_stream_probe_sweep.restype = ctypes.c_int
+    lib.spec_verify_philox_words.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_verify_philox_words.restype = ctypes.c_int
     lib.spec_verify_run_static.argtypes = [ctypes.POINTER(SvConfig), ctypes.POINTER(SvArgs), ctypes.c_void_p]
     lib.spec_verify_run_static.restype = ctypes.c_int
     lib.spec_verify_last_error.argtypes = []
@@ -238,6 +241,17 @@ def spec_verify_stream_probe(data_ptr: int, nbytes: int, out_ptr: int, stream: i
                                                  ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_stream_probe")
+
+
+def spec_verify_philox_words(seed: int, g_ptr: int, t_ptr: int, purpose_ptr: int, n: int, out_ptr: int,
+                             stream: int = 0) -> None:
+    """Word 0 of the device Philox4x32-10 for n counters (device arrays;
+    see the header)."""
+    rc = load_library().spec_verify_philox_words(seed, ctypes.c_void_p(g_ptr), ctypes.c_void_p(t_ptr),
+                                                 ctypes.c_void_p(purpose_ptr), n, ctypes.c_void_p(out_ptr),
+                                                 ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_philox_words")
 
 
 def spec_verify_stream_probe_sweep(data_ptr: int, nbytes: int, loads_per_lane: int, waves_per_cu: int,

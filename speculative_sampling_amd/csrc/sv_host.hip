@@ -375,6 +375,16 @@ int spec_verify_stream_probe(const void* data, size_t bytes, void* out, void* st
   return SV_OK;
 }
 
+int spec_verify_philox_words(uint64_t seed, const uint64_t* g, const uint32_t* t, const uint32_t* purpose,
+                             int64_t n, uint32_t* out, void* stream) {
+  if (n < 0) return fail(SV_EINVAL, "philox words: n must be >= 0");
+  if (n == 0) return SV_OK;
+  if (!g || !t || !purpose || !out) return fail(SV_EINVAL, "philox words: g, t, purpose and out must be device pointers");
+  const hipError_t e = sv::launch_philox_words(seed, g, t, purpose, n, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_EHIP, std::string("philox words launch failed: ") + hipGetErrorString(e));
+  return SV_OK;
+}
+
 int spec_verify_stream_probe_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, void* out,
                                    void* stream) {
   if (!data || !out) return fail(SV_EINVAL, "stream probe sweep: data and out must be device pointers");

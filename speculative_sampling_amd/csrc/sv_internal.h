@@ -177,6 +177,9 @@ hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStr
                          hipEvent_t* ev = nullptr);
 // Reads the first bytes / 8192 whole 8 KB blocks of data once (see spec_verify_stream_probe).
 hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hipStream_t stream);
+// Philox word 0 for n counters (see spec_verify_philox_words).
+hipError_t launch_philox_words(uint64_t seed, const uint64_t* g, const uint32_t* t, const uint32_t* purpose,
+                               int64_t n, uint32_t* out, hipStream_t stream);
 // One point of the read-rate sweep (see spec_verify_stream_probe_sweep).
 hipError_t launch_stream_sweep(const void* data, size_t bytes, int loads_per_lane, int waves_per_cu, uint32_t* out,
                                hipStream_t stream);

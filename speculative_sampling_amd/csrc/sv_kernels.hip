@@ -3164,6 +3164,24 @@ hipError_t launch_stream_probe(const void* data, size_t bytes, uint32_t* out, hi
   return hipGetLastError();
 }
 
+namespace {
+__global__ __launch_bounds__(256) void philox_words_kernel(uint64_t seed, const uint64_t* g, const uint32_t* t,
+                                                           const uint32_t* purpose, int64_t n, uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = philox_word0(seed, g[i], t[i], purpose[i]);
+}
+}  // namespace
+
+hipError_t launch_philox_words(uint64_t seed, const uint64_t* g, const uint32_t* t, const uint32_t* purpose,
+                               int64_t n, uint32_t* out, hipStream_t stream) {
+  for (int64_t i0 = 0; i0 < n; i0 += (int64_t)1 << 30) {  // grids of at most 2^30 work-items
+    const int64_t m = n - i0 < ((int64_t)1 << 30) ? n - i0 : ((int64_t)1 << 30);
+    hipLaunchKernelGGL(philox_words_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, seed, g + i0,
+                       t + i0, purpose + i0, m, out + i0);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_verify(const KParams& p, int dtype, bool vec, int nseq, hipStream_t stream, hipEvent_t* ev) {
   if (nseq <= 0) return hipSuccess;
   hipError_t e;

@@ -196,6 +196,13 @@ def test_stream_probe_rejects_bad_pointers_on_the_host():
     for loads, waves in [(2, 4), (12, 4), (8, 0), (8, 33), (32, 4)]:
         assert lib.spec_verify_stream_probe_sweep(ctypes.c_void_p(64), 16384, loads, waves,
                                                   ctypes.byref(sink), None) == SV_EINVAL
+    # the Philox words entry: NULL arrays with n > 0 and negative n are
+    # refused before anything is launched; n = 0 is a no-op
+    p = ctypes.c_void_p(64)
+    assert lib.spec_verify_philox_words(1, None, p, p, 4, p, None) == SV_EINVAL
+    assert lib.spec_verify_philox_words(1, p, p, p, 4, None, None) == SV_EINVAL
+    assert lib.spec_verify_philox_words(1, p, p, p, -1, p, None) == SV_EINVAL
+    assert lib.spec_verify_philox_words(1, None, None, None, 0, None, None) == 0
 
 
 def test_verifier_refuses_logits_that_disagree_with_the_handle():
