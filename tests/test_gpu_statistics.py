@@ -55,7 +55,8 @@ def test_draft_tokens_follow_p(run):
     toks = w.draft_tokens.cpu().numpy().ravel()
     counts = np.bincount(toks, minlength=4)
     _, pval = stats.chisquare(counts, P * toks.size)
-    assert pval > 1e-3
+    print(f"[worked_example_gpu] draft tokens: chi-square p = {pval:.3f}", flush=True)
+    assert pval > 0.01
 
 
 def test_per_position_acceptance(run):
@@ -72,7 +73,8 @@ def test_accepted_count_law(run):
     n = out["accepted"]
     law = np.array([A ** k * (1 - A) for k in range(4)] + [A ** 4])
     _, pval = stats.chisquare(np.bincount(n, minlength=5), law * n.size)
-    assert pval > 1e-3
+    print(f"[worked_example_gpu] accepted counts: chi-square p = {pval:.3f}", flush=True)
+    assert pval > 0.01
 
 
 def test_expected_tokens_per_pass(run):
