@@ -271,7 +271,6 @@ hipError_t launch_call(sv::KParams p, int dtype, bool vec, hipStream_t s, hipEve
   size_t per = std::min(kMaxSeqPerLaunch, std::max<size_t>(1, kMaxRowsPerLaunch / p.R));
   // the draw-sum grid, nseq x D work-groups of kThreads, stays below 2^32 work-items
   if (p.spread) per = std::min(per, std::max<size_t>(1, kMaxRowsPerLaunch / (size_t)p.D));
-  if (p.fuse) per = std::min(per, (size_t)sv::kMaxFusedSeq);
   const int seq_per_launch = (int)per;
   hipError_t e = hipSuccess;
   for (int b0 = 0; b0 < p.B && e == hipSuccess; b0 += seq_per_launch) {

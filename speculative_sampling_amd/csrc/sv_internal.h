@@ -124,8 +124,9 @@ constexpr int kMaxSplitRows = kRowCUs / 2;
 // Fused calls: calls whose residual draws are not spread over the chip run
 // the per-sequence accept walk and draw in the row kernel, by the last row
 // of each sequence to finish (a counter per sequence), instead of in a
-// second kernel.  Launches of at most kMaxFusedSeq sequences.
-constexpr int kMaxFusedSeq = 1 << 18;
+// second kernel.  A fused launch holds at most three row work-groups per CU,
+// each of at least one row of its own sequence: at most kMaxFusedSeq sequences.
+constexpr int kMaxFusedSeq = 3 * kRowCUs;
 
 struct KParams {
   int32_t B, K_max, V, R, S, L;

@@ -1348,10 +1348,13 @@ __device__ __forceinline__ void merge_parts(const KParams& P, RowSmem& sm, size_
   }
 }
 
-template <int DT, bool VEC, int MODE>
+// FUSE: the launch runs the sequence step too (one filter only); its own
+// instance, so that launches without it keep the plain kernel's registers.
+template <int DT, bool VEC, int MODE, bool FUSE>
 __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   constexpr int VE = Fmt<DT>::VE;
   constexpr bool kAny = MODE == kAnyMode;
+  static_assert(!(FUSE && kAny), "a call with a mode per sequence is not fused");
   // (the sequence step of a fused call reuses the finished row's LDS)
   __shared__ RowSeqSmem U;
   RowSmem& sm = U.r;
@@ -1403,7 +1406,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   if (!sp.valid) {
     // the sequence step reports the parameter error: in a fused call the
     // work-group of the sequence's first row (or its first part)
-    if (!kAny && P.fuse && r == 0 && part == 0) write_error(P, b, SV_ST_PARAM, (int)threadIdx.x, kThreads);
+    if (FUSE && r == 0 && part == 0) write_error(P, b, SV_ST_PARAM, (int)threadIdx.x, kThreads);
     return;
   }
   if (!used) return;      // a padding row
@@ -1542,7 +1545,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
           cr.z = zc;
           cr.o = ch.o;
           cr.pad = 0;
-          if (!kAny && P.fuse) cstore_rec(P.chunks + slot0 + c, cr);
+          if (FUSE) cstore_rec(P.chunks + slot0 + c, cr);
           else P.chunks[slot0 + c] = cr;
         }
       }
@@ -1780,9 +1783,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
   const bool selecting = !(rr.flags & kErrBits) && (is_topk || is_topp);  // work-group uniform
   if (!selecting && wv != 0) {
     // (in a fused call every wave joins the sequence step)
-    if constexpr (!kAny) {
-      if (P.fuse) goto arrive;
-    }
+    if constexpr (FUSE) goto arrive;
     return;
   }
 
@@ -1863,9 +1864,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
       if (!ok) {
         // full-row selection by wave 0: re-read the row
         if (wv != 0) {
-          if constexpr (!kAny) {
-            if (P.fuse) goto arrive;
-          }
+          if constexpr (FUSE) goto arrive;
           return;
         }
         so = wave_select<DT>(
@@ -1931,7 +1930,7 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
             KeptEntry ke;
             ke.idx = e0 + k;
             ke.xq = elem<DT>(v, k);
-            if (!kAny && P.fuse) cstore_rec(kl + off, ke);
+            if (FUSE) cstore_rec(kl + off, ke);
             else kl[off] = ke;
           }
           ++off;
@@ -1954,13 +1953,12 @@ __global__ __launch_bounds__(kThreads, 3) void row_kernel(const KParams P) {
         }
       }
     }
-    if (!kAny && P.fuse) cstore_rec(P.rows + rid, rr);
+    if (FUSE) cstore_rec(P.rows + rid, rr);
     else P.rows[rid] = rr;
   }
   }
 arrive:
-  if constexpr (!kAny) {
-  if (P.fuse) {
+  if constexpr (FUSE) {
     // A fused call: once every output of this row is complete, count its
     // arrival; the sequence's last row to arrive runs the accept walk and
     // the draw, with 4 waves, on records read back with coherent loads.
@@ -1974,7 +1972,6 @@ arrive:
     if (sm.parrive != rows_used - 1) return;  // (work-group uniform)
     if (threadIdx.x == 0) __hip_atomic_store(&P.scount[sq], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     seq_body<DT, VEC, kRowWaves, true>(P, b, sp, U.q);
-  }
   }
 }
 
@@ -3016,16 +3013,25 @@ __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
 }
 
 // start / stop: events recorded on the kernel's own dispatch (NULL: none).
-template <int DT, bool VEC>
-void launch_rows(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+template <int DT, bool VEC, bool FUSE>
+void launch_rows_as(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 block(kThreads);
   switch (mode) {
-    case SV_PLAIN: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_PLAIN>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_TOPK: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPK>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_TOPP: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPP>), grid, block, 0, stream, start, stop, 0, p); break;
-    case SV_GREEDY: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_GREEDY>), grid, block, 0, stream, start, stop, 0, p); break;
-    default: hipExtLaunchKernelGGL((row_kernel<DT, VEC, kAnyMode>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_PLAIN: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_PLAIN, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPK: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPK, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_TOPP: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPP, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_GREEDY: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_GREEDY, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
+    default:
+      if constexpr (!FUSE)
+        hipExtLaunchKernelGGL((row_kernel<DT, VEC, kAnyMode, false>), grid, block, 0, stream, start, stop, 0, p);
+      break;
   }
+}
+
+template <int DT, bool VEC>
+void launch_rows(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (p.fuse) launch_rows_as<DT, VEC, true>(p, mode, grid, stream, start, stop);
+  else launch_rows_as<DT, VEC, false>(p, mode, grid, stream, start, stop);
 }
 
 template <int DT, bool VEC>
@@ -3049,7 +3055,7 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
   // while other rows stream, and the second launch is saved.  Larger
   // launches keep the sequence kernel (its smaller work-groups hold more
   // sequences per CU than a row work-group does).
-  q.fuse = p.fuse && !p.mode && wgs > (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs ? 1 : 0;
+  q.fuse = p.fuse && !p.mode && wgs > (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs && nseq <= kMaxFusedSeq ? 1 : 0;
   const dim3 grid((unsigned)wgs);
   launch_rows<DT, VEC>(q, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipEvent_t seq_start = ev ? ev[2] : nullptr;
