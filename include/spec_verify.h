@@ -268,7 +268,10 @@ int spec_verify_philox_words(uint64_t seed, const uint64_t* g, const uint32_t* t
  * shares that device's buffer: calls that overlap on a device (other
  * streams, other threads, graph replays) race and give wrong results;
  * order them on one stream.  The buffer needs no clearing between calls:
- * each call writes every workspace entry it reads. */
+ * each call writes every workspace entry it reads, except the arrival
+ * counters of rows streamed in parts and of fused sequence steps, which
+ * are zero when the library's code loads and which every call that
+ * completes leaves at zero. */
 #define SV_STATIC_SCRATCH_BYTES ((uint64_t)64 << 20)
 int spec_verify_run_static(const sv_config* cfg, const sv_args* args, void* stream);
 
