@@ -2480,8 +2480,25 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
 
 static_assert(kMaxVocab / kDrawSpan <= kSeqThreads, "one span sum per thread of the sequence's work-group");
 
+// Loads one word of each 64-byte line of the kernel arguments at once and
+// waits for them, so that the scalar cache holds every line before the
+// kernel's first parameter tests.  The compiler loads the arguments where
+// each test needs them, and a test that branches on a pointer waits for
+// its load before the next one issues, so each line's first miss would be
+// a round trip of its own.  (In the short, latency-bound kernels only: the
+// row kernel's start is hidden behind its first chunk's loads, and there
+// the extra wait measured slower.)
+__device__ __forceinline__ void warm_kernel_args() {
+  typedef __attribute__((address_space(4))) const uint32_t karg_u32;
+  static_assert(sizeof(KParams) > 4 * 64 && sizeof(KParams) <= 5 * 64, "the argument block spans five lines");
+  karg_u32* ka = (karg_u32*)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t w0 = ka[0], w1 = ka[16], w2 = ka[32], w3 = ka[48], w4 = ka[64];
+  asm volatile("" ::"s"(w0), "s"(w1), "s"(w2), "s"(w3), "s"(w4));
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void draw_sum_kernel(const KParams P) {
+  warm_kernel_args();
   __shared__ double red[kRowWaves];
   __shared__ int rlo[kRowWaves], rhi[kRowWaves];
   __shared__ int sh_n;
@@ -3002,6 +3019,7 @@ __device__ __forceinline__ void seq_body(const KParams& P, int b, const SeqParam
 
 template <int DT, bool VEC, int NW>
 __global__ __launch_bounds__(NW * kWave) void seq_kernel(const KParams P) {
+  warm_kernel_args();
   __shared__ SmemSeq<NW> sm;
   const int b = P.b_base + (int)blockIdx.x;
   const SeqParams sp = load_params(P, b);
