@@ -82,7 +82,11 @@ enum {
                                     top_p)                                          */
   SV_ST_FULLSELECT = 1u << 7,    /* a top-k/top-p threshold needed the full-row
                                     selection (slow path)                           */
-  SV_ST_REREAD = 1u << 8         /* the final draw re-read full logit rows           */
+  SV_ST_REREAD = 1u << 8,        /* the final draw re-read full logit rows           */
+  SV_ST_LOCATED = 1u << 9        /* that draw read only the span or chunk located by
+                                    sums made before it (the span sums of a spread
+                                    residual draw, or the chunk sums of a plain
+                                    target row for its bonus draw)                  */
 };
 
 /* Create-time capacity.  vocab is fixed for the handle; 1 <= vocab <= 2^22,

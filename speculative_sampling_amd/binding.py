@@ -20,7 +20,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_PLAIN, SV_TOPK, SV_TOPP, SV_GREEDY = 0, 1, 2, 3
 SV_OK, SV_EINVAL, SV_ECAPACITY, SV_EDTYPE, SV_EHIP, SV_ENOMEM = 0, -1, -2, -3, -4, -5
 ST_TOKEN, ST_NONFINITE, ST_EMPTY, ST_ZERO_RESIDUAL = 1, 2, 4, 8
-ST_PZERO, ST_MARGIN, ST_PARAM, ST_FULLSELECT, ST_REREAD = 16, 32, 64, 128, 256
+ST_PZERO, ST_MARGIN, ST_PARAM, ST_FULLSELECT, ST_REREAD, ST_LOCATED = 16, 32, 64, 128, 256, 512
 ST_ERRORS = ST_TOKEN | ST_NONFINITE | ST_EMPTY | ST_PARAM
 
 # Every function the header declares.

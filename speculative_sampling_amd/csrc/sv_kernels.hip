@@ -2278,6 +2278,7 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
       lo = c * P.L;
       hi = min(P.V, lo + P.L);
       located = true;
+      d.flags |= SV_ST_LOCATED;
       force_last = cs == 0x7fffffff;  // u beyond the rounded total: the last token of the last chunk
     }
   }
@@ -2782,7 +2783,7 @@ __device__ __forceinline__ Draw draw_spread(const KParams& P, int b, int n, cons
   const RangeDraw r = draw_range<DT, VEC, kSeqWaves>(P, wq, true, wp, all, qrow, prow, lo, hi, base,
                                                      beyond ? kInf : u * S, sm, lane, wv);
   Draw d;
-  d.flags = SV_ST_REREAD;
+  d.flags = SV_ST_REREAD | SV_ST_LOCATED;
   d.y = r.y;
   if (r.y >= 0) {
     const double plo = (r.crossed ? r.clo : S) / S, phi = (r.crossed ? r.chi : S) / S;
@@ -2995,7 +2996,7 @@ __device__ __forceinline__ void seq_body(const KParams& P, int b, const SeqParam
         draw_range<DT, VEC, NW>(P, wq, false, wq, all, static_cast<const char*>(row_ptr<DT>(P, b, true, n)), nullptr,
                                 sm.dl_lo, sm.dl_hi, 0.0, sm.dl_beyond ? kInf : u - base, sm, lane, wv);
     if (r.y >= 0) {
-      uint32_t fl = SV_ST_REREAD;
+      uint32_t fl = SV_ST_REREAD | SV_ST_LOCATED;
       const double plo = base + (r.crossed ? r.clo : r.total), phi = base + (r.crossed ? r.chi : r.total);
       if (r.glo < r.y && u - plo < kWindow) fl |= SV_ST_MARGIN;
       if (r.ghi > r.y && phi - u < kWindow) fl |= SV_ST_MARGIN;

@@ -23,7 +23,7 @@ import torch
 
 from helpers import compare, run_gpu, run_oracle, with_oracle_drafts
 from speculative_sampling_amd import workloads
-from speculative_sampling_amd.binding import ST_ERRORS, ST_REREAD, SV_PLAIN
+from speculative_sampling_amd.binding import ST_ERRORS, ST_LOCATED, ST_REREAD, ST_ZERO_RESIDUAL, SV_PLAIN
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -45,6 +45,15 @@ def resampled(gpu, w):
     return gpu["accepted"] < kb
 
 
+def located_draws(gpu):
+    """Sequences whose draw read only a located span or chunk of the rows
+    (status bit 9), among those with a residual mass (a draw without one
+    falls back to q over the whole row)."""
+    st = gpu["row_status"]
+    mass = (st & ST_ZERO_RESIDUAL) == 0
+    return (st & ST_LOCATED) != 0, mass
+
+
 def test_spread_draw_plain_bf16_headline_vocab():
     # 16 spans per row, every sequence in one call of 16
     w, gpu, _ = check_all(workloads.iid_normal(16, 4, 128256, sigma_t=3.0, sigma_d=1.0, gen_seed=61, seed=60),
@@ -52,6 +61,24 @@ def test_spread_draw_plain_bf16_headline_vocab():
     r = resampled(gpu, w)
     assert r.sum() >= 8   # the draws under test happened
     assert np.all(gpu["row_status"][r] & ST_REREAD)
+    # Both draws give the same token, so parity alone cannot tell them
+    # apart: the residual draws used the span sums (not the sequence
+    # kernel's own pass over the rows) and the bonus draws the chunk sums.
+    loc, mass = located_draws(gpu)
+    assert np.all(loc[mass]), np.flatnonzero(mass & ~loc)
+
+
+def test_row_draw_without_spans():
+    # 260 sequences, more than the span sums serve (and 780 rows, more than
+    # a fused launch holds): residual draws walk the rows in the sequence
+    # kernel, bonus draws still use the chunk sums
+    w, gpu, _ = check_all(workloads.iid_normal(260, 1, 65536, sigma_t=3.0, sigma_d=1.0, gen_seed=71, seed=70),
+                          "row_draw_no_spans")
+    r = resampled(gpu, w)
+    loc, mass = located_draws(gpu)
+    assert r.sum() > 50 and (~r).sum() > 10
+    assert not np.any(loc[r]), np.flatnonzero(loc & r)
+    assert np.all(loc[~r & mass])
 
 
 def test_spread_draw_fp32_ragged_last_span():
