@@ -218,6 +218,7 @@ def draw_draft_tokens(w: Workload, sampler: Callable) -> Workload:
 def config(name: str, device="cpu", **kw) -> Workload:
     """The named workloads at their full sizes."""
     if name == "worked_example":
+        kw.pop("gen_seed", None)   # its logits are the pages' fixed distributions
         return worked_example(kw.pop("B", 1_000_000), device=device, **kw)
     if name == "latency_b1":
         return iid_normal(kw.pop("B", 1), 4, 32000, sigma_t=3.0, sigma_d=1.0, dtype="bf16",

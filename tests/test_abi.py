@@ -239,3 +239,18 @@ def test_static_entry_refuses_calls_beyond_its_buffer_on_the_host():
     # argument errors are reported as by spec_verify_run
     rc = lib.spec_verify_run_static(ctypes.byref(cfg), ctypes.byref(_args(B=4096, K_max=8, target=None)), None)
     assert rc == SV_EINVAL
+
+
+def test_bench_workloads_take_the_set_seeds():
+    """bench.py builds every input set with config(name, gen_seed=..., seed=...);
+    the small workloads are built here on the host with the same arguments
+    (the worked example's logits are fixed, so its generator seed is unused)."""
+    from speculative_sampling_amd import workloads
+    a = workloads.config("worked_example", gen_seed=1000, seed=0, B=8)
+    b = workloads.config("worked_example", gen_seed=1001, seed=1, B=8)
+    assert (a.B, a.K_max, a.V) == (8, 4, 4)
+    assert torch.equal(a.target, b.target) and torch.equal(a.draft, b.draft)
+    c = workloads.config("latency_b1", gen_seed=1000, seed=0)
+    d = workloads.config("latency_b1", gen_seed=1001, seed=1)
+    assert (c.B, c.K_max, c.V) == (1, 4, 32000)
+    assert not torch.equal(c.target, d.target)
