@@ -252,9 +252,9 @@ sv::KParams make_params(const sv_config& cfg, const Geometry& g, void* ws, const
   // may hold plain rows (their first rejection always needs the rows);
   // other calls draw the rare ones in the sequence kernel.
   // (only where the sequence kernel alone would leave most CUs idle: fewer
-  // sequences than CUs, rows of at least 8 spans)
+  // sequences than CUs, rows longer than 57,344 tokens)
   p.spread = (a->K_max > 0 && p.draft != nullptr && (a->mode != nullptr || a->default_mode == SV_PLAIN) &&
-              a->B <= 256 && g.D >= 8)
+              a->B <= 256 && (size_t)cfg.vocab > (size_t)57344)
                  ? 1
                  : 0;
   // other calls may run the sequence step in the row kernel (decided per

@@ -71,8 +71,9 @@ struct KeptEntry {
 // kernel, one work-group per kDrawSpan tokens of each sequence repeats the
 // accept walk and, for such a sequence, sums its span's weights into a
 // DrawSum; the sequence kernel then locates the span holding the target
-// and draws in it.
-constexpr int kDrawSpan = 8192;
+// and draws in it.  (Spans of 4096 tokens measured faster than 8192 and
+// 2048 at the headline shape in plain mode.)
+constexpr int kDrawSpan = 4096;
 struct DrawSum {
   double s;       // sum of the span's weights, fp32 groups of 8 added in fp64
   int32_t first;  // first token of the span's first group of 8 with weight (INT32_MAX: none)

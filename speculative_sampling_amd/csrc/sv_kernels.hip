@@ -2479,7 +2479,8 @@ __device__ __forceinline__ Draw draw_from_rows(const KParams& P, const RowRec& r
 // added pairwise), so the span the sums locate holds the crossing of the
 // group-level running sum.
 
-static_assert(kMaxVocab / kDrawSpan <= kSeqThreads, "one span sum per thread of the sequence's work-group");
+static_assert(kDrawSpan % (8 * kThreads) == 0 && kDrawSpan <= 16 * kSeqThreads,
+              "whole groups of 8 per thread in the span kernel; a span within one draw_range of the sequence kernel");
 
 // Loads one word of each 64-byte line of the kernel arguments at once and
 // waits for them, so that the scalar cache holds every line before the
@@ -2539,8 +2540,8 @@ __global__ __launch_bounds__(kThreads) void draw_sum_kernel(const KParams P) {
   const char* qrow = static_cast<const char*>(row_ptr<DT>(P, b, true, n));
   const char* prow = static_cast<const char*>(row_ptr<DT>(P, b, false, n));
   const int lo = sp_ * kDrawSpan, hi = min(P.V, lo + kDrawSpan);
-  // thread t takes groups t, t + 256, t + 512, t + 768 of the span (all
-  // loads in flight together)
+  // thread t takes groups t, t + 256, ... of the span (all loads in
+  // flight together)
   constexpr int kG = kDrawSpan / 8 / kThreads;
   uint4 aq[kG][2], ap[kG][2];
 #pragma unroll

@@ -8,7 +8,7 @@ paperlayer.ai summary of arXiv 2302.01318, "Modified Rejection Sampling").
 The library does this in one of three ways, chosen from the call's shape:
 
   * calls of at most 256 sequences that may hold plain rows and rows of at
-    least 8 spans of 8192 tokens: the span sums are made over the whole
+    more than 57,344 tokens: the span sums (one per 4096 tokens) are made over the whole
     chip before the sequence kernel, which locates the span and draws;
   * other calls of fewer than 1024 sequences: the sequence kernel's 8
     waves walk the rows;
@@ -55,7 +55,7 @@ def located_draws(gpu):
 
 
 def test_spread_draw_plain_bf16_headline_vocab():
-    # 16 spans per row, every sequence in one call of 16
+    # 32 spans per row, every sequence in one call of 16
     w, gpu, _ = check_all(workloads.iid_normal(16, 4, 128256, sigma_t=3.0, sigma_d=1.0, gen_seed=61, seed=60),
                           "spread_plain_bf16")
     r = resampled(gpu, w)
@@ -82,7 +82,7 @@ def test_row_draw_without_spans():
 
 
 def test_spread_draw_fp32_ragged_last_span():
-    # V = 70000: nine spans, the last one partial
+    # V = 70000: 18 spans, the last one partial
     check_all(workloads.iid_normal(10, 3, 70000, sigma_t=2.5, sigma_d=1.5, dtype="f32", temperature=1.2,
                                    gen_seed=63, seed=62), "spread_plain_f32")
 
