@@ -3037,7 +3037,10 @@ template <int DT, bool VEC, bool FUSE>
 void launch_rows_as(const KParams& p, int mode, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 block(kThreads);
   switch (mode) {
-    case SV_PLAIN: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_PLAIN, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
+    case SV_PLAIN:  // (plain calls are not fused)
+      if constexpr (!FUSE)
+        hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_PLAIN, false>), grid, block, 0, stream, start, stop, 0, p);
+      break;
     case SV_TOPK: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPK, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
     case SV_TOPP: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_TOPP, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
     case SV_GREEDY: hipExtLaunchKernelGGL((row_kernel<DT, VEC, SV_GREEDY, FUSE>), grid, block, 0, stream, start, stop, 0, p); break;
@@ -3074,8 +3077,13 @@ hipError_t launch_all(const KParams& p, int nseq, hipStream_t stream, hipEvent_t
   // round of one to three work-groups per CU (one filter): there it runs
   // while other rows stream, and the second launch is saved.  Larger
   // launches keep the sequence kernel (its smaller work-groups hold more
-  // sequences per CU than a row work-group does).
-  q.fuse = p.fuse && !p.mode && wgs > (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs && nseq <= kMaxFusedSeq ? 1 : 0;
+  // sequences per CU than a row work-group does), and so do plain calls:
+  // their first rejection always draws from the rows, which the 8-wave
+  // sequence kernel does faster than a row work-group's 4 waves.
+  q.fuse = p.fuse && !p.mode && p.dmode != SV_PLAIN && wgs > (size_t)kRowCUs && wgs <= 3 * (size_t)kRowCUs &&
+                   nseq <= kMaxFusedSeq
+               ? 1
+               : 0;
   const dim3 grid((unsigned)wgs);
   launch_rows<DT, VEC>(q, p.mode ? kAnyMode : p.dmode, grid, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   hipEvent_t seq_start = ev ? ev[2] : nullptr;
